@@ -1,0 +1,301 @@
+"""CPU oracle for confidence-scheduled block verification (test infrastructure).
+
+This package is TEST INFRASTRUCTURE.  Only the test suite, the smoke check and
+the benchmark's CPU-baseline leg may import it.  The HIP library never calls it
+and it shares no code with the library: it is a plain, slow, direct transcript
+of what the path computes, written so that it can be checked against the pages
+by eye.  Floating point is fp64 except where the schedule must reproduce a
+fixed fp32 decision (see ``schedule``).
+
+Sources (page title, then section):
+
+* "DSpark Deep Dive: How DeepSeek Squeezed an 85% Speedup Out of Inference
+  Without Touching a Single Model Weight" (the Deep Dive):
+  "Speculative Decoding From First Principles" (draft, verify, accept with
+  probability min(1, p/q), resample a rejection from the normalised positive
+  part of p - q); "Variable-Length Drafts" (verify from position 1 until the
+  cumulative confidence drops below a threshold); "The Full Scheduling
+  Pipeline" (1 <= L <= K; tokens past L are discarded); "The Optimization
+  Logic" (a verify slot is better spent on a higher-confidence token of
+  another request); "GPU-Resident Scheduling" (maximum-length buffers plus
+  masking).
+* "DSpark Guide: Confidence Speculative Decoding in LLMs" (the Guide):
+  "1. The Mathematics of Suffix Decay" (alpha_k = min(1, P/Q_k);
+  P(accepted length >= L) = prod_{k<=L} alpha_k); "2. Confidence-Scheduled
+  Dynamic Verification" (C_k = prod_{i<=k} p_i; K* = max{k : C_k >= tau},
+  truncate at the first k with C_k < tau; the tutorial code keeps at least one).
+* "DSpark shows why fast AI inference is a scheduling problem, not a model
+  trick": the prefix survival probability, truncated below a threshold.
+
+Readings where the pages are silent (each also listed in the design notes):
+the bonus token on full acceptance is drawn from target row L_b; a zero
+residual (p == q) falls back to p; inverse-CDF draws walk token ids in
+ascending order and take the first id whose cumulative mass exceeds u * Z
+(fallback: the last id with positive mass); uniforms are laid out
+``u[b, k-1]`` for position k's accept test and ``u[b, K]`` for the single final
+draw; draft and target share the request's temperature and T = 0 selects the
+greedy rule; greedy ties go to the lowest id; the budget counts drafted
+positions only and is filled by (C desc, b asc, k asc) after reserving
+``min_len`` positions per request.
+
+Array conventions: target logits [B, K+1, V], draft logits [B, K, V], either
+float32 or bf16 given as uint16 bit patterns; drafted int32 [B, K]; lengths
+int32 [B]; temperature float32 [B]; uniforms float32 [B, K+1].
+
+Parity status: every function here is pinned by the CPU tests (closed forms,
+brute force, textbook special cases, hand-worked fixtures); no function is
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BOUNDARY = 1e-6  # uniforms this close to a decision edge may legitimately differ
+
+# device-status bits, same meaning as the library's (values fixed by the ABI)
+DEV_BAD_TOKEN = 1
+DEV_NONFINITE = 2
+DEV_BAD_TEMP = 4
+DEV_BAD_UNIFORM = 8
+DEV_BAD_CONF = 16
+
+
+def widen(a) -> np.ndarray:
+    """Exact widening to float64: bf16 bit patterns (uint16) or float32."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float32).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# Schedule: survival product, threshold truncation, global verify budget
+# ----------------------------------------------------------------------------
+
+def survival(conf) -> np.ndarray:
+    """C[b,k] = C[b,k-1] * c[b,k] in fp32, left to right (Guide, "2.
+    Confidence-Scheduled Dynamic Verification", C_k = prod_{i<=k} p_i).
+
+    The product is kept in fp32 with one correctly rounded multiply per step so
+    that the truncation decision below is reproducible bit for bit."""
+    conf = np.asarray(conf, dtype=np.float32)
+    C = np.empty_like(conf)
+    if conf.shape[1] == 0:
+        return C
+    C[:, 0] = conf[:, 0]
+    for k in range(1, conf.shape[1]):
+        C[:, k] = C[:, k - 1] * conf[:, k]          # float32 * float32 -> float32
+    return C
+
+
+def threshold_lengths(C, threshold, min_len) -> np.ndarray:
+    """L_thr[b] = number of leading positions with C >= tau (stop at the first
+    C < tau), floored at min_len (Guide, "Dynamic Verification Scheduling
+    Algorithm", step 3; Deep Dive, "The Full Scheduling Pipeline", 1 <= L)."""
+    tau = np.float32(threshold)
+    B, K = C.shape
+    out = np.empty(B, dtype=np.int32)
+    for b in range(B):
+        n = 0
+        while n < K and C[b, n] >= tau:
+            n += 1
+        out[b] = max(int(min_len), n)
+    return out
+
+
+def schedule(conf, threshold, budget, min_len=1):
+    """Return (lengths int32[B], mask uint8[B,K], survival float32[B,K]).
+
+    With ``budget >= 0`` and sum(L_thr) > budget, every request keeps
+    ``min_len`` positions and the remaining ``budget - B*min_len`` slots go to
+    the candidates (b, k), min_len < k <= L_thr[b], in order of C descending,
+    then b ascending, then k ascending (Deep Dive, "The Optimization Logic":
+    a slot goes to the most confident token in the batch).  L[b] is min_len
+    plus the number of row-b candidates taken."""
+    conf = np.asarray(conf, dtype=np.float32)
+    B, K = conf.shape
+    C = survival(conf)
+    L = threshold_lengths(C, threshold, min_len)
+    if budget >= 0 and int(L.sum()) > budget:
+        cands = [(b, k) for b in range(B) for k in range(min_len + 1, int(L[b]) + 1)]
+        # float comparison: -0.0 and +0.0 are the same key
+        cands.sort(key=lambda t: (-float(C[t[0], t[1] - 1]), t[0], t[1]))
+        take = budget - B * min_len
+        L = np.full(B, min_len, dtype=np.int32)
+        for (b, _k) in cands[:take]:
+            L[b] += 1
+    mask = (np.arange(1, K + 1)[None, :] <= L[:, None]).astype(np.uint8)
+    return L.astype(np.int32), mask, C
+
+
+# ----------------------------------------------------------------------------
+# Verification
+# ----------------------------------------------------------------------------
+
+def softmax_T(logits64: np.ndarray, T: float) -> np.ndarray:
+    """p(v) = exp((l_v - M)/T) / sum_w exp((l_w - M)/T), M = max l, in fp64."""
+    M = np.max(logits64)
+    e = np.exp((logits64 - M) / T)
+    return e / np.sum(e)
+
+
+def inverse_cdf(mass: np.ndarray, u: float):
+    """First token id whose cumulative mass exceeds u * Z, Z = total mass.
+
+    Returns (token, distance) where distance = min(|u - F(t-1)|, |u - F(t)|)
+    on the normalised CDF F (F(-1) = 0).  If rounding leaves no qualifying id,
+    the last id with positive mass is returned."""
+    cdf = np.cumsum(mass)
+    Z = cdf[-1]
+    hit = np.nonzero(cdf > u * Z)[0]
+    if hit.size:
+        t = int(hit[0])
+    else:
+        t = int(np.nonzero(mass > 0)[0][-1])
+    F_t = cdf[t] / Z
+    F_prev = cdf[t - 1] / Z if t > 0 else 0.0
+    return t, min(abs(u - F_prev), abs(u - F_t))
+
+
+def _row_flags(row64) -> int:
+    return DEV_NONFINITE if (np.isnan(row64).any() or np.isposinf(row64).any()) else 0
+
+
+def verify_request(target_b, draft_b, drafted_b, L, T, u_b):
+    """Verify one request.
+
+    target_b [K+1, V], draft_b [K, V] (raw arrays), drafted_b [K], L in 0..K,
+    T float32 value, u_b [K+1].  Returns a dict with accepted, tokens [K+1],
+    p_tok [K], q_tok [K], dist (smallest distance of any evaluated decision to
+    its edge; inf when nothing was drawn), flags."""
+    K = target_b.shape[0] - 1
+    V = target_b.shape[1]
+    T = float(np.float32(T))
+    tokens = np.full(K + 1, -1, dtype=np.int32)
+    p_tok = np.zeros(K, dtype=np.float64)
+    q_tok = np.zeros(K, dtype=np.float64)
+    flags = 0
+    y = [int(v) for v in drafted_b[:L]]
+    if any(v < 0 or v >= V for v in y):
+        flags |= DEV_BAD_TOKEN
+    if not (T >= 0.0):                        # negative or NaN
+        flags |= DEV_BAD_TEMP
+    if flags:
+        return dict(accepted=0, tokens=tokens, p_tok=p_tok, q_tok=q_tok,
+                    dist=np.inf, flags=flags)
+
+    if T == 0.0:
+        # greedy rule (T = 0): accept y_k iff it is the lowest-index argmax of
+        # target row k-1; emit the argmax at the first mismatch (or row L).
+        g = []
+        for j in range(L + 1):
+            row = widen(target_b[j])
+            flags |= _row_flags(row)
+            g.append(int(np.argmax(row)))      # first maximal index
+        a = L
+        for k in range(1, L + 1):
+            if y[k - 1] != g[k - 1]:
+                a = k - 1
+                break
+        tokens[:a] = y[:a]
+        tokens[a] = g[a]
+        return dict(accepted=a, tokens=tokens, p_tok=p_tok, q_tok=q_tok,
+                    dist=np.inf, flags=flags)
+
+    u = np.asarray(u_b, dtype=np.float32).astype(np.float64)
+    used_u = list(range(L)) + [K]
+    if any(not (0.0 <= u[i] < 1.0) for i in used_u):
+        flags |= DEV_BAD_UNIFORM
+
+    # temperature softmaxes of every scheduled row (Deep Dive, "Speculative
+    # Decoding From First Principles"; both distributions at the request's T)
+    P = []
+    Q = []
+    for j in range(L + 1):
+        row = widen(target_b[j])
+        flags |= _row_flags(row)
+        P.append(softmax_T(row, T))
+    for j in range(L):
+        row = widen(draft_b[j])
+        flags |= _row_flags(row)
+        Q.append(softmax_T(row, T))
+
+    alpha = np.zeros(L)
+    for k in range(1, L + 1):
+        py = P[k - 1][y[k - 1]]
+        qy = Q[k - 1][y[k - 1]]
+        p_tok[k - 1] = py
+        q_tok[k - 1] = qy
+        # alpha_k = min(1, p/q) (Guide, "1. The Mathematics of Suffix Decay")
+        if py == 0.0:
+            alpha[k - 1] = 0.0
+        elif qy == 0.0:
+            alpha[k - 1] = 1.0
+        else:
+            alpha[k - 1] = min(1.0, py / qy)
+
+    # first rejection: accept position k iff u[k-1] < alpha_k
+    a = L
+    for k in range(1, L + 1):
+        if not (u[k - 1] < alpha[k - 1]):
+            a = k - 1
+            break
+    dist = np.inf
+    for k in range(1, min(a + 1, L) + 1):
+        dist = min(dist, abs(u[k - 1] - alpha[k - 1]))
+
+    if a < L:
+        # residual max(0, p - q) at the rejected position, normalised;
+        # an all-zero residual falls back to p
+        r = np.maximum(0.0, P[a] - Q[a])
+        mass = r if np.sum(r) > 0.0 else P[a]
+    else:
+        # full acceptance: bonus token from the row after the last draft
+        mass = P[L]
+    t, d = inverse_cdf(mass, u[K])
+    dist = min(dist, d)
+    tokens[:a] = y[:a]
+    tokens[a] = t
+    return dict(accepted=a, tokens=tokens, p_tok=p_tok, q_tok=q_tok, dist=dist,
+                flags=flags)
+
+
+def verify(target, draft, drafted, lengths, temperature, uniforms, requests=None):
+    """Batched verification.  ``lengths=None`` verifies all K positions.
+    ``requests`` restricts the work to a subset of request indices (the other
+    rows of the outputs stay at their fill values).
+
+    Returns dict(accepted int32[B], tokens int32[B,K+1], p_tok float64[B,K],
+    q_tok float64[B,K], dist float64[B], flags int)."""
+    B, K1, V = target.shape
+    K = K1 - 1
+    accepted = np.zeros(B, dtype=np.int32)
+    tokens = np.full((B, K + 1), -1, dtype=np.int32)
+    p_tok = np.zeros((B, K))
+    q_tok = np.zeros((B, K))
+    dist = np.full(B, np.inf)
+    flags = 0
+    idx = range(B) if requests is None else requests
+    for b in idx:
+        L = K if lengths is None else int(lengths[b])
+        r = verify_request(target[b], draft[b], drafted[b], L, temperature[b], uniforms[b])
+        accepted[b] = r["accepted"]
+        tokens[b] = r["tokens"]
+        p_tok[b] = r["p_tok"]
+        q_tok[b] = r["q_tok"]
+        dist[b] = r["dist"]
+        flags |= r["flags"]
+    return dict(accepted=accepted, tokens=tokens, p_tok=p_tok, q_tok=q_tok,
+                dist=dist, flags=flags)
+
+
+def verify_greedy(target, drafted, lengths, requests=None):
+    """Greedy (T = 0) verification of every request: returns
+    dict(accepted, tokens, flags)."""
+    B, K1, V = target.shape
+    K = K1 - 1
+    temp = np.zeros(B, dtype=np.float32)
+    u = np.zeros((B, K + 1), dtype=np.float32)
+    # at T = 0 the draft rows are never read; pass the target rows as a stand-in
+    r = verify(target, target[:, :K], drafted, lengths, temp, u, requests=requests)
+    return dict(accepted=r["accepted"], tokens=r["tokens"], flags=r["flags"])
