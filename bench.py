@@ -1,0 +1,217 @@
+"""Benchmark: verified draft positions per second and achieved HBM bandwidth of
+confidence-scheduled block verification on one MI355X.
+
+One step = dspark_schedule + dspark_verify over one batch of the
+V=151936, B=64, K=16 workload (bf16 logits, T=1, threshold 0.2, budget 512;
+seeded synthetic inputs resident in HBM).  Three input sets (seed offsets
+0, 100, 200; 641 MB each) rotate so that no step reads logits left in the
+256 MB last-level cache by the step before.
+
+Prints ONE JSON line on stdout.  ``value`` = sum of verified positions
+(sum_b L_b) per second of schedule + verify.  ``roofline`` reports the verify
+call against the 8 TB/s HBM peak using the algorithmic bytes
+s*V*(sum_{T>0}[(2 L_b + 1) + 2*rejected_b] + sum_{T=0}(L_b + 1)), timed with HIP
+events on the stream the kernels run on.  ``cpu_baseline`` times the CPU
+oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "verified draft positions/sec and achieved HBM GB/s vs peak (V=151936, B=64, K=16)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w, lengths, accepted, temperature) -> int:
+    """Bytes the prescribed streaming design must read for one verify call."""
+    s = 2 if w.dtype == "bf16" else 4
+    L = lengths.astype("int64")
+    a = accepted.astype("int64")
+    T = temperature
+    soft = T > 0
+    rows = ((2 * L + 1) + 2 * (a < L)) * soft + (L + 1) * (~soft)
+    return int(s * w.V * rows.sum())
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--sets", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this path runs on a "
+              f"single device and has no multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import draft_verification_dspark_amd as ds
+    import workloads
+
+    ds.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"device: {torch.cuda.get_device_name(dev)}")
+
+    sets = [workloads.make(args.workload, seed_offset=100 * i, device=dev) for i in range(args.sets)]
+    w0 = sets[0]
+    B, K, V = w0.B, w0.K, w0.V
+    log(f"workload {w0.name}: B={B} K={K} V={V} {w0.dtype}; {args.sets} input sets")
+
+    # preallocated outputs and workspaces (the library never allocates)
+    outs = []
+    for w in sets:
+        outs.append(dict(
+            lengths=torch.empty(B, dtype=torch.int32, device=dev),
+            mask=torch.empty((B, K), dtype=torch.uint8, device=dev),
+            surv=torch.empty((B, K), dtype=torch.float32, device=dev),
+            acc=torch.empty(B, dtype=torch.int32, device=dev),
+            tok=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+            pt=torch.empty((B, K), dtype=torch.float32, device=dev),
+            qt=torch.empty((B, K), dtype=torch.float32, device=dev),
+            st=torch.zeros(1, dtype=torch.int32, device=dev)))
+    ws_s = ds.workspace(ds.OP_SCHEDULE, B, K, 1, dev)
+    ws_v = ds.workspace(ds.OP_VERIFY, B, K, V, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        w, o = sets[i % len(sets)], outs[i % len(sets)]
+        ds.schedule(w.conf, w.threshold, w.budget, w.min_len, lengths=o["lengths"], mask=o["mask"],
+                    survival=o["surv"], dev_status=o["st"], ws=ws_s, stream=stream)
+        ds.verify(w.target, w.draft, w.drafted, o["lengths"], w.temperature, w.uniforms,
+                  accepted=o["acc"], tokens=o["tok"], p_tok=o["pt"], q_tok=o["qt"],
+                  dev_status=o["st"], ws=ws_v, stream=stream)
+
+    def step_events(i, e0, e1, e2):
+        w, o = sets[i % len(sets)], outs[i % len(sets)]
+        e0.record(stream)
+        ds.schedule(w.conf, w.threshold, w.budget, w.min_len, lengths=o["lengths"], mask=o["mask"],
+                    survival=o["surv"], dev_status=o["st"], ws=ws_s, stream=stream)
+        e1.record(stream)
+        ds.verify(w.target, w.draft, w.drafted, o["lengths"], w.temperature, w.uniforms,
+                  accepted=o["acc"], tokens=o["tok"], p_tok=o["pt"], q_tok=o["qt"],
+                  dev_status=o["st"], ws=ws_v, stream=stream)
+        e2.record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    # per-set positions and algorithmic bytes (outputs are deterministic per set)
+    pos, nbytes, accs = [], [], []
+    for i in range(len(sets)):
+        o, w = outs[i], sets[i]
+        L = o["lengths"].cpu().numpy()
+        a = o["acc"].cpu().numpy()
+        assert int(o["st"].item()) == 0, "device status flags set on synthetic inputs"
+        pos.append(int(L.sum()))
+        nbytes.append(algorithmic_bytes(w, L, a, w.temperature.cpu().numpy()))
+        accs.append((a, L))
+
+    # timed region: K steps, events around each call
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step_events(i, *ev[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    sched_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    ver_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    n_pos = sum(pos[i % len(sets)] for i in range(args.steps))
+    n_bytes = sum(nbytes[i % len(sets)] for i in range(args.steps))
+    value = n_pos / (total_ms / 1e3)
+    verify_gbs = n_bytes / (sum(ver_ms) / 1e3) / 1e9
+    log(f"timed {args.steps} steps: {total_ms:.3f} ms; schedule median {np.median(sched_ms)*1e3:.1f} us, "
+        f"verify median {np.median(ver_ms)*1e3:.1f} us; verify {verify_gbs:.0f} GB/s")
+    mean_acc = float(np.mean([a.mean() for a, _ in accs]))
+    waste = float(np.mean([1 - a.sum() / max(1, L.sum()) for a, L in accs]))
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w0.name}: V={V}, B={B}, K={K}, bf16 logits, T=1, threshold 0.2, budget 512",
+            "logits": w0.dtype,
+            "input_sets": len(sets),
+            "positions_per_step": pos,
+            "verify_bytes_per_call": nbytes,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "dspark_verify (plan, pass1, finalize, pass2, sample launches)",
+            "achieved": round(verify_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(verify_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "verify_us_median": round(float(np.median(ver_ms)) * 1e3, 2),
+            "schedule_us_median": round(float(np.median(sched_ms)) * 1e3, 2),
+        },
+        "accepted_mean": round(mean_acc, 3),
+        "waste_ratio": round(waste, 4),
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        cw = sets[0]
+        conf = workloads.to_numpy(cw.conf)
+        tgt = workloads.to_numpy(cw.target)
+        dft = workloads.to_numpy(cw.draft)
+        y = workloads.to_numpy(cw.drafted)
+        T = workloads.to_numpy(cw.temperature)
+        u = workloads.to_numpy(cw.uniforms)
+        runs, cpu_pos, t0 = 0, 0, time.perf_counter()
+        while True:
+            L, _, _ = oracle.schedule(conf, cw.threshold, cw.budget, cw.min_len)
+            oracle.verify(tgt, dft, y, L, T, u)
+            runs += 1
+            cpu_pos += int(L.sum())
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or runs >= 50:
+                break
+        result["cpu_baseline"] = {
+            "value": round(cpu_pos / el, 2),
+            "unit": "positions/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"{runs} full step(s) (schedule + verify, all {B} requests) of {cw.name} "
+                      f"seed+0, {el:.1f} s wall, numpy fp64, single thread",
+        }
+        log(f"cpu oracle: {runs} runs in {el:.1f} s")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,226 @@
+"""Python binding of the gfx950 verify/schedule library (``libdspark.so``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/dspark.h``.  PyTorch provides
+device memory and the current stream.  There is no fallback: if the library
+has not been built (``python -m draft_verification_dspark_amd.build`` or
+``__graft_entry__.build()``), loading raises.
+
+Names follow the C ABI: ``dspark_schedule``, ``dspark_verify``,
+``dspark_verify_greedy``, ``dspark_workspace_bytes``, ``dspark_status_string``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdspark.so")
+
+DSPARK_OK = 0
+DSPARK_F32 = 0
+DSPARK_BF16 = 1
+OP_SCHEDULE, OP_VERIFY, OP_VERIFY_GREEDY = 0, 1, 2
+
+DEV_BAD_TOKEN = 1
+DEV_NONFINITE = 2
+DEV_BAD_TEMP = 4
+DEV_BAD_UNIFORM = 8
+DEV_BAD_CONF = 16
+DEV_BAD_LENGTH = 32
+
+EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_schedule",
+           "dspark_verify", "dspark_verify_greedy")
+
+
+class DsparkError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"dspark status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load (once) and type the C ABI.  Raises if the library is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run python -m draft_verification_dspark_amd.build")
+    lib = ctypes.CDLL(path)
+    vp, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    lib.dspark_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.dspark_workspace_bytes.restype = sz
+    lib.dspark_status_string.argtypes = [i32]
+    lib.dspark_status_string.restype = ctypes.c_char_p
+    lib.dspark_schedule.argtypes = [vp, i32, i32, f32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.dspark_schedule.restype = i32
+    lib.dspark_verify.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                  vp, sz, vp]
+    lib.dspark_verify.restype = i32
+    lib.dspark_verify_greedy.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dspark_verify_greedy.restype = i32
+    _lib = lib
+    return lib
+
+
+def dspark_status_string(status: int) -> str:
+    return load_library().dspark_status_string(int(status)).decode()
+
+
+def dspark_workspace_bytes(op: int, B: int, K: int, V: int) -> int:
+    return int(load_library().dspark_workspace_bytes(int(op), int(B), int(K), int(V)))
+
+
+def _check(status: int):
+    if status != DSPARK_OK:
+        raise DsparkError(status, dspark_status_string(status))
+
+
+# ---------------------------------------------------------------- torch glue
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _req(t, name, dtype, shape, device):
+    torch = _torch()
+    if t.device != device or t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on {device}, got "
+                         f"{t.dtype} {tuple(t.shape)} on {t.device} contiguous={t.is_contiguous()}")
+    return t
+
+
+_ws_cache = {}
+
+
+class Workspace:
+    """Caller-owned workspace: a device byte buffer aligned to 256 bytes."""
+
+    def __init__(self, nbytes: int, device):
+        torch = _torch()
+        self.buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        self.ptr = (self.buf.data_ptr() + 255) // 256 * 256
+        self.nbytes = nbytes
+
+
+def workspace(op: int, B: int, K: int, V: int, device) -> Workspace:
+    """Cached workspace for (device, op, B, K, V)."""
+    torch = _torch()
+    device = torch.device(device)
+    key = (device.index, op, B, K, V)
+    ws = _ws_cache.get(key)
+    if ws is None:
+        nbytes = dspark_workspace_bytes(op, B, K, V)
+        if nbytes == 0:
+            raise DsparkError(2, "bad sizes for the workspace query")
+        ws = Workspace(nbytes, device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def _stream(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return DSPARK_BF16
+    if t.dtype == torch.float32:
+        return DSPARK_F32
+    raise ValueError(f"logits dtype {t.dtype} not supported (bf16 or fp32)")
+
+
+def schedule(conf, threshold: float, budget: int, min_len: int = 1, *, lengths=None, mask=None,
+             survival=None, dev_status=None, ws: Optional[Workspace] = None, stream=None):
+    """dspark_schedule on torch tensors.  Returns (lengths, mask, survival, dev_status)."""
+    torch = _torch()
+    lib = load_library()
+    dev = conf.device
+    B, K = conf.shape
+    _req(conf, "conf", torch.float32, (B, K), dev)
+    lengths = torch.empty(B, dtype=torch.int32, device=dev) if lengths is None else \
+        _req(lengths, "lengths", torch.int32, (B,), dev)
+    mask = torch.empty((B, K), dtype=torch.uint8, device=dev) if mask is None else \
+        _req(mask, "mask", torch.uint8, (B, K), dev)
+    survival = torch.empty((B, K), dtype=torch.float32, device=dev) if survival is None else \
+        _req(survival, "survival", torch.float32, (B, K), dev)
+    if dev_status is None:
+        dev_status = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = ws or workspace(OP_SCHEDULE, B, K, 1, dev)
+    st = lib.dspark_schedule(_ptr(conf), B, K, float(threshold), int(budget), int(min_len),
+                             _ptr(lengths), _ptr(mask), _ptr(survival), _ptr(dev_status),
+                             ws.ptr, ws.nbytes, _stream(stream, dev))
+    _check(st)
+    return lengths, mask, survival, dev_status
+
+
+def verify(target, draft, drafted, lengths, temperature, uniforms, *, accepted=None, tokens=None,
+           p_tok=None, q_tok=None, dev_status=None, ws: Optional[Workspace] = None, stream=None,
+           want_probs: bool = True):
+    """dspark_verify on torch tensors.  ``lengths=None`` verifies all K.
+    Returns dict(accepted, tokens, p_tok, q_tok, dev_status)."""
+    torch = _torch()
+    lib = load_library()
+    dev = target.device
+    B, K1, V = target.shape
+    K = K1 - 1
+    code = _dtype_code(target)
+    _req(target, "target", target.dtype, (B, K + 1, V), dev)
+    _req(draft, "draft", target.dtype, (B, K, V), dev)
+    _req(drafted, "drafted", torch.int32, (B, K), dev)
+    if lengths is not None:
+        _req(lengths, "lengths", torch.int32, (B,), dev)
+    _req(temperature, "temperature", torch.float32, (B,), dev)
+    _req(uniforms, "uniforms", torch.float32, (B, K + 1), dev)
+    accepted = torch.empty(B, dtype=torch.int32, device=dev) if accepted is None else accepted
+    tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev) if tokens is None else tokens
+    if want_probs:
+        p_tok = torch.empty((B, K), dtype=torch.float32, device=dev) if p_tok is None else p_tok
+        q_tok = torch.empty((B, K), dtype=torch.float32, device=dev) if q_tok is None else q_tok
+    if dev_status is None:
+        dev_status = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = ws or workspace(OP_VERIFY, B, K, V, dev)
+    st = lib.dspark_verify(_ptr(target), _ptr(draft), code, B, K, V, _ptr(drafted), _ptr(lengths),
+                           _ptr(temperature), _ptr(uniforms), _ptr(accepted), _ptr(tokens),
+                           _ptr(p_tok), _ptr(q_tok), _ptr(dev_status), ws.ptr, ws.nbytes,
+                           _stream(stream, dev))
+    _check(st)
+    return dict(accepted=accepted, tokens=tokens, p_tok=p_tok, q_tok=q_tok, dev_status=dev_status)
+
+
+def verify_greedy(target, drafted, lengths, *, accepted=None, tokens=None, dev_status=None,
+                  ws: Optional[Workspace] = None, stream=None):
+    """dspark_verify_greedy on torch tensors.  Returns dict(accepted, tokens, dev_status)."""
+    torch = _torch()
+    lib = load_library()
+    dev = target.device
+    B, K1, V = target.shape
+    K = K1 - 1
+    code = _dtype_code(target)
+    _req(target, "target", target.dtype, (B, K + 1, V), dev)
+    _req(drafted, "drafted", torch.int32, (B, K), dev)
+    if lengths is not None:
+        _req(lengths, "lengths", torch.int32, (B,), dev)
+    accepted = torch.empty(B, dtype=torch.int32, device=dev) if accepted is None else accepted
+    tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev) if tokens is None else tokens
+    if dev_status is None:
+        dev_status = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = ws or workspace(OP_VERIFY_GREEDY, B, K, V, dev)
+    st = lib.dspark_verify_greedy(_ptr(target), code, B, K, V, _ptr(drafted), _ptr(lengths),
+                                  _ptr(accepted), _ptr(tokens), _ptr(dev_status), ws.ptr,
+                                  ws.nbytes, _stream(stream, dev))
+    _check(st)
+    return dict(accepted=accepted, tokens=tokens, dev_status=dev_status)

@@ -1,0 +1,47 @@
+"""Build the gfx950 shared library ``libdspark.so`` in-tree with hipcc.
+
+Every HIP source under ``csrc/`` is compiled in one hipcc invocation; the
+C ABI is declared in ``include/dspark.h`` at the repository root."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SOURCES = ["api.hip", "schedule.hip", "verify.hip"]
+LIB = os.path.join(HERE, "libdspark.so")
+
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
+    # exact control of rounding: no implicit contraction into FMA
+    "-ffp-contract=off",
+    # only the C ABI is exported
+    "-fvisibility=hidden",
+    # never emit packed fp32 arithmetic
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def build(verbose: bool = False) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    srcs = [os.path.join(HERE, "csrc", s) for s in SOURCES]
+    tmp = LIB + ".tmp"
+    cmd = [hipcc, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
+           *srcs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

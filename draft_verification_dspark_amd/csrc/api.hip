@@ -1,0 +1,164 @@
+// C ABI entry points: synchronous argument checks, workspace carving and
+// kernel launches on the caller's stream.  No allocation, no synchronisation.
+#include <hip/hip_runtime.h>
+
+#include "args.hpp"
+
+namespace dspark {
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxB = 1 << 24;
+constexpr int kMaxK = 64;
+
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct VerifyLayout {
+  size_t req, n_rows, rows, part1, part2, total;
+};
+
+VerifyLayout verify_layout(int B, int K, int V) {
+  VerifyLayout L;
+  const size_t R = (size_t)2 * K + 1;
+  const size_t G = (size_t)chunks_per_row_max(V);
+  size_t off = 0;
+  L.req = off;    off += up(sizeof(ReqState) * (size_t)B);
+  L.n_rows = off; off += kAlign;
+  L.rows = off;   off += up(sizeof(int32_t) * (size_t)B * R);
+  L.part1 = off;  off += up(sizeof(Partial) * (size_t)B * R * G);
+  L.part2 = off;  off += up(sizeof(double) * (size_t)B * G);
+  L.total = off;
+  return L;
+}
+
+struct ScheduleLayout {
+  size_t surv, lthr, total;
+};
+
+ScheduleLayout schedule_layout(int B, int K) {
+  ScheduleLayout L;
+  size_t off = 0;
+  L.surv = off; off += up(sizeof(float) * (size_t)B * K);
+  L.lthr = off; off += up(sizeof(int32_t) * (size_t)B);
+  L.total = off;
+  return L;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+}  // namespace dspark
+
+using namespace dspark;
+
+extern "C" {
+
+size_t dspark_workspace_bytes(int op, int B, int K, int V) {
+  if (B < 1 || K < 1 || B > kMaxB) return 0;
+  if (op == DSPARK_OP_SCHEDULE) return schedule_layout(B, K).total;
+  if (op == DSPARK_OP_VERIFY || op == DSPARK_OP_VERIFY_GREEDY) {
+    if (V < 1 || K > kMaxK) return 0;
+    return verify_layout(B, K, V).total;
+  }
+  return 0;
+}
+
+const char* dspark_status_string(int status) {
+  switch (status) {
+    case DSPARK_OK: return "ok";
+    case DSPARK_ERR_NULL: return "a required pointer is NULL";
+    case DSPARK_ERR_SHAPE: return "B, K or V out of range";
+    case DSPARK_ERR_DTYPE: return "unknown logits dtype";
+    case DSPARK_ERR_BUDGET: return "budget below B*min_len or min_len outside [0,K]";
+    case DSPARK_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case DSPARK_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int dspark_schedule(const float* conf, int B, int K, float threshold, int budget, int min_len,
+                    int32_t* lengths, uint8_t* mask, float* survival, int32_t* dev_status,
+                    void* workspace, size_t ws_bytes, void* stream) {
+  if (!conf || !lengths || !dev_status || !workspace) return DSPARK_ERR_NULL;
+  if (B < 1 || K < 1 || B > kMaxB || (long long)B * K > (1LL << 30)) return DSPARK_ERR_SHAPE;
+  if (min_len < 0 || min_len > K) return DSPARK_ERR_BUDGET;
+  if (budget >= 0 && (long long)budget < (long long)B * min_len) return DSPARK_ERR_BUDGET;
+  const ScheduleLayout L = schedule_layout(B, K);
+  if (ws_bytes < L.total || !aligned(workspace, kAlign)) return DSPARK_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  ScheduleArgs a;
+  a.conf = conf;
+  a.B = B;
+  a.K = K;
+  a.tau = threshold;
+  a.budget = budget;
+  a.min_len = min_len;
+  a.lengths = lengths;
+  a.mask = mask;
+  a.surv = survival ? survival : reinterpret_cast<float*>(ws + L.surv);
+  a.lthr = reinterpret_cast<int32_t*>(ws + L.lthr);
+  a.dev_status = dev_status;
+  return launch_schedule(a, static_cast<hipStream_t>(stream));
+}
+
+static int verify_common(const void* target, const void* draft, int dtype, int B, int K, int V,
+                         const int32_t* drafted, const int32_t* lengths, const float* temperature,
+                         const float* uniforms, int32_t* accepted, int32_t* tokens, float* p_tok,
+                         float* q_tok, int32_t* dev_status, void* workspace, size_t ws_bytes,
+                         void* stream, int greedy_only) {
+  if (!target || !drafted || !accepted || !tokens || !dev_status || !workspace)
+    return DSPARK_ERR_NULL;
+  if (!greedy_only && (!draft || !temperature || !uniforms)) return DSPARK_ERR_NULL;
+  if (B < 1 || K < 1 || V < 1 || K > kMaxK || B > kMaxB || V > (1 << 30)) return DSPARK_ERR_SHAPE;
+  if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return DSPARK_ERR_DTYPE;
+  const VerifyLayout L = verify_layout(B, K, V);
+  if (ws_bytes < L.total || !aligned(workspace, kAlign)) return DSPARK_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  VerifyArgs a;
+  a.target = target;
+  a.draft = greedy_only ? nullptr : draft;
+  a.drafted = drafted;
+  a.lengths = lengths;
+  a.temperature = temperature;
+  a.uniforms = uniforms;
+  a.accepted = accepted;
+  a.tokens = tokens;
+  a.p_tok = greedy_only ? nullptr : p_tok;
+  a.q_tok = greedy_only ? nullptr : q_tok;
+  a.dev_status = dev_status;
+  a.req = reinterpret_cast<ReqState*>(ws + L.req);
+  a.n_rows = reinterpret_cast<int32_t*>(ws + L.n_rows);
+  a.rows = reinterpret_cast<int32_t*>(ws + L.rows);
+  a.part1 = reinterpret_cast<Partial*>(ws + L.part1);
+  a.part2 = reinterpret_cast<double*>(ws + L.part2);
+  a.B = B;
+  a.K = K;
+  a.V = V;
+  const int per_vec = dtype == DSPARK_BF16 ? 8 : 4;
+  a.G = dtype == DSPARK_BF16 ? chunks_per_row<DSPARK_BF16>(V) : chunks_per_row<DSPARK_F32>(V);
+  a.greedy_only = greedy_only;
+  a.vec_ok = (V % per_vec == 0) && aligned(target, 16) && (greedy_only || aligned(draft, 16));
+  return launch_verify(a, dtype, static_cast<hipStream_t>(stream));
+}
+
+int dspark_verify(const void* target_logits, const void* draft_logits, int dtype, int B, int K,
+                  int V, const int32_t* drafted, const int32_t* lengths,
+                  const float* temperature, const float* uniforms, int32_t* accepted,
+                  int32_t* tokens, float* p_tok, float* q_tok, int32_t* dev_status,
+                  void* workspace, size_t ws_bytes, void* stream) {
+  return verify_common(target_logits, draft_logits, dtype, B, K, V, drafted, lengths, temperature,
+                       uniforms, accepted, tokens, p_tok, q_tok, dev_status, workspace, ws_bytes,
+                       stream, 0);
+}
+
+int dspark_verify_greedy(const void* target_logits, int dtype, int B, int K, int V,
+                         const int32_t* drafted, const int32_t* lengths, int32_t* accepted,
+                         int32_t* tokens, int32_t* dev_status, void* workspace, size_t ws_bytes,
+                         void* stream) {
+  return verify_common(target_logits, nullptr, dtype, B, K, V, drafted, lengths, nullptr, nullptr,
+                       accepted, tokens, nullptr, nullptr, dev_status, workspace, ws_bytes, stream,
+                       1);
+}
+
+}  // extern "C"

@@ -1,0 +1,193 @@
+/*
+ * dspark.h — C ABI of the MI355X (gfx950) library for confidence-scheduled
+ * block verification in speculative decoding.
+ *
+ * Three calls make up the data-parallel hot path of one decoding round:
+ *
+ *   dspark_schedule       survival product, threshold truncation and a global
+ *                         verify-token budget (which drafted positions go to
+ *                         the target model);
+ *   dspark_verify         temperature softmaxes of target and draft rows,
+ *                         lossless rejection sampling up to the first
+ *                         rejection, and the correction (residual) or bonus
+ *                         draw; requests with temperature 0 use the greedy rule;
+ *   dspark_verify_greedy  the greedy (T = 0) rule for the whole batch.
+ *
+ * Sources (page title, then section):
+ *   "DSpark Deep Dive: How DeepSeek Squeezed an 85% Speedup Out of Inference
+ *    Without Touching a Single Model Weight" — "Speculative Decoding From First
+ *    Principles" (draft, verify in one target pass, accept with probability
+ *    min(1, p/q), resample a rejection from the normalised positive part of
+ *    p - q), "Variable-Length Drafts", "The Optimization Logic", "GPU-Resident
+ *    Scheduling" (scheduler on the GPU; maximum-length buffers plus masking so
+ *    that variable lengths fit a fixed launch), "The Full Scheduling Pipeline"
+ *    (1 <= L <= K; drafted tokens past L are discarded).
+ *   "DSpark Guide: Confidence Speculative Decoding in LLMs" — "1. The
+ *    Mathematics of Suffix Decay" (alpha_k = min(1, P/Q_k)), "2. Confidence-
+ *    Scheduled Dynamic Verification" (C_k = prod_{i<=k} p_i, truncate at the
+ *    first k with C_k < tau).
+ *   "DSpark shows why fast AI inference is a scheduling problem, not a model
+ *    trick" — prefix survival probability cut at a threshold.
+ *
+ * Conventions shared by every call:
+ *   - All array arguments are DEVICE pointers owned by the caller; the
+ *     library never allocates, frees or synchronises. Work is enqueued on
+ *     `stream` (a hipStream_t passed as void*; NULL = the default stream) and
+ *     outputs are valid once the stream reaches the call. Every call is a
+ *     fixed sequence of kernel launches whose shape depends only on the
+ *     scalar arguments, so it can be captured in a HIP graph.
+ *   - Arrays are dense, row-major, with the shapes given below; logits rows
+ *     must start on 16-byte boundaries for the vectorised path (a row-wise
+ *     scalar path handles any other V).
+ *   - Indices: b = request 0..B-1; drafted position k = 1..K is stored at
+ *     column k-1. Target row j (0..K) is the target distribution for the
+ *     token after the prefix plus the first j drafted tokens; row j = k-1
+ *     scores drafted token y_k and row L_b is the bonus row. Draft row j
+ *     (0..K-1) is the distribution drafted token y_{j+1} came from.
+ *   - The return value is a synchronous status (argument checks only; no
+ *     launch happens unless it is DSPARK_OK). Faults found in the DATA are
+ *     OR-ed as DSPARK_DEV_* bits into *dev_status (the caller zeroes it);
+ *     outputs of an affected request are then unspecified but every access
+ *     stays in bounds.
+ *   - `workspace` is caller-allocated device memory of at least
+ *     dspark_workspace_bytes(op, B, K, V) bytes, 256-byte aligned. Calls that
+ *     run concurrently need distinct workspaces. Nothing in it needs to be
+ *     initialised.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define DSPARK_API __attribute__((visibility("default")))
+#else
+#define DSPARK_API
+#endif
+
+typedef enum {
+  DSPARK_OK = 0,
+  DSPARK_ERR_NULL = 1,      /* a required pointer is NULL                         */
+  DSPARK_ERR_SHAPE = 2,     /* B, K or V out of range (B,K,V >= 1; K <= 64 for verify) */
+  DSPARK_ERR_DTYPE = 3,     /* unknown logits dtype                               */
+  DSPARK_ERR_BUDGET = 4,    /* budget >= 0 but < B*min_len, or min_len not in [0,K] */
+  DSPARK_ERR_WORKSPACE = 5, /* ws_bytes too small or workspace misaligned         */
+  DSPARK_ERR_LAUNCH = 6     /* the HIP runtime rejected a launch                  */
+} dspark_status;
+
+typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
+
+/* Device status bits (OR-ed into *dev_status). */
+#define DSPARK_DEV_BAD_TOKEN 1    /* a drafted id that is read lies outside [0, V)      */
+#define DSPARK_DEV_NONFINITE 2    /* a row that is read holds NaN or +Inf, or no finite logit (-Inf alone is legal) */
+#define DSPARK_DEV_BAD_TEMP 4     /* temperature < 0 or NaN                              */
+#define DSPARK_DEV_BAD_UNIFORM 8  /* a uniform that is read lies outside [0, 1)          */
+#define DSPARK_DEV_BAD_CONF 16    /* a confidence is NaN or outside [0, 1]               */
+#define DSPARK_DEV_BAD_LENGTH 32  /* lengths[b] outside [0, K] (clamped)                 */
+
+#define DSPARK_OP_SCHEDULE 0
+#define DSPARK_OP_VERIFY 1
+#define DSPARK_OP_VERIFY_GREEDY 2
+
+/* Bytes of workspace `op` needs for these sizes (0 for bad sizes). */
+DSPARK_API size_t dspark_workspace_bytes(int op, int B, int K, int V);
+
+/* Static text for a dspark_status value. */
+DSPARK_API const char* dspark_status_string(int status);
+
+/*
+ * dspark_schedule — which drafted positions are verified.
+ *
+ * Defines (DSpark Guide, "2. Confidence-Scheduled Dynamic Verification";
+ * DSpark Deep Dive, "Variable-Length Drafts", "The Optimization Logic"):
+ *   C[b,1] = conf[b,1];  C[b,k] = fp32(C[b,k-1] * conf[b,k])   (left to right)
+ *   Lthr[b] = max(min_len, number of leading k with C[b,k] >= threshold)
+ *   if budget >= 0 and sum_b Lthr[b] > budget:
+ *     each request keeps min_len positions; the other budget - B*min_len
+ *     slots go to candidates (b,k), min_len < k <= Lthr[b], ordered by C
+ *     descending, then b ascending, then k ascending;
+ *     lengths[b] = min_len + (number of row-b candidates taken)
+ *   else lengths[b] = Lthr[b].
+ * For confidences in [0,1] the survival is non-increasing in k, so the
+ * selected set is a prefix of every row and the budget fill maximises the
+ * total survival of the verified positions.
+ *
+ *   conf      [B,K] float32 per-position confidence, expected in [0,1]
+ *   threshold survival threshold tau (compared as fp32)
+ *   budget    total drafted positions to verify, < 0 = no budget
+ *   min_len   positions every request keeps (1 by default; 0 allowed)
+ *   lengths   [B] int32 out, min_len <= lengths[b] <= K
+ *   mask      [B,K] uint8 out, mask[b,k-1] = (k <= lengths[b]); may be NULL
+ *   survival  [B,K] float32 out C[b,k]; may be NULL
+ * Errors: NULL conf/lengths/dev_status/workspace; B < 1 or K < 1;
+ * min_len outside [0,K]; 0 <= budget < B*min_len; small workspace.
+ */
+DSPARK_API int dspark_schedule(const float* conf, int B, int K, float threshold, int budget, int min_len,
+                    int32_t* lengths, uint8_t* mask, float* survival,
+                    int32_t* dev_status, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * dspark_verify — lossless block verification.
+ *
+ * For every request b with T = temperature[b] > 0 and L = lengths[b]
+ * (DSpark Deep Dive, "Speculative Decoding From First Principles";
+ * DSpark Guide, "1. The Mathematics of Suffix Decay"):
+ *   p_k = softmax(target[b,k-1,:] / T),  q_k = softmax(draft[b,k-1,:] / T)
+ *   alpha_k = min(1, p_k(y_k) / q_k(y_k))  (0 if p_k(y_k) = 0, 1 if only q is 0)
+ *   a = (first k <= L with NOT uniforms[b,k-1] < alpha_k) - 1, or L if none
+ *   if a < L: t drawn from r = max(0, p_{a+1} - q_{a+1}) / sum(r)
+ *             (r == 0 everywhere: drawn from p_{a+1})
+ *   else:     t drawn from softmax(target[b,L,:] / T)  (the bonus token)
+ *   draw = the smallest token id whose cumulative mass exceeds
+ *          uniforms[b,K] * (total mass), ids in ascending order
+ *   accepted[b] = a; tokens[b,:] = (y_1 .. y_a, t, -1, ...).
+ * For T = 0 the greedy rule of dspark_verify_greedy applies to that request.
+ * Target rows past L and draft rows past L-1 are never read; draft rows of
+ * T = 0 requests are never read.
+ *
+ *   target_logits [B,K+1,V] dtype; draft_logits [B,K,V] dtype
+ *   dtype         DSPARK_F32 or DSPARK_BF16
+ *   drafted       [B,K] int32 drafted ids y_k
+ *   lengths       [B] int32 verify lengths (normally dspark_schedule's);
+ *                 NULL = K for every request; out-of-range values are clamped
+ *                 to [0,K] and flagged
+ *   temperature   [B] float32 (0 = greedy)
+ *   uniforms      [B,K+1] float32 in [0,1): column k-1 is position k's
+ *                 accept test, column K the final draw
+ *   accepted      [B] int32 out
+ *   tokens        [B,K+1] int32 out, -1 padded
+ *   p_tok, q_tok  [B,K] float32 out p_k(y_k), q_k(y_k) for k <= L and T > 0,
+ *                 0 elsewhere; either may be NULL
+ * Errors: NULL required pointer; B,V < 1; K < 1 or K > 64; bad dtype; small
+ * workspace.
+ */
+DSPARK_API int dspark_verify(const void* target_logits, const void* draft_logits, int dtype, int B, int K,
+                  int V, const int32_t* drafted, const int32_t* lengths,
+                  const float* temperature, const float* uniforms, int32_t* accepted,
+                  int32_t* tokens, float* p_tok, float* q_tok, int32_t* dev_status,
+                  void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * dspark_verify_greedy — greedy (T = 0) verification of the whole batch
+ * (perchy.ai "The Technology": outputs match standard decoding; DSpark Guide,
+ * tutorial drafter takes the argmax):
+ *   g_j = lowest token id attaining max_v target[b,j,v] (compared as floats)
+ *   a = (first k <= L with y_k != g_{k-1}) - 1, or L if none
+ *   accepted[b] = a; tokens[b,:] = (y_1 .. y_a, g_a, -1, ...).
+ * Reads target rows 0..L only.  Arguments as for dspark_verify.
+ */
+DSPARK_API int dspark_verify_greedy(const void* target_logits, int dtype, int B, int K, int V,
+                         const int32_t* drafted, const int32_t* lengths, int32_t* accepted,
+                         int32_t* tokens, int32_t* dev_status, void* workspace, size_t ws_bytes,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

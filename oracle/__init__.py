@@ -158,7 +158,10 @@ def inverse_cdf(mass: np.ndarray, u: float):
 
 
 def _row_flags(row64) -> int:
-    return DEV_NONFINITE if (np.isnan(row64).any() or np.isposinf(row64).any()) else 0
+    """A row that is read must hold no NaN and no +Inf, and at least one
+    finite logit (-Inf alone is a legal, masked logit)."""
+    bad = np.isnan(row64).any() or np.isposinf(row64).any() or not np.isfinite(row64).any()
+    return DEV_NONFINITE if bad else 0
 
 
 def verify_request(target_b, draft_b, drafted_b, L, T, u_b):
@@ -178,9 +181,18 @@ def verify_request(target_b, draft_b, drafted_b, L, T, u_b):
     y = [int(v) for v in drafted_b[:L]]
     if any(v < 0 or v >= V for v in y):
         flags |= DEV_BAD_TOKEN
-    if not (T >= 0.0):                        # negative or NaN
-        flags |= DEV_BAD_TEMP
-    if flags:
+    if not (T >= 0.0):                        # negative or NaN: nothing is read
+        return dict(accepted=0, tokens=tokens, p_tok=p_tok, q_tok=q_tok,
+                    dist=np.inf, flags=flags | DEV_BAD_TEMP)
+    # every row that the rule reads is checked, whatever the drafted ids are
+    n_target = L + 1
+    n_draft = L if T > 0.0 else 0
+    for j in range(n_target):
+        flags |= _row_flags(widen(target_b[j]))
+    for j in range(n_draft):
+        flags |= _row_flags(widen(draft_b[j]))
+    if flags & (DEV_BAD_TOKEN | DEV_NONFINITE):
+        # outputs of a flagged request are unspecified
         return dict(accepted=0, tokens=tokens, p_tok=p_tok, q_tok=q_tok,
                     dist=np.inf, flags=flags)
 
@@ -190,7 +202,6 @@ def verify_request(target_b, draft_b, drafted_b, L, T, u_b):
         g = []
         for j in range(L + 1):
             row = widen(target_b[j])
-            flags |= _row_flags(row)
             g.append(int(np.argmax(row)))      # first maximal index
         a = L
         for k in range(1, L + 1):
@@ -209,16 +220,8 @@ def verify_request(target_b, draft_b, drafted_b, L, T, u_b):
 
     # temperature softmaxes of every scheduled row (Deep Dive, "Speculative
     # Decoding From First Principles"; both distributions at the request's T)
-    P = []
-    Q = []
-    for j in range(L + 1):
-        row = widen(target_b[j])
-        flags |= _row_flags(row)
-        P.append(softmax_T(row, T))
-    for j in range(L):
-        row = widen(draft_b[j])
-        flags |= _row_flags(row)
-        Q.append(softmax_T(row, T))
+    P = [softmax_T(widen(target_b[j]), T) for j in range(L + 1)]
+    Q = [softmax_T(widen(draft_b[j]), T) for j in range(L)]
 
     alpha = np.zeros(L)
     for k in range(1, L + 1):
@@ -266,7 +269,8 @@ def verify(target, draft, drafted, lengths, temperature, uniforms, requests=None
     rows of the outputs stay at their fill values).
 
     Returns dict(accepted int32[B], tokens int32[B,K+1], p_tok float64[B,K],
-    q_tok float64[B,K], dist float64[B], flags int)."""
+    q_tok float64[B,K], dist float64[B], flags int (OR over requests),
+    req_flags int32[B]).  Outputs of a request with flags are unspecified."""
     B, K1, V = target.shape
     K = K1 - 1
     accepted = np.zeros(B, dtype=np.int32)
@@ -274,6 +278,7 @@ def verify(target, draft, drafted, lengths, temperature, uniforms, requests=None
     p_tok = np.zeros((B, K))
     q_tok = np.zeros((B, K))
     dist = np.full(B, np.inf)
+    req_flags = np.zeros(B, dtype=np.int32)
     flags = 0
     idx = range(B) if requests is None else requests
     for b in idx:
@@ -284,9 +289,10 @@ def verify(target, draft, drafted, lengths, temperature, uniforms, requests=None
         p_tok[b] = r["p_tok"]
         q_tok[b] = r["q_tok"]
         dist[b] = r["dist"]
+        req_flags[b] = r["flags"]
         flags |= r["flags"]
     return dict(accepted=accepted, tokens=tokens, p_tok=p_tok, q_tok=q_tok,
-                dist=dist, flags=flags)
+                dist=dist, flags=flags, req_flags=req_flags)
 
 
 def verify_greedy(target, drafted, lengths, requests=None):

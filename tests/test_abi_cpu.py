@@ -1,0 +1,98 @@
+"""The C ABI library on the CPU: it loads, exports every function the header
+declares, and its synchronous argument checks return before any GPU call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import draft_verification_dspark_amd as ds
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "dspark.h")) as f:
+        src = f.read()
+    return re.findall(r"DSPARK_API\s+[\w\s\*]+?\b(dspark_\w+)\s*\(", src)
+
+
+def test_exports_every_declared_symbol():
+    lib = ds.load_library()
+    names = _declared()
+    assert set(names) == set(ds.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in range(7):
+        assert ds.dspark_status_string(s)
+    assert ds.dspark_status_string(99) == "unknown status"
+
+
+def test_workspace_sizes():
+    w = ds.dspark_workspace_bytes
+    assert w(ds.OP_VERIFY, 0, 4, 10) == 0
+    assert w(ds.OP_VERIFY, 1, 65, 10) == 0
+    assert w(7, 1, 1, 1) == 0
+    a = w(ds.OP_VERIFY, 64, 16, 151936)
+    assert a > 0 and a % 256 == 0
+    assert w(ds.OP_VERIFY, 128, 16, 151936) > a
+    assert w(ds.OP_VERIFY_GREEDY, 64, 16, 151936) == a
+    assert w(ds.OP_SCHEDULE, 64, 16, 1) >= 64 * 16 * 4 + 64 * 4
+
+
+P = 4096  # any 256-aligned non-null "pointer": the checks never dereference it
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, 4, 4, 0.1, -1, 1, P, None, None, P, P, 10 ** 6, None), 1),
+    ((P, 0, 4, 0.1, -1, 1, P, None, None, P, P, 10 ** 6, None), 2),
+    ((P, 4, 0, 0.1, -1, 1, P, None, None, P, P, 10 ** 6, None), 2),
+    ((P, 4, 4, 0.1, 3, 1, P, None, None, P, P, 10 ** 6, None), 4),
+    ((P, 4, 4, 0.1, -1, 5, P, None, None, P, P, 10 ** 6, None), 4),
+    ((P, 4, 4, 0.1, -1, -1, P, None, None, P, P, 10 ** 6, None), 4),
+    ((P, 4, 4, 0.1, -1, 1, P, None, None, P, P, 8, None), 5),
+    ((P, 4, 4, 0.1, -1, 1, P, None, None, P, P + 8, 10 ** 6, None), 5),
+])
+def test_schedule_argument_errors(args, code):
+    assert ds.load_library().dspark_schedule(*args) == code
+
+
+def _v(**kw):
+    a = dict(t=P, d=P, dtype=1, B=2, K=4, V=100, y=P, L=None, T=P, u=P, acc=P, tok=P, pt=None,
+             qt=None, st=P, ws=P, nb=10 ** 9, stream=None)
+    a.update(kw)
+    return ds.load_library().dspark_verify(a["t"], a["d"], a["dtype"], a["B"], a["K"], a["V"],
+                                           a["y"], a["L"], a["T"], a["u"], a["acc"], a["tok"],
+                                           a["pt"], a["qt"], a["st"], a["ws"], a["nb"], a["stream"])
+
+
+def test_verify_argument_errors():
+    assert _v(t=None) == 1
+    assert _v(d=None) == 1
+    assert _v(u=None) == 1
+    assert _v(st=None) == 1
+    assert _v(B=0) == 2
+    assert _v(K=65) == 2
+    assert _v(V=0) == 2
+    assert _v(dtype=2) == 3
+    assert _v(nb=16) == 5
+    assert _v(ws=P + 64) == 5
+    lib = ds.load_library()
+    # greedy needs no draft, temperature or uniforms
+    assert lib.dspark_verify_greedy(P, 1, 2, 4, 100, P, None, P, P, P, P, 16, None) == 5
+    assert lib.dspark_verify_greedy(P, 1, 2, 4, 100, None, None, P, P, P, P, 10 ** 9, None) == 1
+
+
+def test_binding_refuses_without_library(tmp_path):
+    import importlib
+    mod = importlib.import_module("draft_verification_dspark_amd")
+    saved = mod._lib
+    try:
+        mod._lib = None
+        with pytest.raises(RuntimeError):
+            mod.load_library(str(tmp_path / "missing.so"))
+    finally:
+        mod._lib = saved

@@ -1,0 +1,408 @@
+"""GPU parity: the HIP library through its C ABI versus the CPU oracle.
+
+Workloads are the five benchmark workloads (seeded synthetic stand-ins for
+the pages' datasets), at full size and at reduced sizes that still span many
+4096-token chunks and a ragged last chunk."""
+import numpy as np
+import pytest
+import torch
+
+import draft_verification_dspark_amd as ds
+import oracle
+import workloads
+from parity import compare_schedule, compare_verify, host
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _sched(w):
+    return ds.schedule(w.conf, w.threshold, w.budget, w.min_len)
+
+
+def _check_workload(w, requests=None, check_sched=True):
+    lengths, mask, surv, st = _sched(w)
+    torch.cuda.synchronize()
+    ref_s = oracle.schedule(host(w.conf), w.threshold, w.budget, w.min_len)
+    if check_sched:
+        compare_schedule((host(lengths), host(mask), host(surv)), ref_s)
+    assert int(st.item()) == 0
+    out = ds.verify(w.target, w.draft, w.drafted, lengths, w.temperature, w.uniforms)
+    torch.cuda.synchronize()
+    g = {k: host(v) for k, v in out.items()}
+    L = host(lengths)
+    ref = oracle.verify(host(w.target), host(w.draft), host(w.drafted), L, host(w.temperature),
+                        host(w.uniforms), requests=requests)
+    rep = compare_verify(g, ref, L, host(w.temperature), requests=requests)
+    print(f"[{w.name} seed+{w.seed_offset}] requests={rep.n_requests} mismatches={rep.n_mismatch} "
+          f"boundary={rep.n_boundary} worst_prob_rel={rep.worst_prob_rel:.2e} sumL={int(L.sum())}",
+          flush=True)
+    rep.assert_ok()
+    assert int(g["dev_status"][0]) == ref["flags"] == 0
+    return g, ref, L
+
+
+@pytest.mark.parametrize("seed", [0, 100, 200])
+@pytest.mark.parametrize("wid", [1, 2, 3])
+def test_workload_full_size(wid, seed):
+    w = workloads.make(wid, seed_offset=seed, device=DEV)
+    _check_workload(w)
+
+
+@pytest.mark.parametrize("wid", [4, 5])
+def test_workload_full_size_large(wid):
+    w = workloads.make(wid, seed_offset=0, device=DEV)
+    # every request for workload 4; a deterministic quarter of workload 5
+    req = None if wid == 4 else list(range(0, w.B, 4))
+    _check_workload(w, requests=req)
+
+
+@pytest.mark.parametrize("seed", [100, 200])
+@pytest.mark.parametrize("wid,B", [(4, 24), (5, 96)])
+def test_workload_reduced_batch(wid, B, seed):
+    w = workloads.make(wid, seed_offset=seed, device=DEV, B=B)
+    _check_workload(w)
+
+
+def test_greedy_workload2():
+    w = workloads.make(2, device=DEV)
+    lengths, _, _, _ = _sched(w)
+    out = ds.verify_greedy(w.target, w.greedy_drafted, lengths)
+    torch.cuda.synchronize()
+    ref = oracle.verify_greedy(host(w.target), host(w.greedy_drafted), host(lengths))
+    assert np.array_equal(host(out["accepted"]), ref["accepted"])
+    assert np.array_equal(host(out["tokens"]), ref["tokens"])
+    assert int(out["dev_status"].item()) == 0
+    # the greedy rule inside dspark_verify (temperature 0) gives the same answer
+    out2 = ds.verify(w.target, w.draft, w.greedy_drafted, lengths, torch.zeros_like(w.temperature),
+                     w.uniforms)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out2["accepted"]), ref["accepted"])
+    assert np.array_equal(host(out2["tokens"]), ref["tokens"])
+
+
+# ---------------------------------------------------------------- shapes / edges
+
+def _rand_case(B, K, V, dtype, seed, T=None, scale=3.0, draft_noise=1.0, lengths="rand"):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    tgt = scale * torch.randn((B, K + 1, V), generator=g, device=DEV)
+    dft = tgt[:, :K] + draft_noise * torch.randn((B, K, V), generator=g, device=DEV)
+    st = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tgt, dft = tgt.to(st).contiguous(), dft.to(st).contiguous()
+    if T is None:
+        temp = torch.rand(B, generator=g, device=DEV) * 1.5 + 0.2
+    else:
+        temp = torch.full((B,), float(T), device=DEV)
+    temp = temp.float().contiguous()
+    probs = torch.softmax(dft.float() / torch.where(temp > 0, temp, 1.0).view(B, 1, 1), -1)
+    drafted = torch.multinomial(probs.view(B * K, V), 1, generator=g).view(B, K).int().contiguous()
+    if lengths == "rand":
+        L = torch.randint(0, K + 1, (B,), generator=g, device=DEV).int()
+    elif lengths == "full":
+        L = torch.full((B,), K, dtype=torch.int32, device=DEV)
+    else:
+        L = lengths
+    u = torch.rand((B, K + 1), generator=g, device=DEV).float().contiguous()
+    return tgt, dft, drafted, L.contiguous(), temp, u
+
+
+def _verify_and_compare(tgt, dft, drafted, L, temp, u, expect_flags=0):
+    out = ds.verify(tgt, dft, drafted, L, temp, u)
+    torch.cuda.synchronize()
+    g = {k: host(v) for k, v in out.items()}
+    Lh = host(L) if L is not None else np.full(tgt.shape[0], tgt.shape[1] - 1, np.int32)
+    ref = oracle.verify(host(tgt), host(dft), host(drafted), Lh, host(temp), host(u))
+    rep = compare_verify(g, ref, Lh, host(temp))
+    rep.assert_ok()
+    assert int(g["dev_status"][0]) == ref["flags"] == expect_flags
+    return g, ref
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V", [1, 7, 1000, 1001, 4095, 4096, 4097, 8200, 20001])
+def test_vocab_sizes_and_ragged_tails(dtype, V):
+    # V not a multiple of the vector width takes the scalar path
+    B, K = 6, 5
+    case = _rand_case(B, K, V, dtype, seed=V * 7 + (dtype == "f32"))
+    _verify_and_compare(*case)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_misaligned_rows_scalar_path(dtype):
+    B, K, V = 3, 4, 4104
+    tgt, dft, drafted, L, temp, u = _rand_case(B, K, V, dtype, seed=5)
+    st = tgt.dtype
+    # storage shifted by one element: rows no longer start on 16-byte boundaries
+    flat_t = torch.empty(tgt.numel() + 1, dtype=st, device=DEV)
+    flat_t[1:].copy_(tgt.view(-1))
+    flat_d = torch.empty(dft.numel() + 1, dtype=st, device=DEV)
+    flat_d[1:].copy_(dft.view(-1))
+    tv = flat_t[1:].view(B, K + 1, V)
+    dv = flat_d[1:].view(B, K, V)
+    assert tv.data_ptr() % 16 != 0
+    g1, _ = _verify_and_compare(tv, dv, drafted, L, temp, u)
+    out = ds.verify(tgt, dft, drafted, L, temp, u)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out["accepted"]), g1["accepted"])
+    assert np.array_equal(host(out["tokens"]), g1["tokens"])
+
+
+def test_max_k_and_full_length():
+    B, K, V = 4, 64, 2048
+    tgt, dft, drafted, L, temp, u = _rand_case(B, K, V, "bf16", seed=11, lengths="full",
+                                                draft_noise=0.0, T=1.0)
+    # q == p: every position accepted, bonus from row 64
+    g, ref = _verify_and_compare(tgt, tgt[:, :K].contiguous(), drafted, L, temp, u)
+    assert (g["accepted"] == K).all()
+    assert np.array_equal(g["p_tok"], g["q_tok"])
+    # greedy on the same rows with drafts equal to the argmax: all accepted
+    am = tgt.float().argmax(-1).int()
+    og = ds.verify_greedy(tgt, am[:, :K].contiguous(), L)
+    torch.cuda.synchronize()
+    assert (host(og["accepted"]) == K).all()
+    assert np.array_equal(host(og["tokens"])[:, K], host(am)[:, K])
+
+
+def test_q_equals_p_all_accept_exactly():
+    B, K, V = 32, 8, 151936
+    tgt, _, drafted, L, temp, u = _rand_case(B, K, V, "bf16", seed=13)
+    g, ref = _verify_and_compare(tgt, tgt[:, :K].contiguous(), drafted, L, temp, u)
+    assert np.array_equal(g["accepted"], host(L))
+    assert np.array_equal(g["p_tok"], g["q_tok"])
+
+
+def test_lengths_null_and_zero():
+    B, K, V = 5, 6, 3000
+    tgt, dft, drafted, _, temp, u = _rand_case(B, K, V, "bf16", seed=17)
+    _verify_and_compare(tgt, dft, drafted, None, temp, u)
+    zero = torch.zeros(B, dtype=torch.int32, device=DEV)
+    g, ref = _verify_and_compare(tgt, dft, drafted, zero, temp, u)
+    assert (g["accepted"] == 0).all() and (g["tokens"][:, 1:] == -1).all()
+
+
+@pytest.mark.parametrize("T", [1e-3, 0.05, 5.0, 100.0])
+def test_temperature_extremes(T):
+    B, K, V = 8, 4, 5000
+    _verify_and_compare(*_rand_case(B, K, V, "f32", seed=int(T * 1000) + 3, T=T))
+
+
+def test_large_and_masked_logits():
+    B, K, V = 6, 4, 9000
+    tgt, dft, drafted, L, temp, u = _rand_case(B, K, V, "f32", seed=19, scale=400.0)
+    _verify_and_compare(tgt, dft, drafted, L, temp, u)
+    # -inf everywhere except a handful of tokens (masked vocabulary)
+    keep = torch.zeros(V, dtype=torch.bool, device=DEV)
+    keep[torch.tensor([3, 4100, 8999], device=DEV)] = True
+    tgt2 = torch.where(keep, tgt, torch.tensor(-float("inf"), device=DEV)).contiguous()
+    dft2 = torch.where(keep, dft, torch.tensor(-float("inf"), device=DEV)).contiguous()
+    probs = torch.softmax(dft2.float(), -1)
+    drafted2 = torch.multinomial(probs.view(-1, V), 1).view(B, K).int().contiguous()
+    _verify_and_compare(tgt2, dft2, drafted2, L, temp, u)
+
+
+def test_mixed_greedy_and_sampled_requests():
+    B, K, V = 40, 8, 32000
+    tgt, dft, drafted, L, temp, u = _rand_case(B, K, V, "bf16", seed=23)
+    temp[::3] = 0.0
+    am = dft.float().argmax(-1).int()
+    drafted = torch.where((temp == 0).view(B, 1), am, drafted).contiguous()
+    _verify_and_compare(tgt, dft, drafted, L, temp, u)
+
+
+def test_device_status_flags():
+    B, K, V = 4, 3, 1000
+    tgt, dft, drafted, L, temp, u = _rand_case(B, K, V, "f32", seed=29, lengths="full")
+    bad_tok = drafted.clone()
+    bad_tok[1, 2] = V
+    _verify_and_compare(tgt, dft, bad_tok, L, temp, u, expect_flags=ds.DEV_BAD_TOKEN)
+    nan_t = tgt.clone()
+    nan_t[2, 1, 17] = float("nan")
+    _verify_and_compare(nan_t, dft, drafted, L, temp, u, expect_flags=ds.DEV_NONFINITE)
+    bad_u = u.clone()
+    bad_u[0, K] = 1.0
+    _verify_and_compare(tgt, dft, drafted, L, temp, bad_u, expect_flags=ds.DEV_BAD_UNIFORM)
+    bad_T = temp.clone()
+    bad_T[3] = -1.0
+    _verify_and_compare(tgt, dft, drafted, L, bad_T, u, expect_flags=ds.DEV_BAD_TEMP)
+    bad_L = L.clone()
+    bad_L[0] = K + 3
+    out = ds.verify(tgt, dft, drafted, bad_L, temp, u)
+    torch.cuda.synchronize()
+    assert int(out["dev_status"].item()) == ds.DEV_BAD_LENGTH
+    # a row past the scheduled length is never read
+    nan2 = tgt.clone()
+    nan2[0, K, 5] = float("nan")
+    Ls = L.clone()
+    Ls[0] = 1
+    out = ds.verify(nan2, dft, drafted, Ls, temp, u)
+    torch.cuda.synchronize()
+    assert int(out["dev_status"].item()) == 0
+
+
+# ---------------------------------------------------------------- schedule
+
+@pytest.mark.parametrize("B,K", [(1, 1), (3, 4), (64, 16), (1024, 8), (5000, 7), (300, 64)])
+def test_schedule_random(B, K):
+    rng = np.random.default_rng(B * 31 + K)
+    for trial in range(4):
+        conf = (rng.uniform(0, 1, size=(B, K)) ** rng.uniform(0.05, 1.0, size=(B, 1))).astype(np.float32)
+        conf[rng.random(size=(B, K)) < 0.02] = 0.0
+        if trial == 3:
+            conf = np.round(conf * 8) / 8           # many exact ties
+        tau = float(rng.uniform(0, 0.6))
+        min_len = int(rng.integers(0, 2))
+        budget = int(rng.integers(B * min_len, B * K + 1))
+        ct = torch.from_numpy(conf).to(DEV)
+        for bud in (budget, -1, B * min_len):
+            g = ds.schedule(ct, tau, bud, min_len)
+            torch.cuda.synchronize()
+            compare_schedule((host(g[0]), host(g[1]), host(g[2])), oracle.schedule(conf, tau, bud, min_len))
+            assert int(g[3].item()) == 0
+
+
+def test_schedule_golden_and_subnormals():
+    import json, os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "schedule_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        conf = torch.tensor(c["conf"], dtype=torch.float32, device=DEV)
+        L, m, s, st = ds.schedule(conf, c["threshold"], c["budget"], c["min_len"])
+        torch.cuda.synchronize()
+        assert host(L).tolist() == c["lengths"], c["name"]
+        assert host(s).tolist() == c["survival"], c["name"]
+    conf = np.full((2, 8), 1e-20, np.float32)
+    conf[1, 2] = 0.5
+    L, m, s, st = ds.schedule(torch.from_numpy(conf).to(DEV), 0.0, -1, 1)
+    torch.cuda.synchronize()
+    compare_schedule((host(L), host(m), host(s)), oracle.schedule(conf, 0.0, -1, 1))
+    assert 0 < host(s)[0, 1] < np.finfo(np.float32).tiny
+
+
+def test_schedule_bad_conf_flag():
+    conf = torch.tensor([[0.5, 1.5, 0.5], [0.2, float("nan"), 0.1]], device=DEV)
+    _, _, _, st = ds.schedule(conf, 0.1, -1, 1)
+    torch.cuda.synchronize()
+    assert int(st.item()) == ds.DEV_BAD_CONF
+
+
+def test_schedule_budget_error_is_synchronous():
+    conf = torch.rand((4, 4), device=DEV)
+    with pytest.raises(ds.DsparkError) as e:
+        ds.schedule(conf, 0.1, 3, 1)
+    assert e.value.status == 4
+
+
+# ---------------------------------------------------------------- statistics
+
+def test_lossless_replicated_batch():
+    """Many copies of one tiny request with fresh uniforms and drafts y ~ q:
+    the token emitted at each position (among requests that reached it) is
+    distributed as the target softmax of that position."""
+    import scipy.stats
+    n, K, V = 1 << 17, 3, 6
+    g = torch.Generator(device=DEV)
+    g.manual_seed(77)
+    base_t = 1.5 * torch.randn((K + 1, V), generator=g, device=DEV)
+    base_d = base_t[:K] + 1.2 * torch.randn((K, V), generator=g, device=DEV)
+    T = 0.9
+    tgt = base_t.expand(n, K + 1, V).contiguous()
+    dft = base_d.expand(n, K, V).contiguous()
+    q = torch.softmax(base_d / T, -1)
+    drafted = torch.stack([torch.multinomial(q[k], n, replacement=True, generator=g) for k in range(K)],
+                          1).int().contiguous()
+    u = torch.rand((n, K + 1), generator=g, device=DEV).contiguous()
+    temp = torch.full((n,), T, device=DEV)
+    out = ds.verify(tgt, dft, drafted, None, temp, u)
+    torch.cuda.synchronize()
+    a = host(out["accepted"])
+    tok = host(out["tokens"])
+    P = torch.softmax(base_t.double().cpu() / float(np.float32(T)), -1).numpy()
+    for k in range(K + 1):
+        reached = a >= k
+        counts = np.bincount(tok[reached, k], minlength=V)
+        _, pval = scipy.stats.chisquare(counts, P[k] * reached.sum())
+        assert pval > 1e-4, (k, counts, P[k] * reached.sum())
+
+
+def test_expected_accepted_length_closed_form():
+    """P(a >= L) = prod_{k<=L} alpha_k for fixed drafts and fresh uniforms."""
+    n, K, V = 1 << 16, 6, 50
+    g = torch.Generator(device=DEV)
+    g.manual_seed(79)
+    base_t = 2.0 * torch.randn((K + 1, V), generator=g, device=DEV)
+    base_d = base_t[:K] + 0.8 * torch.randn((K, V), generator=g, device=DEV)
+    y = base_d.argmax(-1).int()
+    tgt = base_t.expand(n, K + 1, V).contiguous()
+    dft = base_d.expand(n, K, V).contiguous()
+    drafted = y.expand(n, K).contiguous()
+    u = torch.rand((n, K + 1), generator=g, device=DEV).contiguous()
+    out = ds.verify(tgt, dft, drafted, None, torch.ones(n, device=DEV), u)
+    torch.cuda.synchronize()
+    a = host(out["accepted"]).astype(np.float64)
+    P = torch.softmax(base_t.double(), -1).cpu().numpy()
+    Q = torch.softmax(base_d.double(), -1).cpu().numpy()
+    yy = host(y)
+    alpha = [min(1.0, P[k][yy[k]] / Q[k][yy[k]]) for k in range(K)]
+    expect = sum(np.prod(alpha[:L]) for L in range(1, K + 1))
+    assert abs(a.mean() - expect) <= 5 * a.std() / np.sqrt(n) + 1e-9
+
+
+# ---------------------------------------------------------------- determinism / graphs
+
+def test_deterministic_repeat():
+    w = workloads.make(3, device=DEV, B=16)
+    lengths, _, _, _ = _sched(w)
+    r1 = ds.verify(w.target, w.draft, w.drafted, lengths, w.temperature, w.uniforms)
+    torch.cuda.synchronize()
+    snap = {k: v.clone() for k, v in r1.items()}
+    for _ in range(3):
+        r2 = ds.verify(w.target, w.draft, w.drafted, lengths, w.temperature, w.uniforms)
+        torch.cuda.synchronize()
+        for k in snap:
+            assert torch.equal(snap[k], r2[k]), k
+
+
+def test_graph_capture_replay():
+    w = workloads.make(2, device=DEV)
+    B, K, V = w.B, w.K, w.V
+    lengths = torch.empty(B, dtype=torch.int32, device=DEV)
+    mask = torch.empty((B, K), dtype=torch.uint8, device=DEV)
+    surv = torch.empty((B, K), dtype=torch.float32, device=DEV)
+    acc = torch.empty(B, dtype=torch.int32, device=DEV)
+    tok = torch.empty((B, K + 1), dtype=torch.int32, device=DEV)
+    pt = torch.empty((B, K), dtype=torch.float32, device=DEV)
+    qt = torch.empty((B, K), dtype=torch.float32, device=DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ws_s = ds.workspace(ds.OP_SCHEDULE, B, K, 1, DEV)
+    ws_v = ds.workspace(ds.OP_VERIFY, B, K, V, DEV)
+    u = w.uniforms.clone()
+
+    def step():
+        st.zero_()
+        ds.schedule(w.conf, w.threshold, w.budget, w.min_len, lengths=lengths, mask=mask,
+                    survival=surv, dev_status=st, ws=ws_s)
+        ds.verify(w.target, w.draft, w.drafted, lengths, w.temperature, u, accepted=acc,
+                  tokens=tok, p_tok=pt, q_tok=qt, dev_status=st, ws=ws_v)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(5)
+    for rep in range(4):
+        u.copy_(torch.rand(u.shape, generator=gen, device=DEV))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (acc.clone(), tok.clone(), pt.clone(), lengths.clone())
+        step()                                   # eager on the same inputs
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], acc) and torch.equal(got[1], tok) and torch.equal(got[2], pt)
+        assert torch.equal(got[3], lengths)
+        assert int(st.item()) == 0

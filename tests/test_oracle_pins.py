@@ -422,3 +422,26 @@ def test_inverse_cdf_edges():
     assert oracle.inverse_cdf(np.array([0.25, 0.25, 0.5]), 0.5)[0] == 2
     assert oracle.inverse_cdf(np.array([0.25, 0.0, 0.75]), 0.25)[0] == 2
     assert oracle.inverse_cdf(np.array([0.5, 0.5, 0.0]), np.nextafter(1.0, 0.0))[0] == 1
+
+
+def test_nonfinite_row_rules():
+    """A read row with NaN or +Inf, or without any finite logit, is flagged;
+    rows are checked whatever the drafted ids are."""
+    B, K, V = 1, 2, 8
+    t = np.zeros((B, K + 1, V), np.float32)
+    d = np.zeros((B, K, V), np.float32)
+    y = np.array([[1, 2]], np.int32)
+    T = np.ones(B, np.float32)
+    u = np.full((B, K + 1), 0.5, np.float32)
+    allinf = t.copy()
+    allinf[0, 2] = -np.inf
+    assert oracle.verify(allinf, d, y, None, T, u)["flags"] == oracle.DEV_NONFINITE
+    pinf = t.copy()
+    pinf[0, 0, 3] = np.inf
+    f = oracle.verify(pinf, d, np.array([[1, V]], np.int32), None, T, u)["flags"]
+    assert f == oracle.DEV_NONFINITE | oracle.DEV_BAD_TOKEN
+    # greedy reads no draft row
+    dn = d.copy()
+    dn[0, 0, 0] = np.nan
+    assert oracle.verify(t, dn, y, None, np.zeros(B, np.float32), u)["flags"] == 0
+    assert oracle.verify(t, dn, y, None, T, u)["flags"] == oracle.DEV_NONFINITE
