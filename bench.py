@@ -3,8 +3,8 @@ confidence-scheduled block verification on one MI355X.
 
 One step = dspark_schedule + dspark_verify over one batch of the
 V=151936, B=64, K=16 workload (bf16 logits, T=1, threshold 0.2, budget 512;
-seeded synthetic inputs resident in HBM).  Three input sets (seed offsets
-0, 100, 200; 641 MB each) rotate so that no step reads logits left in the
+seeded synthetic inputs resident in HBM).  Six input sets (seed offsets
+0, 100, ..., 500; 641 MB each) rotate so that no step reads logits left in the
 256 MB last-level cache by the step before.
 
 Prints ONE JSON line on stdout.  ``value`` = sum of verified positions
@@ -50,7 +50,7 @@ def main():
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=3)
-    ap.add_argument("--sets", type=int, default=3)
+    ap.add_argument("--sets", type=int, default=6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
@@ -170,7 +170,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "dspark_verify (plan, pass1, finalize, pass2, sample launches)",
+            "kernel": "dspark_verify (k_stream_rows, k_decide, k_draw launches)",
             "achieved": round(verify_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -25,12 +25,13 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile the library to ``out``; ``defines`` are extra -D tuning knobs."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     srcs = [os.path.join(HERE, "csrc", s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-           *srcs, "-o", tmp]
+    tmp = out + ".tmp"
+    cmd = [hipcc, *FLAGS, *[f"-D{d}" for d in defines], "-I", os.path.join(ROOT, "include"),
+           "-I", os.path.join(HERE, "csrc"), *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -39,8 +40,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -15,19 +15,20 @@ constexpr int kMaxK = 64;
 size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct VerifyLayout {
-  size_t req, n_rows, rows, part1, part2, total;
+  size_t req, part1, rows, part2, total;
 };
 
 VerifyLayout verify_layout(int B, int K, int V) {
   VerifyLayout L;
-  const size_t R = (size_t)2 * K + 1;
+  if (B > kLaunchBatch) B = kLaunchBatch;  // sub-batches reuse the workspace
   const size_t G = (size_t)chunks_per_row_max(V);
+  // residual pieces hold at least 1024 tokens (fp32; 2048 for bf16)
+  const size_t G2 = ((size_t)V + 1023) / 1024;
   size_t off = 0;
-  L.req = off;    off += up(sizeof(ReqState) * (size_t)B);
-  L.n_rows = off; off += kAlign;
-  L.rows = off;   off += up(sizeof(int32_t) * (size_t)B * R);
-  L.part1 = off;  off += up(sizeof(Partial) * (size_t)B * R * G);
-  L.part2 = off;  off += up(sizeof(double) * (size_t)B * G);
+  L.req = off;   off += up(sizeof(ReqState) * (size_t)B);
+  L.part1 = off; off += up(sizeof(Partial) * (size_t)B * (K + 1) * 2 * G);
+  L.rows = off;  off += up(sizeof(RowSum) * (size_t)B * (K + 1) * 2);
+  L.part2 = off; off += up(sizeof(double) * (size_t)B * G2);
   L.total = off;
   return L;
 }
@@ -48,6 +49,31 @@ ScheduleLayout schedule_layout(int B, int K) {
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 }  // namespace
+
+// Workgroups of `kernel` that fit on the current device at once (occupancy x
+// compute units); cached per device, kernel and LDS size.
+int resident_blocks(const void* kernel, int threads, size_t lds) {
+  struct Entry {
+    const void* k;
+    size_t lds;
+    int dev, blocks;
+  };
+  static Entry cache[64];
+  static int n_cache = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1024;
+  for (int i = 0; i < n_cache; ++i)
+    if (cache[i].k == kernel && cache[i].dev == dev && cache[i].lds == lds) return cache[i].blocks;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      per_cu < 1 || cus < 1)
+    return 1024;
+  const int blocks = per_cu * cus;
+  if (n_cache < 64) cache[n_cache++] = Entry{kernel, lds, dev, blocks};
+  return blocks;
+}
+
 }  // namespace dspark
 
 using namespace dspark;
@@ -128,18 +154,35 @@ static int verify_common(const void* target, const void* draft, int dtype, int B
   a.q_tok = greedy_only ? nullptr : q_tok;
   a.dev_status = dev_status;
   a.req = reinterpret_cast<ReqState*>(ws + L.req);
-  a.n_rows = reinterpret_cast<int32_t*>(ws + L.n_rows);
-  a.rows = reinterpret_cast<int32_t*>(ws + L.rows);
   a.part1 = reinterpret_cast<Partial*>(ws + L.part1);
+  a.rows = reinterpret_cast<RowSum*>(ws + L.rows);
   a.part2 = reinterpret_cast<double*>(ws + L.part2);
-  a.B = B;
   a.K = K;
   a.V = V;
   const int per_vec = dtype == DSPARK_BF16 ? 8 : 4;
   a.G = dtype == DSPARK_BF16 ? chunks_per_row<DSPARK_BF16>(V) : chunks_per_row<DSPARK_F32>(V);
   a.greedy_only = greedy_only;
   a.vec_ok = (V % per_vec == 0) && aligned(target, 16) && (greedy_only || aligned(draft, 16));
-  return launch_verify(a, dtype, static_cast<hipStream_t>(stream));
+  // consecutive sub-batches of at most kLaunchBatch requests on one stream
+  const size_t s = dtype == DSPARK_BF16 ? 2 : 4;
+  for (int b0 = 0; b0 < B; b0 += kLaunchBatch) {
+    VerifyArgs sub = a;
+    const int nb = B - b0 < kLaunchBatch ? B - b0 : kLaunchBatch;
+    sub.B = nb;
+    sub.target = static_cast<const char*>(target) + (size_t)b0 * (K + 1) * V * s;
+    sub.draft = greedy_only ? nullptr : static_cast<const char*>(draft) + (size_t)b0 * K * V * s;
+    sub.drafted = drafted + (size_t)b0 * K;
+    sub.lengths = lengths ? lengths + b0 : nullptr;
+    sub.temperature = greedy_only ? nullptr : temperature + b0;
+    sub.uniforms = greedy_only ? nullptr : uniforms + (size_t)b0 * (K + 1);
+    sub.accepted = accepted + b0;
+    sub.tokens = tokens + (size_t)b0 * (K + 1);
+    sub.p_tok = a.p_tok ? a.p_tok + (size_t)b0 * K : nullptr;
+    sub.q_tok = a.q_tok ? a.q_tok + (size_t)b0 * K : nullptr;
+    const int st = launch_verify(sub, dtype, static_cast<hipStream_t>(stream));
+    if (st != DSPARK_OK) return st;
+  }
+  return DSPARK_OK;
 }
 
 int dspark_verify(const void* target_logits, const void* draft_logits, int dtype, int B, int K,

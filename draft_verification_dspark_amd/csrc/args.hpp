@@ -34,16 +34,22 @@ struct VerifyArgs {
   float* q_tok;
   int32_t* dev_status;
   ReqState* req;       // [B]
-  int32_t* n_rows;     // [1]
-  int32_t* rows;       // [B*(2K+1)]
-  Partial* part1;      // [B*(2K+1)*G]
-  double* part2;       // [B*G]
+  Partial* part1;      // [B*(K+1)*2*G] chunk summaries, (request, row j, side) major
+  RowSum* rows;        // [B*(K+1)*2] merged rows, (request, row j, side) major
+  double* part2;       // [B*G] residual mass per chunk
   int B, K, V, G;
+  int groups;          // k_decide workgroups per request
   int greedy_only;
   int vec_ok;
 };
 
 int launch_verify(VerifyArgs& a, int dtype, hipStream_t st);
+int resident_blocks(const void* kernel, int threads, size_t lds);
+
+// Requests per launch sequence of dspark_verify (the streaming kernel keeps
+// a per-request plan of this many entries in LDS); larger batches run as
+// consecutive sub-batches on the same stream.
+constexpr int kLaunchBatch = 2048;
 int launch_schedule(ScheduleArgs& a, hipStream_t st);
 
 }  // namespace dspark

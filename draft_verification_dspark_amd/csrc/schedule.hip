@@ -94,18 +94,25 @@ __global__ void __launch_bounds__(kSchedThreads) k_schedule(ScheduleArgs a) {
   long long local = 0;
   int bad = 0;
   for (int b = tid; b < B; b += kSchedThreads) {
-    const float* cr = a.conf + (size_t)b * K;
-    float* sr = a.surv + (size_t)b * K;
+    const float* __restrict__ cr = a.conf + (size_t)b * K;
+    float* __restrict__ sr = a.surv + (size_t)b * K;
     float C = 1.f;
     int cnt_keep = 0;
     bool go = true;
-    for (int k = 0; k < K; ++k) {
-      const float ck = cr[k];
-      if (!(ck >= 0.f && ck <= 1.f)) bad |= DSPARK_DEV_BAD_CONF;
-      C = k == 0 ? ck : C * ck;
-      sr[k] = C;
-      if (go && C >= a.tau) ++cnt_keep;
-      else go = false;
+    // confidences are loaded 8 at a time ahead of the dependent products
+    for (int k0 = 0; k0 < K; k0 += 8) {
+      float ck[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ck[i] = k0 + i < K ? cr[k0 + i] : 1.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (k0 + i >= K) break;
+        if (!(ck[i] >= 0.f && ck[i] <= 1.f)) bad |= DSPARK_DEV_BAD_CONF;
+        C = k0 + i == 0 ? ck[i] : C * ck[i];
+        sr[k0 + i] = C;
+        if (go && C >= a.tau) ++cnt_keep;
+        else go = false;
+      }
     }
     const int lt = max(a.min_len, cnt_keep);
     a.lthr[b] = lt;

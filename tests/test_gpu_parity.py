@@ -164,6 +164,19 @@ def test_max_k_and_full_length():
     assert np.array_equal(host(og["tokens"])[:, K], host(am)[:, K])
 
 
+def test_batch_larger_than_one_launch():
+    # more requests than one launch sequence handles: consecutive sub-batches
+    B, K, V = 4500, 3, 520
+    tgt, dft, drafted, L, temp, u = _rand_case(B, K, V, "bf16", seed=31)
+    temp[::5] = 0.0
+    _verify_and_compare(tgt, dft, drafted, L, temp, u)
+    og = ds.verify_greedy(tgt, drafted, L)
+    torch.cuda.synchronize()
+    rg = oracle.verify_greedy(host(tgt), host(drafted), host(L))
+    assert np.array_equal(host(og["accepted"]), rg["accepted"])
+    assert np.array_equal(host(og["tokens"]), rg["tokens"])
+
+
 def test_q_equals_p_all_accept_exactly():
     B, K, V = 32, 8, 151936
     tgt, _, drafted, L, temp, u = _rand_case(B, K, V, "bf16", seed=13)
