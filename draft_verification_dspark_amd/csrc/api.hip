@@ -15,20 +15,17 @@ constexpr int kMaxK = 64;
 size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct VerifyLayout {
-  size_t req, part1, rows, part2, total;
+  size_t req, part1, part2, total;
 };
 
 VerifyLayout verify_layout(int B, int K, int V) {
   VerifyLayout L;
   if (B > kLaunchBatch) B = kLaunchBatch;  // sub-batches reuse the workspace
   const size_t G = (size_t)chunks_per_row_max(V);
-  // residual pieces hold at least 1024 tokens (fp32; 2048 for bf16)
-  const size_t G2 = ((size_t)V + 1023) / 1024;
   size_t off = 0;
   L.req = off;   off += up(sizeof(ReqState) * (size_t)B);
   L.part1 = off; off += up(sizeof(Partial) * (size_t)B * (K + 1) * 2 * G);
-  L.rows = off;  off += up(sizeof(RowSum) * (size_t)B * (K + 1) * 2);
-  L.part2 = off; off += up(sizeof(double) * (size_t)B * G2);
+  L.part2 = off; off += up(sizeof(double) * (size_t)B * G);
   L.total = off;
   return L;
 }
@@ -50,28 +47,19 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 }  // namespace
 
-// Workgroups of `kernel` that fit on the current device at once (occupancy x
-// compute units); cached per device, kernel and LDS size.
-int resident_blocks(const void* kernel, int threads, size_t lds) {
-  struct Entry {
-    const void* k;
-    size_t lds;
-    int dev, blocks;
-  };
-  static Entry cache[64];
-  static int n_cache = 0;
+// Compute units of the current device (cached per device; 256 if the query
+// fails).
+int compute_units() {
+  static int cache[64];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 1024;
-  for (int i = 0; i < n_cache; ++i)
-    if (cache[i].k == kernel && cache[i].dev == dev && cache[i].lds == lds) return cache[i].blocks;
-  int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      per_cu < 1 || cus < 1)
-    return 1024;
-  const int blocks = per_cu * cus;
-  if (n_cache < 64) cache[n_cache++] = Entry{kernel, lds, dev, blocks};
-  return blocks;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    return 256;
+  if (dev < 64) cache[dev] = cus;
+  return cus;
 }
 
 }  // namespace dspark
@@ -155,7 +143,6 @@ static int verify_common(const void* target, const void* draft, int dtype, int B
   a.dev_status = dev_status;
   a.req = reinterpret_cast<ReqState*>(ws + L.req);
   a.part1 = reinterpret_cast<Partial*>(ws + L.part1);
-  a.rows = reinterpret_cast<RowSum*>(ws + L.rows);
   a.part2 = reinterpret_cast<double*>(ws + L.part2);
   a.K = K;
   a.V = V;

@@ -35,8 +35,7 @@ struct VerifyArgs {
   int32_t* dev_status;
   ReqState* req;       // [B]
   Partial* part1;      // [B*(K+1)*2*G] chunk summaries, (request, row j, side) major
-  RowSum* rows;        // [B*(K+1)*2] merged rows, (request, row j, side) major
-  double* part2;       // [B*G] residual mass per chunk
+  double* part2;       // [B*G] residual mass per chunk of the rejected row pair
   int B, K, V, G;
   int groups;          // k_decide workgroups per request
   int greedy_only;
@@ -44,7 +43,7 @@ struct VerifyArgs {
 };
 
 int launch_verify(VerifyArgs& a, int dtype, hipStream_t st);
-int resident_blocks(const void* kernel, int threads, size_t lds);
+int compute_units();  // of the current device
 
 // Requests per launch sequence of dspark_verify (the streaming kernel keeps
 // a per-request plan of this many entries in LDS); larger batches run as

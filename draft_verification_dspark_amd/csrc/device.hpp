@@ -349,21 +349,21 @@ template <int DT, int U> struct TileN {
 
 template <int DT> using Tile = TileN<DT, kUnroll>;
 
-// LaneRun<DT, NV>: the chunk laid out so that lane l holds NV consecutive
-// 16-byte vectors, i.e. elements [l*NV*P, (l+1)*NV*P) in token order.  Used by
-// the draws, which scan one chunk: a single wave scan over lane totals then
-// finds the crossing lane.  Elements past `n` are -inf.
+// LaneRun<DT, NV>: a chunk laid out so that thread `owner` holds NV
+// consecutive 16-byte vectors, i.e. elements [owner*NV*P, (owner+1)*NV*P) in
+// token order.  Used by the draws, which scan one chunk: a block scan over
+// the per-thread totals finds the crossing thread.  Elements past `n` are
+// -inf.
 template <int DT, int NV> struct LaneRun {
   static constexpr int P = Elem<DT>::kPerVec;
   static constexpr int kElems = NV * P;
   uint32_t w[NV][4];
 
   template <bool VEC>
-  __device__ __forceinline__ void load(const void* chunk_base, int n) {
-    const int l = lane_id();
+  __device__ __forceinline__ void load(const void* chunk_base, int n, int owner) {
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      const int e0 = (l * NV + v) * P;
+      const int e0 = (owner * NV + v) * P;
       if (VEC && e0 + P <= n) {
         const uint4 q = *reinterpret_cast<const uint4*>(
             static_cast<const char*>(chunk_base) + (size_t)e0 * Elem<DT>::kBytes);
@@ -385,7 +385,7 @@ template <int DT, int NV> struct LaneRun {
       }
     }
   }
-  // element i (0..kElems-1) of this lane, exact widening; i compile-time
+  // element i (0..kElems-1) of this thread's run, exact widening; i compile-time
   __device__ __forceinline__ float at(int i) const {
     const int v = i / P, e = i % P;
     if constexpr (DT == DSPARK_BF16) {
@@ -395,39 +395,7 @@ template <int DT, int NV> struct LaneRun {
       return __uint_as_float(w[v][e]);
     }
   }
-  // chunk index of this lane's element i
-  __device__ __forceinline__ static int index(int i) { return lane_id() * kElems + i; }
 };
-
-// Wave-cooperative copy of a chunk (n valid elements, at most kWave*NV*P) into
-// LDS words; elements past n become -inf.  NV 16-byte vectors per lane are
-// loaded first (all in flight), then written.
-template <int DT, int NV, bool VEC>
-__device__ __forceinline__ void stage_lds(const void* base, int n, uint32_t* lds) {
-  TileN<DT, NV> t;
-  t.template load<VEC>(base, n);
-  const int l = lane_id();
-  constexpr int P = Elem<DT>::kPerVec;
-  constexpr uint32_t ninf = TileN<DT, NV>::kNegInfWord;
-#pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    const bool ok = t.valid(v);
-    uint4 q = make_uint4(t.w[v][0], t.w[v][1], t.w[v][2], t.w[v][3]);
-    if (!ok) q = make_uint4(ninf, ninf, ninf, ninf);
-    reinterpret_cast<uint4*>(lds)[v * kWave + l] = q;
-  }
-  (void)P;
-}
-
-// element idx of a staged chunk (exact widening)
-template <int DT> __device__ __forceinline__ float lds_elem(const uint32_t* lds, int idx) {
-  if constexpr (DT == DSPARK_BF16) {
-    const uint32_t x = lds[idx >> 1];
-    return (idx & 1) ? __uint_as_float(x & 0xffff0000u) : __uint_as_float(x << 16);
-  } else {
-    return __uint_as_float(lds[idx]);
-  }
-}
 
 // scalar element fetch (exact widening)
 template <int DT> __device__ __forceinline__ float load_elem(const void* row, int idx) {

@@ -171,14 +171,22 @@ struct TileRef {
   int b;              // request
 };
 
+// Threads of a streaming workgroup: one workgroup per compute unit, 12 waves
+// (three per SIMD), which is what the kernel's register use allows.
+#ifndef DSPARK_STREAM_BLOCK
+#define DSPARK_STREAM_BLOCK 768
+#endif
+constexpr int kStreamBlock = DSPARK_STREAM_BLOCK;
+constexpr int kStreamWaves = kStreamBlock / kWave;
+
 // Per-workgroup plan in LDS: start[b] = index of request b's first tile,
 // start[B] = total; info[b] = L | kind << 8; cval[b] = log2(e) / T.  Request
 // b's tiles are its rows (target 0..L, then draft 0..L-1) times G chunks,
 // row-major.
 __device__ void build_plan(const VerifyArgs& a, int* start, int* info, float* cval) {
-  __shared__ int wsum[kWavesPerBlock];
+  __shared__ int wsum[kStreamWaves];
   const int tid = threadIdx.x;
-  const int per = (a.B + kBlock - 1) / kBlock;
+  const int per = (a.B + kStreamBlock - 1) / kStreamBlock;
   const int b0 = tid * per;
   int local = 0;
   for (int i = 0; i < per; ++i) {
@@ -211,7 +219,7 @@ __device__ void build_plan(const VerifyArgs& a, int* start, int* info, float* cv
       off += cnt;
     }
   }
-  if (tid == kBlock - 1) start[a.B] = off;
+  if (tid == kStreamBlock - 1) start[a.B] = off;
   __syncthreads();
 }
 
@@ -266,76 +274,85 @@ __device__ __forceinline__ void summarise_tile(const Tile<DT>& t, const TileRef&
   *ref.out = out;
 }
 
-#ifndef DSPARK_STREAM_MIN_WAVES
-#define DSPARK_STREAM_MIN_WAVES 1
-#endif
-
+// k_stream_rows: one workgroup per compute unit.  Workgroup g owns the
+// contiguous tile range [T*g/n, T*(g+1)/n) of the plan; its waves take tiles
+// from that range through an LDS counter, so that waves which the compute
+// unit's arbitration serves more slowly simply take fewer tiles.
 template <int DT, bool VEC>
-__global__ void __launch_bounds__(kBlock, DSPARK_STREAM_MIN_WAVES) k_stream_rows(VerifyArgs a) {
+__global__ void __launch_bounds__(kStreamBlock) k_stream_rows(VerifyArgs a) {
   extern __shared__ int plan[];
+  __shared__ int s_next;
   int* start = plan;                                        // [B + 1]
   int* info = plan + a.B + 1;                               // [B]
   float* cval = reinterpret_cast<float*>(plan + 2 * a.B + 1);  // [B]
   build_plan(a, start, info, cval);
   const int total = uniform(start[a.B]);
-  const int W = gridDim.x * kWavesPerBlock;
-  int t0 = uniform((int)(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave));
+  const int n = gridDim.x, g = blockIdx.x;
+  const int per = total / n, rem = total - per * n;
+  const int begin = uniform(g * per + min(g, rem));
+  const int end = uniform(begin + per + (g < rem ? 1 : 0));
+  if (threadIdx.x == 0) s_next = begin + kStreamWaves;
+  __syncthreads();
+  const int w = uniform((int)(threadIdx.x / kWave));
+  // next tile index for this wave (one LDS atomic by lane 0)
+  auto grab = [&]() -> int {
+    int x = 0;
+    if (lane_id() == 0) x = atomicAdd(&s_next, 1);
+    return uniform(readlane(x, 0));
+  };
+  int t0 = begin + w;
   // Two tile buffers: the next tile's loads are in flight while the current
   // one is summarised.  The prefetch is issued unconditionally (past the end
-  // of the list a wave re-reads its current tile, a cache hit, and drops
+  // of the range a wave re-reads its current tile, a cache hit, and drops
   // it), so every path has the same loads outstanding and the compiler can
   // wait for the older tile only.
   Tile<DT> A, Bt;
   TileRef ra, rb;
-  if (t0 >= total) return;
+  if (t0 >= end) return;
   ra = decode_tile<DT>(a, start, info, t0);
   A.template load<VEC>(ra.base, ra.n);
   while (true) {
-    const int t1 = t0 + W;
-    rb = decode_tile<DT>(a, start, info, t1 < total ? t1 : t0);
+    const int t1 = grab();
+    rb = decode_tile<DT>(a, start, info, t1 < end ? t1 : t0);
     Bt.template load<VEC>(rb.base, rb.n);
     summarise_tile<DT>(A, ra, uniform(info[ra.b]) >> 8, uniform(cval[ra.b]));
-    if (t1 >= total) break;
-    t0 = t1 + W;
-    ra = decode_tile<DT>(a, start, info, t0 < total ? t0 : t1);
+    if (t1 >= end) break;
+    t0 = grab();
+    ra = decode_tile<DT>(a, start, info, t0 < end ? t0 : t1);
     A.template load<VEC>(ra.base, ra.n);
     summarise_tile<DT>(Bt, rb, uniform(info[rb.b]) >> 8, uniform(cval[rb.b]));
-    if (t0 >= total) break;
+    if (t0 >= end) break;
   }
 }
 
 // ------------------------------------------------------------------ merges
 
-// Softmax row from its chunk summaries: shift K* = max k_c over chunks with
-// mass, S = sum_c s_c * 2^(k_c - K*) (exact scaling).  Wave-cooperative.
-__device__ RowSum merge_softmax_row(const Partial* p, int G) {
+__device__ __forceinline__ int shift_amount(float d) { return d < -2000.f ? -2000 : (int)d; }
+
+// Chunk summaries of one row folded into a merged row, wave-cooperatively.
+// Each lane folds the chunks c = lane, lane + 64, ... (the first one passed
+// in, already loaded) with exact power-of-two rescaling, then the wave takes
+// K* = max shift and S = sum of the lane sums scaled to K*.
+__device__ RowSum merge_softmax(Partial first, const Partial* p, int G) {
   const int l = lane_id();
   float km = -INFINITY;
   double s = 0.0;
   int fl = 0;
-  for (int c0 = 0; c0 < G; c0 += kWave) {
-    const int c = c0 + l;
-    if (c < G) {
-      fl |= p[c].idx;
-      if (p[c].s > 0.0) km = fmaxf(km, p[c].k);
-    }
-  }
-  km = wave_max(km);
-  if (km > -INFINITY) {
-    for (int c0 = 0; c0 < G; c0 += kWave) {
-      const int c = c0 + l;
-      if (c < G) {
-        const double sc = p[c].s;
-        if (sc > 0.0) {
-          const float d = p[c].k - km;  // integer valued, <= 0
-          s += ldexp(sc, d < -2000.f ? -2000 : (int)d);
-        }
+  Partial q = first;
+  for (int c = l; c < G; c += kWave) {
+    if (c != l) q = p[c];
+    fl |= q.idx;
+    if (q.s > 0.0) {
+      if (q.k > km) {
+        s = ldexp(s, shift_amount(km - q.k));
+        km = q.k;
       }
+      s += ldexp(q.s, shift_amount(q.k - km));
     }
   }
   RowSum r;
-  r.k = km;
-  r.s = wave_sum(s);
+  r.k = wave_max(km);
+  r.s = wave_sum(km > -INFINITY ? ldexp(s, shift_amount(km - r.k)) : 0.0);
   r.idx = 0;
   r.bad = wave_or(fl);
   r.pad = 0;
@@ -343,13 +360,15 @@ __device__ RowSum merge_softmax_row(const Partial* p, int G) {
 }
 
 // Greedy row: (max, lowest index) over its chunk summaries.
-__device__ RowSum merge_argmax_row(const Partial* p, int G) {
+__device__ RowSum merge_argmax(Partial first, const Partial* p, int G) {
   const int l = lane_id();
   float best = -INFINITY;
   int bi = 0x7fffffff, fl = 0;
+  Partial q = first;
   for (int c = l; c < G; c += kWave) {
-    argmax_merge(best, bi, p[c].k, p[c].idx);
-    fl |= (int)p[c].s;
+    if (c != l) q = p[c];
+    argmax_merge(best, bi, q.k, q.idx);
+    fl |= (int)q.s;
   }
   wave_argmax(best, bi);
   RowSum r;
@@ -367,151 +386,16 @@ __device__ __forceinline__ double row_prob(float x, float c, float kmax, double 
   return exp2_f64((double)x * (double)c - (double)kmax) / S;
 }
 
-// k_merge: one wave per row slot (request, row j, side), merging the chunk
-// summaries of every scheduled row once.
-__global__ void __launch_bounds__(kBlock) k_merge(VerifyArgs a) {
-  const int slot = uniform((int)(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave));
-  const int per_req = 2 * (a.K + 1);
-  if (slot >= a.B * per_req) return;
-  const int b = slot / per_req;
-  const int j = (slot - b * per_req) >> 1;
-  const int side = slot & 1;
-  const ReqInfo r = req_info(a, b);
-  if (r.kind == kKindSkip || j > r.L) return;
-  if (side == 1 && (r.kind != kKindSoftmax || j >= r.L)) return;
-  const Partial* pr = row_parts(a, b, j, side);
-  const RowSum m = r.kind == kKindSoftmax ? merge_softmax_row(pr, a.G) : merge_argmax_row(pr, a.G);
-  if (lane_id() == 0) a.rows[slot] = m;
-}
-
-__device__ __forceinline__ const RowSum& row_sum(const VerifyArgs& a, int b, int j, int side) {
-  return a.rows[((size_t)b * (a.K + 1) + j) * 2 + side];
-}
-
-// ------------------------------------------------------------------ draws
-
-// Chunk masses of one draw, held in registers (up to kMaxGroups*64 chunks;
-// more are re-read): total, then the chunk whose inclusive prefix first
-// exceeds u * total (if rounding leaves none, the last chunk with mass and
-// `past_end`), and `base`, the mass before it.
-constexpr int kMaxGroups = 4;
-template <typename ChunkFn>
-__device__ int locate_chunk(ChunkFn chunk_mass, int G, double u, double& total, double& base,
-                            bool& past_end) {
-  const int l = lane_id();
-  double w[kMaxGroups];
-  double sum = 0.0;
-#pragma unroll
-  for (int i = 0; i < kMaxGroups; ++i) {
-    const int c = i * kWave + l;
-    w[i] = c < G ? chunk_mass(c) : 0.0;
-    sum += w[i];
-  }
-  for (int c = kMaxGroups * kWave + l; c < G; c += kWave) sum += chunk_mass(c);
-  total = wave_sum(sum);
-  const double target = u * total;
-  int cstar = -1, clast = -1;
-  base = 0.0;
-  for (int c0 = 0; c0 < G && cstar < 0; c0 += kWave) {
-    const int g = c0 / kWave;
-    double x = 0.0;
-#pragma unroll
-    for (int i = 0; i < kMaxGroups; ++i)
-      if (i == g) x = w[i];
-    if (g >= kMaxGroups) x = c0 + l < G ? chunk_mass(c0 + l) : 0.0;
-    const double incl = wave_incl_scan(x);
-    const uint64_t hit = __ballot(base + incl > target && x > 0.0);
-    const uint64_t pos = __ballot(x > 0.0);
-    if (pos) clast = c0 + 63 - __builtin_clzll(pos);
-    if (hit) {
-      const int hl = __builtin_ctzll(hit);
-      cstar = c0 + hl;
-      base += readlane(incl - x, hl);
-    } else {
-      base += readlane(incl, kWave - 1);
-    }
-  }
-  past_end = cstar < 0;
-  return past_end ? clast : cstar;
-}
-
-// Inside one chunk held as LaneRuns (lane l owns a contiguous run of N
-// tokens), the first token whose running mass exceeds `target`, else the last
-// token with mass (-1 if none).  mass(i) is this lane's element i.
-template <int N, typename MassFn>
-__device__ int scan_runs(MassFn mass, double target) {
-  const int l = lane_id();
-  double ls = 0.0;
-  int lp = -1;
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const double m = mass(i);
-    ls += m;
-    if (m > 0.0) lp = l * N + i;
-  }
-  const double incl = wave_incl_scan(ls);
-  const uint64_t hit = __ballot(incl > target && ls > 0.0);
-  int found = -1;
-  if (hit) {
-    const int x = __builtin_ctzll(hit);
-    if (l == x) {
-      double run = incl - ls;
-#pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const double m = mass(i);
-        run += m;
-        if (found < 0 && run > target && m > 0.0) found = l * N + i;
-      }
-      if (found < 0) found = lp;
-    }
-    found = readlane(found, x);
-  } else {
-    found = wave_max_i(lp);
-  }
-  return found;
-}
-
-// Draw from the softmax of target row `row` (bonus token, or the fallback of
-// an all-zero residual): chunk masses come from the row's pass-1 summaries
-// scaled to the merged shift; the chosen chunk is recomputed with the same
-// fp32 arithmetic.  One wave.
-template <int DT, bool VEC>
-__device__ int draw_from_p(const VerifyArgs& a, int b, int row, float c, double u) {
-  constexpr int S = Elem<DT>::kBytes;
-  constexpr int E = item_elems<DT>();
-  const Partial* pr = row_parts(a, b, row, 0);
-  const float kp = row_sum(a, b, row, 0).k;
-  auto chunk_mass = [&](int ci) -> double {
-    const Partial p = pr[ci];
-    if (!(p.s > 0.0)) return 0.0;
-    const float d = p.k - kp;
-    return ldexp(p.s, d < -2000.f ? -2000 : (int)d);
-  };
-  double total, base;
-  bool past_end;
-  const int cstar = locate_chunk(chunk_mass, a.G, u, total, base, past_end);
-  if (cstar < 0) return 0;
-  const int e0 = cstar * E;
-  const int n = min(E, a.V - e0);
-  LaneRun<DT, kUnroll> run;
-  run.template load<VEC>(target_row(a, b, row, S) + (size_t)e0 * S, n);
-  const float kc = pr[cstar].k;
-  const float d = kc - kp;
-  const int sh = d < -2000.f ? -2000 : (int)d;
-  const int f = scan_runs<LaneRun<DT, kUnroll>::kElems>(
-      [&](int i) -> double { return ldexp((double)fast_exp2(fmaf(run.at(i), c, -kc)), sh); },
-      past_end ? INFINITY : u * total - base);
-  return e0 + (f >= 0 ? f : 0);
-}
-
 // Residual p - q of one row pair at fp32 speed, with the elements whose
 // normalised p or q reaches 2^-12 redone in fp64 (their fp32 rounding would
 // show after dividing by a small residual mass).
 struct ResidualRows {
   float c, nbt, nbd, kt, kd;
-  double st, sd;
-  __device__ ResidualRows(float c_, float kt_, double st_, float kd_, double sd_)
-      : c(c_), kt(kt_), kd(kd_), st(st_), sd(sd_) {
+  double rst, rsd;  // 1 / S of the target and draft rows
+  __device__ ResidualRows(float c_, float kt_, double st, float kd_, double sd)
+      : c(c_), kt(kt_), kd(kd_) {
+    rst = 1.0 / st;
+    rsd = 1.0 / sd;
     nbt = (float)(-(double)kt - log2(st));
     nbd = (float)(-(double)kd - log2(sd));
   }
@@ -522,38 +406,59 @@ struct ResidualRows {
     return fmaxf(p - q, 0.f);
   }
   __device__ __forceinline__ double exact(float xt, float xd) const {
-    const double p = exp2_f64((double)xt * (double)c - (double)kt) / st;
-    const double q = exp2_f64((double)xd * (double)c - (double)kd) / sd;
+    const double p = exp2_f64((double)xt * (double)c - (double)kt) * rst;
+    const double q = exp2_f64((double)xd * (double)c - (double)kd) * rsd;
     return fmax(p - q, 0.0);
-  }
-  // the value every kernel uses for one element
-  __device__ __forceinline__ double mass(float xt, float xd) const {
-    float big;
-    const float r = fast(xt, xd, big);
-    return big >= kHeavy ? exact(xt, xd) : (double)r;
   }
 };
 
-// Residual pieces: 2048 tokens (bf16) or 1024 (fp32), i.e. 4 vectors a lane.
-constexpr int kPieceVecs = 4;
-template <int DT> constexpr int piece_elems() { return kWave * kPieceVecs * Elem<DT>::kPerVec; }
-template <int DT> __host__ __device__ inline int pieces_per_row(int V) {
-  return (V + piece_elems<DT>() - 1) / piece_elems<DT>();
+// element i of a register-held run, i only known at run time (select chain)
+template <int DT, int NV>
+__device__ __forceinline__ float run_elem(const uint32_t (&w)[NV][4], int i) {
+  constexpr int P = Elem<DT>::kPerVec;
+  constexpr int WPV = 4;
+  const int word = DT == DSPARK_BF16 ? (i >> 1) : i;  // word index within the run
+  uint32_t x = 0;
+#pragma unroll
+  for (int v = 0; v < NV; ++v)
+#pragma unroll
+    for (int q = 0; q < WPV; ++q)
+      if (word == v * WPV + q) x = w[v][q];
+  (void)P;
+  if constexpr (DT == DSPARK_BF16)
+    return (i & 1) ? __uint_as_float(x & 0xffff0000u) : __uint_as_float(x << 16);
+  else
+    return __uint_as_float(x);
 }
 
-// Residual mass of one piece (wave total).
+// element e of one 16-byte vector, e only known at run time
+template <int DT>
+__device__ __forceinline__ float vec_elem(const uint32_t (&w)[4], int e) {
+  const int word = DT == DSPARK_BF16 ? (e >> 1) : e;
+  const uint32_t x = word == 0 ? w[0] : word == 1 ? w[1] : word == 2 ? w[2] : w[3];
+  if constexpr (DT == DSPARK_BF16)
+    return (e & 1) ? __uint_as_float(x & 0xffff0000u) : __uint_as_float(x << 16);
+  else
+    return __uint_as_float(x);
+}
+
+// Residual mass of one chunk of the rejected row pair (wave total).  Vector
+// by vector: the fp32 terms, then, for a vector holding an element with p or
+// q >= 2^-12, those elements again in fp64 (a rolled loop).  The empty asm
+// statements keep each vector's work in place, so that the compiler does not
+// spread all vectors' conversions over the whole pass.
 template <int DT, bool VEC>
-__device__ double residual_piece_mass(const ResidualRows& rr, const char* tpiece,
-                                      const char* dpiece, int n) {
+__device__ double residual_chunk_mass(const ResidualRows& rr, const char* tchunk,
+                                      const char* dchunk, int n) {
   constexpr int P = Elem<DT>::kPerVec;
-  constexpr int H = kPieceVecs;
-  TileN<DT, H> tt, td;
-  tt.template load<VEC>(tpiece, n);
-  td.template load<VEC>(dpiece, n);
+  constexpr int U = kUnroll;
+  Tile<DT> tt, td;
+  tt.template load<VEC>(tchunk, n);
+  td.template load<VEC>(dchunk, n);
   float light = 0.f;
-  float vbig[H];
+  double heavy = 0.0;
 #pragma unroll
-  for (int v = 0; v < H; ++v) {
+  for (int v = 0; v < U; ++v) {
     float r[P];
     float hv = 0.f;
 #pragma unroll
@@ -564,35 +469,50 @@ __device__ double residual_piece_mass(const ResidualRows& rr, const char* tpiece
       r[e] = big >= kHeavy ? 0.f : x;
     }
     const bool ok = tt.valid(v);
-    vbig[v] = ok ? hv : 0.f;
     float s4 = (r[0] + r[1]) + (r[2] + r[3]);
     if constexpr (P == 8) s4 += (r[4] + r[5]) + (r[6] + r[7]);
     light += ok ? s4 : 0.f;
-  }
-  // heavy elements in fp64; a vector without any is skipped by the wave
-  double heavy = 0.0;
-#pragma unroll
-  for (int v = 0; v < H; ++v) {
-    if (vbig[v] >= kHeavy) {
-#pragma unroll
+    if (ok && hv >= kHeavy) {
+      const uint32_t wt[4] = {tt.w[v][0], tt.w[v][1], tt.w[v][2], tt.w[v][3]};
+      const uint32_t wd[4] = {td.w[v][0], td.w[v][1], td.w[v][2], td.w[v][3]};
+#pragma unroll 1
       for (int e = 0; e < P; ++e) {
+        const float xt = vec_elem<DT>(wt, e), xd = vec_elem<DT>(wd, e);
         float big;
-        rr.fast(tt.at(v, e), td.at(v, e), big);
-        if (big >= kHeavy) heavy += rr.exact(tt.at(v, e), td.at(v, e));
+        rr.fast(xt, xd, big);
+        if (big >= kHeavy) heavy += rr.exact(xt, xd);
       }
     }
+    asm volatile("" : "+v"(light), "+v"(heavy));
   }
   return wave_sum((double)light + heavy);
 }
 
 // ------------------------------------------------------------------ decide
 
+// k_decide: `groups` workgroups of kDecideBlock threads per request.  Each
+// merges the request's row summaries (waves take rows in turn, a few rows'
+// loads in flight at once), then wave 0 decides: p(y), q(y), alpha, the
+// accept ballot, the first rejection.  Workgroup 0 writes the outputs and the
+// draw state.  On a rejection every wave then sums the residual mass of one
+// chunk of the rejected row pair.
+#ifndef DSPARK_DECIDE_BLOCK
+#define DSPARK_DECIDE_BLOCK 256
+#endif
+#ifndef DSPARK_ROWS_IN_FLIGHT
+#define DSPARK_ROWS_IN_FLIGHT 4
+#endif
+constexpr int kDecideBlock = DSPARK_DECIDE_BLOCK;
+constexpr int kDecideWaves = kDecideBlock / kWave;
+constexpr int kRowsInFlight = DSPARK_ROWS_IN_FLIGHT;
+constexpr int kMaxRows = 2 * 64 + 1;
+
 template <int DT, bool VEC>
-__global__ void __launch_bounds__(kBlock) k_decide(VerifyArgs a) {
+__global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
   constexpr int S = Elem<DT>::kBytes;
-  constexpr int PE = piece_elems<DT>();
+  constexpr int E = item_elems<DT>();
+  __shared__ RowSum s_rows[kMaxRows + 2];  // merged rows, then the rejected pair
   __shared__ int s_a, s_bad;
-  __shared__ RowSum s_rt, s_rd;
   const int b = blockIdx.x / a.groups;
   const int g = blockIdx.x - b * a.groups;
   const int w = uniform((int)(threadIdx.x / kWave));
@@ -618,45 +538,73 @@ __global__ void __launch_bounds__(kBlock) k_decide(VerifyArgs a) {
     }
     return;
   }
+  const bool soft = r.kind == kKindSoftmax;
+
+  // wave 0, lane l: position l+1's drafted id, its two logits and uniform,
+  // loaded now so that they arrive during the merges
+  int y = 0;
+  bool yok = true;
+  float xt = 0.f, xd = 0.f, u = 0.f;
+  if (w == 0 && l < L) {
+    y = a.drafted[(size_t)b * K + l];
+    yok = y >= 0 && y < a.V;
+    if (yok) {
+      xt = load_elem<DT>(target_row(a, b, l, S), y);
+      if (soft) xd = load_elem<DT>(draft_row(a, b, l, S), y);
+    }
+    if (soft) u = a.uniforms[(size_t)b * (K + 1) + l];
+  }
+
+  // merges: row index q in [0, nrows): target rows 0..L, then draft rows 0..L-1
+  const int nrows = soft ? 2 * L + 1 : L + 1;
+  for (int q0 = w; q0 < nrows; q0 += kDecideWaves * kRowsInFlight) {
+    Partial first[kRowsInFlight];
+    const Partial* base[kRowsInFlight];
+#pragma unroll
+    for (int i = 0; i < kRowsInFlight; ++i) {
+      const int q = q0 + i * kDecideWaves;
+      const int side = q <= L ? 0 : 1;
+      const int j = side ? q - L - 1 : q;
+      base[i] = row_parts(a, b, q < nrows ? j : 0, q < nrows ? side : 0);
+      first[i] = l < a.G ? base[i][l] : Partial{-INFINITY, 0x7fffffff, 0.0};
+    }
+#pragma unroll
+    for (int i = 0; i < kRowsInFlight; ++i) {
+      const int q = q0 + i * kDecideWaves;
+      if (q < nrows) {
+        const RowSum m = soft ? merge_softmax(first[i], base[i], a.G)
+                              : merge_argmax(first[i], base[i], a.G);
+        if (l == 0) s_rows[q] = m;
+      }
+    }
+  }
+  __syncthreads();
 
   if (w == 0) {
-    // lane l: position l+1 (drafted id, its logits, merged rows 0..L)
     int bad = r.bad;
-    int y = 0;
-    bool yok = true;
-    float xt = 0.f, xd = 0.f, u = 0.f;
-    if (l < L) {
-      y = a.drafted[(size_t)b * K + l];
-      yok = y >= 0 && y < a.V;
-      if (yok) {
-        xt = load_elem<DT>(target_row(a, b, l, S), y);
-        if (r.kind == kKindSoftmax) xd = load_elem<DT>(draft_row(a, b, l, S), y);
-      }
-      if (r.kind == kKindSoftmax) u = a.uniforms[(size_t)b * (K + 1) + l];
-    }
     RowSum rt{}, rd{};
-    if (l <= L) rt = row_sum(a, b, l, 0);
-    if (l < L && r.kind == kKindSoftmax) rd = row_sum(a, b, l, 1);
+    if (l <= L) rt = s_rows[l];
+    if (soft && l < L) rd = s_rows[L + 1 + l];
     RowSum r64{};
-    if (L == 64) r64 = row_sum(a, b, 64, 0);  // the row past lane 63
+    if (L == 64) r64 = s_rows[64];  // the row past lane 63
     if (!yok) bad |= DSPARK_DEV_BAD_TOKEN;
     if (l <= L) bad |= rt.bad;
     if (l < L) bad |= rd.bad;
     if (L == 64 && l == 0) bad |= r64.bad;
     bool acc = false;
     float pf = 0.f, qf = 0.f;
-    if (r.kind == kKindSoftmax) {
+    if (soft) {
       if (l <= L && !(rt.s > 0.0)) bad |= DSPARK_DEV_NONFINITE;  // no finite logit
       if (l < L) {
         if (!(rd.s > 0.0)) bad |= DSPARK_DEV_NONFINITE;
         if (!(u >= 0.f && u < 1.f)) bad |= DSPARK_DEV_BAD_UNIFORM;
         if (yok) {
           const double p = row_prob(xt, r.c, rt.k, rt.s);
-          const double q = row_prob(xd, r.c, rd.k, rd.s);
-          const double alpha = p == 0.0 ? 0.0 : (q == 0.0 ? 1.0 : fmin(1.0, p / q));
+          const double qv = row_prob(xd, r.c, rd.k, rd.s);
+          const double alpha = p == 0.0 ? 0.0 : (qv == 0.0 ? 1.0 : fmin(1.0, p / qv));
           acc = (double)u < alpha;
           pf = (float)p;
-          qf = (float)q;
+          qf = (float)qv;
         }
       }
       if (l == 0) {
@@ -674,25 +622,41 @@ __global__ void __launch_bounds__(kBlock) k_decide(VerifyArgs a) {
     const uint64_t rej = ~m & want;
     const int an = rej ? __builtin_ctzll(rej) : L;
     bad = wave_or(bad);
-    int gtok = 0;
-    if (r.kind == kKindGreedy) gtok = an < 64 ? readlane(rt.idx, an) : readlane(r64.idx, 0);
     if (lead) {
+      int gtok = 0;
+      if (!soft) gtok = an < 64 ? readlane(rt.idx, an) : readlane(r64.idx, 0);
       if (l < K) {
         if (a.p_tok) a.p_tok[(size_t)b * K + l] = pf;
         if (a.q_tok) a.q_tok[(size_t)b * K + l] = qf;
       }
       for (int i = l; i <= K; i += kWave) {
         if (i < an) tok[i] = a.drafted[(size_t)b * K + i];
-        else if (i > an || r.kind == kKindGreedy) tok[i] = i == an ? gtok : -1;
+        else if (i > an || !soft) tok[i] = i == an ? gtok : -1;
       }
+      // draw state: the target row of the draw and, on a rejection, the
+      // draft row's shift and sum as well
+      const RowSum dt = an < 64 ? RowSum{readlane(rt.s, an), readlane(rt.k, an), 0, 0, 0} : r64;
+      const RowSum dd = an < L ? RowSum{readlane(rd.s, an), readlane(rd.k, an), 0, 0, 0} : RowSum{};
       if (l == 0) {
         a.accepted[b] = an;
         if (bad) flag(a.dev_status, bad);
+        ReqState st;
+        st.mode = (!soft || (bad & (DSPARK_DEV_BAD_TOKEN | DSPARK_DEV_NONFINITE)))
+                      ? kModeNone
+                      : (an == L ? kModeBonus : kModeResidual);
+        st.row = an;
+        st.a = an;
+        st.c = r.c;
+        st.kt = dt.k;
+        st.st = dt.s;
+        st.kd = dd.k;
+        st.sd = dd.s;
+        a.req[b] = st;
       }
     }
     if (an < L && an == l) {
-      s_rt = rt;
-      s_rd = rd;
+      s_rows[kMaxRows] = rt;  // the rejected target row
+      s_rows[kMaxRows + 1] = rd;  // and its draft row
     }
     if (l == 0) {
       s_a = an;
@@ -702,84 +666,245 @@ __global__ void __launch_bounds__(kBlock) k_decide(VerifyArgs a) {
   __syncthreads();
   const int an = s_a;
   const int bad = s_bad;
-  if (r.kind == kKindGreedy || (bad & (DSPARK_DEV_BAD_TOKEN | DSPARK_DEV_NONFINITE))) {
-    // greedy requests are complete; faulty ones have unspecified outputs
-    if (lead && threadIdx.x == 0) a.req[b].mode = kModeNone;
-    return;
-  }
-  if (an == L) {
-    // everything accepted: k_draw draws the bonus token from target row L
-    if (lead && threadIdx.x == 0) {
-      ReqState& st = a.req[b];
-      st.mode = kModeBonus;
-      st.row = L;
-      st.a = an;
-      st.c = r.c;
-    }
-    return;
-  }
-  // rejection at position an+1: residual mass of this workgroup's pieces
-  const RowSum rt = s_rt, rd = s_rd;
+  // greedy requests are complete, faulty ones have unspecified outputs, and
+  // after a full acceptance k_draw draws the bonus token from pass-1 sums
+  if (!soft || (bad & (DSPARK_DEV_BAD_TOKEN | DSPARK_DEV_NONFINITE)) || an == L) return;
+  const RowSum rt = s_rows[kMaxRows], rd = s_rows[kMaxRows + 1];
   const ResidualRows rr(r.c, rt.k, rt.s, rd.k, rd.s);
-  if (lead && threadIdx.x == 0) {
-    ReqState& st = a.req[b];
-    st.mode = kModeResidual;
-    st.row = an;
-    st.a = an;
-    st.c = r.c;
-    st.kt = rr.kt;
-    st.kd = rr.kd;
-    st.st = rr.st;
-    st.sd = rr.sd;
-  }
-  const int G2 = pieces_per_row<DT>(a.V);
-  const int pi = g * kWavesPerBlock + w;
-  if (pi < G2) {
-    const int e0 = pi * PE;
-    const int n = min(PE, a.V - e0);
-    const double z = residual_piece_mass<DT, VEC>(rr, target_row(a, b, an, S) + (size_t)e0 * S,
+  const int pi = g * kDecideWaves + w;
+  if (pi < a.G) {
+    const int e0 = pi * E;
+    const int n = min(E, a.V - e0);
+    const double z = residual_chunk_mass<DT, VEC>(rr, target_row(a, b, an, S) + (size_t)e0 * S,
                                                   draft_row(a, b, an, S) + (size_t)e0 * S, n);
-    if (l == 0) a.part2[(size_t)b * G2 + pi] = z;
+    if (l == 0) a.part2[(size_t)b * a.G + pi] = z;
   }
 }
 
 // ------------------------------------------------------------------ draw
 
+// Block-wide helpers for kBlock threads (4 waves); every thread must call
+// them (they synchronise).
+__device__ __forceinline__ double block_sum(double x, double* s_w) {
+  const double t = wave_sum(x);
+  const int w = threadIdx.x / kWave;
+  if (lane_id() == 0) s_w[w] = t;
+  __syncthreads();
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < kWavesPerBlock; ++i) s += s_w[i];
+  __syncthreads();
+  return s;
+}
+
+// Inclusive scan over the block in thread order; also the block total.
+__device__ __forceinline__ double block_incl_scan(double x, double* s_w, double& total) {
+  const double incl = wave_incl_scan(x);
+  const int w = threadIdx.x / kWave;
+  if (lane_id() == kWave - 1) s_w[w] = incl;
+  __syncthreads();
+  double pre = 0.0, tot = 0.0;
+#pragma unroll
+  for (int i = 0; i < kWavesPerBlock; ++i) {
+    const double v = s_w[i];
+    if (i < w) pre += v;
+    tot += v;
+  }
+  __syncthreads();
+  total = tot;
+  return pre + incl;
+}
+
+// lowest thread of the block with `pred` (kBlock if none)
+__device__ __forceinline__ int block_first(bool pred, int* s_i) {
+  const uint64_t bal = __ballot(pred);
+  const int w = threadIdx.x / kWave;
+  if (lane_id() == 0) s_i[w] = bal ? w * kWave + __builtin_ctzll(bal) : kBlock;
+  __syncthreads();
+  int f = kBlock;
+#pragma unroll
+  for (int i = 0; i < kWavesPerBlock; ++i) f = min(f, s_i[i]);
+  __syncthreads();
+  return f;
+}
+
+__device__ __forceinline__ int block_max_i(int x, int* s_i) {
+  const int m = wave_max_i(x);
+  const int w = threadIdx.x / kWave;
+  if (lane_id() == 0) s_i[w] = m;
+  __syncthreads();
+  int f = INT_MIN;
+#pragma unroll
+  for (int i = 0; i < kWavesPerBlock; ++i) f = max(f, s_i[i]);
+  __syncthreads();
+  return f;
+}
+
+struct DrawShared {
+  double w[kWavesPerBlock];
+  int i[kWavesPerBlock];
+  double base;
+  int found;
+};
+
+// Inverse CDF over n non-negative weights f(0..n-1), in index order: the first
+// index whose running sum exceeds u * total (and has weight), else the last
+// index with weight (`past_end`), else -1.  `base` = the sum before it.
+template <typename F>
+__device__ int block_locate(F f, int n, double u, double& total, double& base, bool& past_end,
+                            DrawShared& sh) {
+  const int tid = threadIdx.x;
+  const double x0 = tid < n ? f(tid) : 0.0;
+  double part = x0;
+  for (int i = tid + kBlock; i < n; i += kBlock) part += f(i);
+  total = block_sum(part, sh.w);
+  const double target = u * total;
+  double run = 0.0;
+  int last = -1;
+  for (int r0 = 0; r0 < n; r0 += kBlock) {
+    const int i = r0 + tid;
+    const double x = r0 == 0 ? x0 : (i < n ? f(i) : 0.0);
+    double rtot;
+    const double incl = block_incl_scan(x, sh.w, rtot);
+    const int hit = block_first(run + incl > target && x > 0.0, sh.i);
+    last = max(last, block_max_i(x > 0.0 ? i : -1, sh.i));
+    if (hit < kBlock) {
+      if (tid == hit) sh.base = run + (incl - x);
+      __syncthreads();
+      base = sh.base;
+      past_end = false;
+      return r0 + hit;
+    }
+    run += rtot;
+  }
+  base = run;
+  past_end = true;
+  return last;
+}
+
+// Inside one chunk (n elements, R per thread in a contiguous run), the first
+// element whose running mass exceeds `target`, else the last with mass, else
+// 0.  mass(i) gives this thread's element i (0..R-1) as a double.
+template <int R, typename M>
+__device__ int block_scan_chunk(M mass, double target, DrawShared& sh) {
+  const int tid = threadIdx.x;
+  double m[R];
+  double ls = 0.0;
+  int lp = -1;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    m[i] = mass(i);
+    ls += m[i];
+    if (m[i] > 0.0) lp = tid * R + i;
+  }
+  double tot;
+  const double incl = block_incl_scan(ls, sh.w, tot);
+  const int x = block_first(incl > target && ls > 0.0, sh.i);
+  if (x < kBlock) {
+    if (tid == x) {
+      double run = incl - ls;
+      int found = -1;
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        run += m[i];
+        if (found < 0 && run > target && m[i] > 0.0) found = tid * R + i;
+      }
+      sh.found = found >= 0 ? found : lp;
+    }
+    __syncthreads();
+    return sh.found;
+  }
+  const int f = block_max_i(lp, sh.i);
+  return f >= 0 ? f : 0;
+}
+
+// Draw from the softmax of target row `row` (bonus token, or the fallback of
+// an all-zero residual): chunk masses come from the row's pass-1 summaries
+// scaled to the merged shift kp; the chosen chunk is recomputed with the same
+// fp32 arithmetic as pass 1.
+template <int DT, bool VEC>
+__device__ int draw_from_p(const VerifyArgs& a, int b, int row, float c, float kp, double u,
+                           DrawShared& sh) {
+  constexpr int S = Elem<DT>::kBytes;
+  constexpr int E = item_elems<DT>();
+  constexpr int R = E / kBlock;
+  constexpr int NV = R / Elem<DT>::kPerVec;
+  const Partial* pr = row_parts(a, b, row, 0);
+  double total, base;
+  bool past_end;
+  const int cstar = block_locate(
+      [&](int ci) -> double {
+        const Partial p = pr[ci];
+        return p.s > 0.0 ? ldexp(p.s, shift_amount(p.k - kp)) : 0.0;
+      },
+      a.G, u, total, base, past_end, sh);
+  if (cstar < 0) return 0;
+  const int e0 = cstar * E;
+  const int n = min(E, a.V - e0);
+  LaneRun<DT, NV> run;
+  run.template load<VEC>(target_row(a, b, row, S) + (size_t)e0 * S, n, threadIdx.x);
+  const float kc = pr[cstar].k;
+  const int sh_c = shift_amount(kc - kp);
+  const int f = block_scan_chunk<R>(
+      [&](int i) -> double { return ldexp((double)fast_exp2(fmaf(run.at(i), c, -kc)), sh_c); },
+      past_end ? INFINITY : u * total - base, sh);
+  return e0 + f;
+}
+
+// k_draw: one workgroup per request with a pending draw.
 template <int DT, bool VEC>
 __global__ void __launch_bounds__(kBlock) k_draw(VerifyArgs a) {
   constexpr int S = Elem<DT>::kBytes;
-  constexpr int PE = piece_elems<DT>();
-  const int b = uniform((int)(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave));
-  if (b >= a.B) return;
+  constexpr int E = item_elems<DT>();
+  constexpr int R = E / kBlock;
+  constexpr int NV = R / Elem<DT>::kPerVec;
+  __shared__ DrawShared sh;
+  const int b = blockIdx.x;
   const ReqState st = a.req[b];
   if (st.mode != kModeResidual && st.mode != kModeBonus) return;
   const int K = a.K;
-  const int G2 = pieces_per_row<DT>(a.V);
   const double u = (double)a.uniforms[(size_t)b * (K + 1) + K];
   int t = 0;
   bool from_p = st.mode == kModeBonus;
   if (!from_p) {
-    const double* z = a.part2 + (size_t)b * G2;
+    const double* z = a.part2 + (size_t)b * a.G;
     double Z, base;
     bool past_end;
-    const int pstar = locate_chunk([&](int ci) -> double { return z[ci]; }, G2, u, Z, base, past_end);
-    if (!(Z > 0.0)) {
+    const int pstar = block_locate([&](int ci) -> double { return z[ci]; }, a.G, u, Z, base,
+                                   past_end, sh);
+    if (!(Z > 0.0) || pstar < 0) {
       from_p = true;  // no residual mass: draw from p at the rejected position
-    } else if (pstar >= 0) {
+    } else {
       const ResidualRows rr(st.c, st.kt, st.st, st.kd, st.sd);
-      const int e0 = pstar * PE;
-      const int n = min(PE, a.V - e0);
-      LaneRun<DT, kPieceVecs> rt, rd;
-      rt.template load<VEC>(target_row(a, b, st.row, S) + (size_t)e0 * S, n);
-      rd.template load<VEC>(draft_row(a, b, st.row, S) + (size_t)e0 * S, n);
-      const int f = scan_runs<LaneRun<DT, kPieceVecs>::kElems>(
-          [&](int i) -> double { return rr.mass(rt.at(i), rd.at(i)); },
-          past_end ? INFINITY : u * Z - base);
-      t = e0 + (f >= 0 ? f : 0);
+      const int e0 = pstar * E;
+      const int n = min(E, a.V - e0);
+      LaneRun<DT, NV> rt, rd;
+      rt.template load<VEC>(target_row(a, b, st.row, S) + (size_t)e0 * S, n, threadIdx.x);
+      rd.template load<VEC>(draft_row(a, b, st.row, S) + (size_t)e0 * S, n, threadIdx.x);
+      // fp32 masses, then the heavy elements redone in fp64 by a rolled loop
+      double m[R];
+      uint32_t heavy = 0;
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        float big;
+        m[i] = (double)rr.fast(rt.at(i), rd.at(i), big);
+        if (big >= kHeavy) heavy |= 1u << i;
+      }
+      while (heavy) {
+        const int i = __builtin_ctz(heavy);
+        heavy &= heavy - 1;
+        const double ex = rr.exact(run_elem<DT, NV>(rt.w, i), run_elem<DT, NV>(rd.w, i));
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+          if (j == i) m[j] = ex;
+      }
+      const int f = block_scan_chunk<R>([&](int i) -> double { return m[i]; },
+                                        past_end ? INFINITY : u * Z - base, sh);
+      t = e0 + f;
     }
   }
-  if (from_p) t = draw_from_p<DT, VEC>(a, b, st.row, st.c, u);
-  if (lane_id() == 0) a.tokens[(size_t)b * (K + 1) + st.a] = t;
+  if (from_p) t = draw_from_p<DT, VEC>(a, b, st.row, st.c, st.kt, u, sh);
+  if (threadIdx.x == 0) a.tokens[(size_t)b * (K + 1) + st.a] = t;
 }
 
 // ------------------------------------------------------------------ launch
@@ -787,23 +912,14 @@ __global__ void __launch_bounds__(kBlock) k_draw(VerifyArgs a) {
 template <int DT, bool VEC>
 static int launch_verify_t(VerifyArgs& a, hipStream_t st) {
   const size_t lds = sizeof(int) * (3 * (size_t)a.B + 1);
-  const long tiles = (long)a.B * a.G * (2 * a.K + 1);
-  long grid = (tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-  const int resident =
-      resident_blocks(reinterpret_cast<const void*>(&k_stream_rows<DT, VEC>), kBlock, lds);
-  if (grid > resident) grid = resident;
-  if (grid < 1) grid = 1;
-  hipLaunchKernelGGL((k_stream_rows<DT, VEC>), dim3((unsigned)grid), dim3(kBlock), lds, st, a);
-  const long slots = (long)a.B * 2 * (a.K + 1);
-  hipLaunchKernelGGL(k_merge, dim3((unsigned)((slots + kWavesPerBlock - 1) / kWavesPerBlock)),
-                     dim3(kBlock), 0, st, a);
-  a.groups = (pieces_per_row<DT>(a.V) + kWavesPerBlock - 1) / kWavesPerBlock;
-  hipLaunchKernelGGL((k_decide<DT, VEC>), dim3((unsigned)((long)a.B * a.groups)), dim3(kBlock), 0,
-                     st, a);
-  if (!a.greedy_only) {
-    const int gb = (a.B + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL((k_draw<DT, VEC>), dim3(gb), dim3(kBlock), 0, st, a);
-  }
+  const int grid = compute_units();
+  hipLaunchKernelGGL((k_stream_rows<DT, VEC>), dim3((unsigned)grid), dim3(kStreamBlock), lds, st,
+                     a);
+  a.groups = (a.G + kDecideWaves - 1) / kDecideWaves;
+  hipLaunchKernelGGL((k_decide<DT, VEC>), dim3((unsigned)((long)a.B * a.groups)),
+                     dim3(kDecideBlock), 0, st, a);
+  if (!a.greedy_only)
+    hipLaunchKernelGGL((k_draw<DT, VEC>), dim3((unsigned)a.B), dim3(kBlock), 0, st, a);
   return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_ERR_LAUNCH;
 }
 
