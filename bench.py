@@ -8,16 +8,26 @@ seeded synthetic inputs resident in HBM).  Six input sets (seed offsets
 256 MB last-level cache by the step before.
 
 Prints ONE JSON line on stdout.  ``value`` = sum of verified positions
-(sum_b L_b) per second of schedule + verify.  ``roofline`` reports the verify
-call against the 8 TB/s HBM peak using the algorithmic bytes
-s*V*(sum_{T>0}[(2 L_b + 1) + 2*rejected_b] + sum_{T=0}(L_b + 1)), timed with HIP
-events on the stream the kernels run on.  ``cpu_baseline`` times the CPU
+(sum_b L_b) per second of schedule + verify.  ``roofline`` reports the
+dominant kernel, the streaming pass (k_stream_rows), against the 8 TB/s HBM
+peak: its algorithmic bytes per launch, s*V*sum_b rows_b with rows_b = 2 L_b + 1
+(T > 0) or L_b + 1 (T = 0), over its average duration, timed with HIP events
+that the library records on its own stream around that launch.  ``traffic`` is
+the HBM bytes per launch that rocprofv3 counters measured for the same kernel
+(profiles/k_stream_rows_b64_k16_v151936_pmc.md), used only while the kernel
+sources still hash to the recorded value.  ``cpu_baseline`` times the CPU
 oracle on a bounded sample of the same workload.
+
+--calibrate-copy N runs, after the timed steps, a plain elementwise copy of
+N MiB (read N MiB, write N MiB) five times: the reference kernel of known size
+for the FETCH_SIZE / WRITE_SIZE counter runs.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -26,6 +36,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_stream_rows_b64_k16_v151936_pmc.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "draft_verification_dspark_amd", "csrc", f)
+                  for f in ("verify.hip", "device.hpp", "args.hpp")]
 METRIC = "verified draft positions/sec and achieved HBM GB/s vs peak (V=151936, B=64, K=16)"
 
 
@@ -34,7 +47,7 @@ def log(*a):
 
 
 def algorithmic_bytes(w, lengths, accepted, temperature) -> int:
-    """Bytes the prescribed streaming design must read for one verify call."""
+    """Bytes the whole verify call must read (streaming pass + residual rows)."""
     s = 2 if w.dtype == "bf16" else 4
     L = lengths.astype("int64")
     a = accepted.astype("int64")
@@ -42,6 +55,40 @@ def algorithmic_bytes(w, lengths, accepted, temperature) -> int:
     soft = T > 0
     rows = ((2 * L + 1) + 2 * (a < L)) * soft + (L + 1) * (~soft)
     return int(s * w.V * rows.sum())
+
+
+def stream_bytes(w, lengths, temperature) -> int:
+    """Bytes the streaming pass must read: every scheduled row once."""
+    s = 2 if w.dtype == "bf16" else 4
+    L = lengths.astype("int64")
+    soft = temperature > 0
+    rows = (2 * L + 1) * soft + (L + 1) * (~soft)
+    return int(s * w.V * rows.sum())
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per streaming launch from the committed counter summary, if
+    it was taken on the current kernel sources (else None)."""
+    try:
+        with open(PMC_SUMMARY) as f:
+            txt = f.read()
+    except OSError:
+        return None, "no counter summary"
+    m_h = re.search(r"source_sha256:\s*([0-9a-f]{64})", txt)
+    m_t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not (m_h and m_t):
+        return None, "counter summary unreadable"
+    if m_h.group(1) != kernel_source_hash():
+        return None, "kernel changed since the counters were taken"
+    return float(m_t.group(1)), "rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-kernel scaled"
 
 
 def main():
@@ -53,6 +100,7 @@ def main():
     ap.add_argument("--sets", type=int, default=6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this path runs on a "
@@ -99,12 +147,13 @@ def main():
                   accepted=o["acc"], tokens=o["tok"], p_tok=o["pt"], q_tok=o["qt"],
                   dev_status=o["st"], ws=ws_v, stream=stream)
 
-    def step_events(i, e0, e1, e2):
+    def step_events(i, e0, e1, e2, s0, s1):
         w, o = sets[i % len(sets)], outs[i % len(sets)]
         e0.record(stream)
         ds.schedule(w.conf, w.threshold, w.budget, w.min_len, lengths=o["lengths"], mask=o["mask"],
                     survival=o["surv"], dev_status=o["st"], ws=ws_s, stream=stream)
         e1.record(stream)
+        ds.dspark_set_stream_events(s0, s1)
         ds.verify(w.target, w.draft, w.drafted, o["lengths"], w.temperature, w.uniforms,
                   accepted=o["acc"], tokens=o["tok"], p_tok=o["pt"], q_tok=o["qt"],
                   dev_status=o["st"], ws=ws_v, stream=stream)
@@ -116,18 +165,24 @@ def main():
     log(f"warmup {args.warmup} steps done")
 
     # per-set positions and algorithmic bytes (outputs are deterministic per set)
-    pos, nbytes, accs = [], [], []
+    pos, nbytes, sbytes, accs = [], [], [], []
     for i in range(len(sets)):
         o, w = outs[i], sets[i]
         L = o["lengths"].cpu().numpy()
         a = o["acc"].cpu().numpy()
+        T = w.temperature.cpu().numpy()
         assert int(o["st"].item()) == 0, "device status flags set on synthetic inputs"
         pos.append(int(L.sum()))
-        nbytes.append(algorithmic_bytes(w, L, a, w.temperature.cpu().numpy()))
+        nbytes.append(algorithmic_bytes(w, L, a, T))
+        sbytes.append(stream_bytes(w, L, T))
         accs.append((a, L))
 
-    # timed region: K steps, events around each call
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # timed region: K steps; events around each call and, recorded by the
+    # library on the same stream, around each streaming launch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for e in ev:
+        for x in e[3:]:
+            x.record(stream)           # creates the HIP events the library records
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -136,17 +191,23 @@ def main():
         step_events(i, *ev[i])
     t_end.record(stream)
     torch.cuda.synchronize()
+    ds.dspark_set_stream_events(None, None)
     total_ms = t_start.elapsed_time(t_end)
     sched_ms = [e[0].elapsed_time(e[1]) for e in ev]
     ver_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    str_ms = [e[3].elapsed_time(e[4]) for e in ev]
     n_pos = sum(pos[i % len(sets)] for i in range(args.steps))
     n_bytes = sum(nbytes[i % len(sets)] for i in range(args.steps))
+    s_bytes = sum(sbytes[i % len(sets)] for i in range(args.steps))
     value = n_pos / (total_ms / 1e3)
     verify_gbs = n_bytes / (sum(ver_ms) / 1e3) / 1e9
+    stream_gbs = s_bytes / (sum(str_ms) / 1e3) / 1e9
     log(f"timed {args.steps} steps: {total_ms:.3f} ms; schedule median {np.median(sched_ms)*1e3:.1f} us, "
-        f"verify median {np.median(ver_ms)*1e3:.1f} us; verify {verify_gbs:.0f} GB/s")
+        f"verify median {np.median(ver_ms)*1e3:.1f} us ({verify_gbs:.0f} GB/s); streaming pass median "
+        f"{np.median(str_ms)*1e3:.1f} us ({stream_gbs:.0f} GB/s)")
     mean_acc = float(np.mean([a.mean() for a, _ in accs]))
     waste = float(np.mean([1 - a.sum() / max(1, L.sum()) for a, L in accs]))
+    traffic, traffic_note = measured_traffic()
 
     result = {
         "metric": METRIC,
@@ -167,21 +228,37 @@ def main():
             "input_sets": len(sets),
             "positions_per_step": pos,
             "verify_bytes_per_call": nbytes,
+            "stream_bytes_per_call": sbytes,
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "dspark_verify (k_stream_rows, k_decide, k_draw launches)",
-            "achieved": round(verify_gbs, 1),
+            "kernel": "k_stream_rows (streaming pass of dspark_verify)",
+            "achieved": round(stream_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(verify_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "frac": round(stream_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None if traffic is None else round(traffic),
+            "traffic_note": traffic_note,
+            "algorithmic_bytes_per_launch": round(s_bytes / args.steps),
+            "launch_us_mean": round(float(np.mean(str_ms)) * 1e3, 2),
+            "verify_call_gbs": round(verify_gbs, 1),
             "verify_us_median": round(float(np.median(ver_ms)) * 1e3, 2),
             "schedule_us_median": round(float(np.median(sched_ms)) * 1e3, 2),
         },
         "accepted_mean": round(mean_acc, 3),
         "waste_ratio": round(waste, 4),
     }
+
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.rand(n, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            torch.add(src, 0.0, out=dst)   # reads and writes n*4 bytes
+        torch.cuda.synchronize()
+        log(f"calibration copy: 5 x {args.calibrate_copy} MiB read + written")
+        del src, dst
 
     if not args.no_cpu_baseline:
         import oracle

@@ -31,7 +31,7 @@ DEV_BAD_CONF = 16
 DEV_BAD_LENGTH = 32
 
 EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_schedule",
-           "dspark_verify", "dspark_verify_greedy")
+           "dspark_verify", "dspark_verify_greedy", "dspark_set_stream_events")
 
 
 class DsparkError(RuntimeError):
@@ -63,6 +63,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dspark_verify.restype = i32
     lib.dspark_verify_greedy.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.dspark_verify_greedy.restype = i32
+    lib.dspark_set_stream_events.argtypes = [vp, vp]
+    lib.dspark_set_stream_events.restype = i32
     _lib = lib
     return lib
 
@@ -73,6 +75,20 @@ def dspark_status_string(status: int) -> str:
 
 def dspark_workspace_bytes(op: int, B: int, K: int, V: int) -> int:
     return int(load_library().dspark_workspace_bytes(int(op), int(B), int(K), int(V)))
+
+
+def dspark_set_stream_events(before, after) -> None:
+    """Record ``before`` / ``after`` (``torch.cuda.Event`` objects that have
+    been recorded once, so that they exist, or raw hipEvent_t handles) around
+    the streaming pass of every following verify call; ``None`` turns it off."""
+    def handle(e):
+        if e is None:
+            return None
+        h = getattr(e, "cuda_event", e)
+        if not h:
+            raise ValueError("event has no HIP handle yet: record it once first")
+        return h
+    _check(load_library().dspark_set_stream_events(handle(before), handle(after)))
 
 
 def _check(status: int):

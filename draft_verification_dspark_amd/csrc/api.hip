@@ -45,6 +45,9 @@ ScheduleLayout schedule_layout(int B, int K) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// events of dspark_set_stream_events (both NULL = off)
+hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
+
 }  // namespace
 
 // Compute units of the current device (cached per device; 256 if the query
@@ -166,7 +169,9 @@ static int verify_common(const void* target, const void* draft, int dtype, int B
     sub.tokens = tokens + (size_t)b0 * (K + 1);
     sub.p_tok = a.p_tok ? a.p_tok + (size_t)b0 * K : nullptr;
     sub.q_tok = a.q_tok ? a.q_tok + (size_t)b0 * K : nullptr;
-    const int st = launch_verify(sub, dtype, static_cast<hipStream_t>(stream));
+    const bool first = b0 == 0;
+    const int st = launch_verify(sub, dtype, static_cast<hipStream_t>(stream),
+                                 first ? g_ev_before : nullptr, first ? g_ev_after : nullptr);
     if (st != DSPARK_OK) return st;
   }
   return DSPARK_OK;
@@ -189,6 +194,16 @@ int dspark_verify_greedy(const void* target_logits, int dtype, int B, int K, int
   return verify_common(target_logits, nullptr, dtype, B, K, V, drafted, lengths, nullptr, nullptr,
                        accepted, tokens, nullptr, nullptr, dev_status, workspace, ws_bytes, stream,
                        1);
+}
+
+int dspark_set_stream_events(void* before, void* after) {
+  if (before && after) {
+    g_ev_before = static_cast<hipEvent_t>(before);
+    g_ev_after = static_cast<hipEvent_t>(after);
+  } else {
+    g_ev_before = g_ev_after = nullptr;
+  }
+  return DSPARK_OK;
 }
 
 }  // extern "C"

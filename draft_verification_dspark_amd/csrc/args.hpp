@@ -42,7 +42,9 @@ struct VerifyArgs {
   int vec_ok;
 };
 
-int launch_verify(VerifyArgs& a, int dtype, hipStream_t st);
+// ev_before / ev_after: optional events recorded around the streaming pass
+int launch_verify(VerifyArgs& a, int dtype, hipStream_t st, hipEvent_t ev_before,
+                  hipEvent_t ev_after);
 int compute_units();  // of the current device
 
 // Requests per launch sequence of dspark_verify (the streaming kernel keeps

@@ -14,27 +14,29 @@
 //
 // Three launches on the caller's stream, shapes fixed by (B, K, V); kernel
 // boundaries are the only cross-workgroup synchronisation:
-//   k_stream_rows  the streaming pass.  Every workgroup first lays out the
-//                  scheduled rows of all requests (target rows 0..L, draft
-//                  rows 0..L-1, or target rows only for greedy requests) as a
-//                  dense list of 4096-token tiles in LDS; waves then walk the
-//                  list with a stride, double-buffering the 16-byte loads of
-//                  the next tile while summarising the current one: an integer
-//                  exponent shift k = ceil(max * c) and the sum of 2^(x*c - k)
-//                  (fp32 terms, fp64 accumulation), or (max, lowest index).
+//   k_stream_rows  the streaming pass, one workgroup per compute unit.  Each
+//                  workgroup lays out the scheduled rows of all requests
+//                  (target rows 0..L, draft rows 0..L-1, or target rows only
+//                  for greedy requests) as a dense list of 4096-token tiles in
+//                  LDS and owns a contiguous range of it; its waves take tiles
+//                  through an LDS counter, double-buffering the 16-byte loads
+//                  of the next tile while summarising the current one: an
+//                  integer exponent shift k = ceil(max * c) and the sum of
+//                  2^(x*c - k) (fp32 terms, fp64 accumulation), or (max,
+//                  lowest index).
 //   k_decide       `groups` workgroups per request: each merges the request's
-//                  row summaries (shifts align by exact powers of two), forms
-//                  p(y), q(y), alpha, the accept ballot and the first
-//                  rejection; workgroup 0 writes the outputs; on a
-//                  rejection every workgroup sums the
-//                  residual mass of its 2048-token pieces of the rejected row
-//                  pair (fp32, elements with normalised mass >= 2^-12 in fp64).
-//   k_draw         one wave per request: the bonus token (from the pass-1
-//                  chunk summaries of target row L) or the correction token
-//                  (from the residual pieces); locates the chunk or piece
-//                  holding the draw, re-reads it with each lane holding a
-//                  contiguous run of tokens, and finds the token with one wave
-//                  scan plus a sequential scan inside the crossing lane.
+//                  row summaries (shifts align by exact powers of two), and
+//                  wave 0 forms p(y), q(y), alpha, the accept ballot and the
+//                  first rejection; workgroup 0 writes the outputs and the
+//                  draw state; on a rejection every wave sums the residual
+//                  mass of one 4096-token chunk of the rejected row pair
+//                  (fp32, elements with normalised mass >= 2^-12 in fp64).
+//   k_draw         one workgroup per request with a pending draw: the bonus
+//                  token (from the pass-1 chunk sums of target row L) or the
+//                  correction token (from the residual chunk masses); a block
+//                  scan locates the chunk holding the draw, the chunk is
+//                  re-read with each thread owning a contiguous run of
+//                  tokens, and a second block scan finds the token.
 #include <hip/hip_runtime.h>
 
 #include "args.hpp"
@@ -910,11 +912,13 @@ __global__ void __launch_bounds__(kBlock) k_draw(VerifyArgs a) {
 // ------------------------------------------------------------------ launch
 
 template <int DT, bool VEC>
-static int launch_verify_t(VerifyArgs& a, hipStream_t st) {
+static int launch_verify_t(VerifyArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   const size_t lds = sizeof(int) * (3 * (size_t)a.B + 1);
   const int grid = compute_units();
+  if (ev0 && ev1 && hipEventRecord(ev0, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
   hipLaunchKernelGGL((k_stream_rows<DT, VEC>), dim3((unsigned)grid), dim3(kStreamBlock), lds, st,
                      a);
+  if (ev0 && ev1 && hipEventRecord(ev1, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
   a.groups = (a.G + kDecideWaves - 1) / kDecideWaves;
   hipLaunchKernelGGL((k_decide<DT, VEC>), dim3((unsigned)((long)a.B * a.groups)),
                      dim3(kDecideBlock), 0, st, a);
@@ -923,12 +927,12 @@ static int launch_verify_t(VerifyArgs& a, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_ERR_LAUNCH;
 }
 
-int launch_verify(VerifyArgs& a, int dtype, hipStream_t st) {
+int launch_verify(VerifyArgs& a, int dtype, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   if (dtype == DSPARK_BF16)
-    return a.vec_ok ? launch_verify_t<DSPARK_BF16, true>(a, st)
-                    : launch_verify_t<DSPARK_BF16, false>(a, st);
-  return a.vec_ok ? launch_verify_t<DSPARK_F32, true>(a, st)
-                  : launch_verify_t<DSPARK_F32, false>(a, st);
+    return a.vec_ok ? launch_verify_t<DSPARK_BF16, true>(a, st, ev0, ev1)
+                    : launch_verify_t<DSPARK_BF16, false>(a, st, ev0, ev1);
+  return a.vec_ok ? launch_verify_t<DSPARK_F32, true>(a, st, ev0, ev1)
+                  : launch_verify_t<DSPARK_F32, false>(a, st, ev0, ev1);
 }
 
 }  // namespace dspark

@@ -186,6 +186,23 @@ DSPARK_API int dspark_verify_greedy(const void* target_logits, int dtype, int B,
                          int32_t* tokens, int32_t* dev_status, void* workspace, size_t ws_bytes,
                          void* stream);
 
+/*
+ * dspark_set_stream_events — timing hook for the streaming pass (measurement
+ * support; the pages define no such call).
+ *
+ * When `before` and `after` (hipEvent_t handles passed as void*, created by
+ * the caller) are both non-NULL, every following dspark_verify and
+ * dspark_verify_greedy call records `before` on its stream immediately before
+ * it launches its streaming pass (the kernel that reads each scheduled logits
+ * row once) and `after` immediately after that launch, so that
+ * hipEventElapsedTime(before, after) is the streaming pass alone. With
+ * several sub-batches (B > 2048) the events bracket the first sub-batch's
+ * pass. Passing NULL for either turns the hook off. The setting is
+ * process-wide and unsynchronised: set it from the thread that issues the
+ * calls, and keep the events alive while it is set. Returns DSPARK_OK.
+ */
+DSPARK_API int dspark_set_stream_events(void* before, void* after);
+
 #ifdef __cplusplus
 }
 #endif

@@ -96,3 +96,11 @@ def test_binding_refuses_without_library(tmp_path):
             mod.load_library(str(tmp_path / "missing.so"))
     finally:
         mod._lib = saved
+
+
+def test_stream_events_hook_off_without_gpu():
+    # NULL handles switch the hook off; no HIP call is made
+    lib = ds.load_library()
+    assert lib.dspark_set_stream_events(None, None) == 0
+    assert lib.dspark_set_stream_events(P, None) == 0
+    ds.dspark_set_stream_events(None, None)

@@ -419,3 +419,30 @@ def test_graph_capture_replay():
         assert torch.equal(got[0], acc) and torch.equal(got[1], tok) and torch.equal(got[2], pt)
         assert torch.equal(got[3], lengths)
         assert int(st.item()) == 0
+
+
+# ---------------------------------------------------------------- timing hook
+
+def test_stream_events_bracket_the_streaming_pass():
+    w = workloads.make(3, device=DEV)
+    lengths, _, _, _ = _sched(w)
+    stream = torch.cuda.current_stream()
+    e0, e1, c0, c1 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+    for e in (e0, e1):
+        e.record(stream)               # creates the HIP events
+    ds.dspark_set_stream_events(e0, e1)
+    try:
+        c0.record(stream)
+        out = ds.verify(w.target, w.draft, w.drafted, lengths, w.temperature, w.uniforms)
+        c1.record(stream)
+        torch.cuda.synchronize()
+    finally:
+        ds.dspark_set_stream_events(None, None)
+    t_pass, t_call = e0.elapsed_time(e1), c0.elapsed_time(c1)
+    print(f"streaming pass {t_pass * 1e3:.1f} us of verify {t_call * 1e3:.1f} us", flush=True)
+    assert 0.0 < t_pass < t_call
+    # the hook changes no result
+    ref = ds.verify(w.target, w.draft, w.drafted, lengths, w.temperature, w.uniforms)
+    torch.cuda.synchronize()
+    for k in ("accepted", "tokens", "p_tok", "q_tok"):
+        assert torch.equal(out[k], ref[k]), k
