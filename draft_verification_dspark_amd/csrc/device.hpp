@@ -78,6 +78,12 @@ struct alignas(16) ReqState {
   float kd;     // shift of the draft row
   double st;    // sum of 2^(x*c - kt) over the target row
   double sd;    // same for the draft row
+  // bonus draws located in advance: the chunk holding u * total (-1 = not
+  // located), whether rounding left no crossing, and the masses
+  int cstar;
+  int past_end;
+  double base;  // mass of the chunks before cstar
+  double total; // mass of the row (sum of its chunk masses)
 };
 
 // ---------------------------------------------------------------- wave ops
@@ -137,6 +143,16 @@ template <typename T, typename Op> __device__ __forceinline__ T wave_reduce(T v,
   return op(op(readlane(v, 0), readlane(v, 16)), op(readlane(v, 32), readlane(v, 48)));
 }
 
+// The same four DPP steps alone: every lane of each 16-lane row ends with
+// its row's result (used where a wave works on four rows at once).
+template <typename T, typename Op> __device__ __forceinline__ T row16_reduce(T v, Op op) {
+  v = op(v, dpp<kQuadXor1>(v));
+  v = op(v, dpp<kQuadXor2>(v));
+  v = op(v, dpp<kRowHalfMirror>(v));
+  v = op(v, dpp<kRowMirror>(v));
+  return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   return wave_reduce(v, [](float x, float y) { return fmaxf(x, y); });
 }
@@ -178,6 +194,13 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   for (int r = 16; r < kWave; r += 16) argmax_merge(bv, bi, readlane(v, r), readlane(i, r));
   v = bv;
   i = bi;
+}
+
+__device__ __forceinline__ void row16_argmax(float& v, int& i) {
+  argmax_step<kQuadXor1>(v, i);
+  argmax_step<kQuadXor2>(v, i);
+  argmax_step<kRowHalfMirror>(v, i);
+  argmax_step<kRowMirror>(v, i);
 }
 
 // inclusive prefix sum over the wave in lane order: Hillis-Steele within each
@@ -411,11 +434,12 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // 2^a in fp64 for the few elements that need it: range reduction a = n + f,
 // |f| <= 1/2, then the Taylor series of e^t, t = f ln 2, to degree 9 by
 // Horner's rule (truncation below t^10/10! < 1e-11 relative) and an exact
-// scaling by 2^n.  Arguments below -2000 (and NaN) give 0.
+// scaling by 2^n.  Arguments below -2000 (and NaN) give 0.  Branch-free, so
+// that independent calls interleave.
 __device__ __forceinline__ double exp2_f64(double a) {
-  if (!(a > -2000.0)) return 0.0;
-  const double n = rint(a);
-  const double t = (a - n) * 0.69314718055994530942;
+  const double aa = fmax(a, -2000.0);  // NaN gives -2000 here and 0 below
+  const double n = rint(aa);
+  const double t = (aa - n) * 0.69314718055994530942;
   double p = 1.0 / 362880.0;
   p = fma(p, t, 1.0 / 40320.0);
   p = fma(p, t, 1.0 / 5040.0);
@@ -426,7 +450,8 @@ __device__ __forceinline__ double exp2_f64(double a) {
   p = fma(p, t, 0.5);
   p = fma(p, t, 1.0);
   p = fma(p, t, 1.0);
-  return ldexp(p, (int)n);
+  const double r = ldexp(p, (int)n);
+  return a > -2000.0 ? r : 0.0;
 }
 
 __device__ __forceinline__ void flag(int32_t* st, int bits) {

@@ -382,6 +382,51 @@ __device__ RowSum merge_argmax(Partial first, const Partial* p, int G) {
   return r;
 }
 
+// The same merges by one 16-lane group from summaries staged in LDS: lane
+// `sub` folds chunks sub, sub + 16, ...; the group then combines its lanes.
+__device__ RowSum merge_softmax16(const Partial* p, int G, int sub) {
+  float km = -INFINITY;
+  double s = 0.0;
+  int fl = 0;
+  for (int c = sub; c < G; c += 16) {
+    const Partial q = p[c];
+    fl |= q.idx;
+    if (q.s > 0.0) {
+      if (q.k > km) {
+        s = ldexp(s, shift_amount(km - q.k));
+        km = q.k;
+      }
+      s += ldexp(q.s, shift_amount(q.k - km));
+    }
+  }
+  RowSum r;
+  r.k = row16_reduce(km, [](float x, float y) { return fmaxf(x, y); });
+  r.s = row16_reduce(km > -INFINITY ? ldexp(s, shift_amount(km - r.k)) : 0.0,
+                     [](double x, double y) { return x + y; });
+  r.idx = 0;
+  r.bad = row16_reduce(fl, [](int x, int y) { return x | y; });
+  r.pad = 0;
+  return r;
+}
+
+__device__ RowSum merge_argmax16(const Partial* p, int G, int sub) {
+  float best = -INFINITY;
+  int bi = 0x7fffffff, fl = 0;
+  for (int c = sub; c < G; c += 16) {
+    const Partial q = p[c];
+    argmax_merge(best, bi, q.k, q.idx);
+    fl |= (int)q.s;
+  }
+  row16_argmax(best, bi);
+  RowSum r;
+  r.k = best;
+  r.idx = bi == 0x7fffffff ? 0 : bi;
+  r.s = 0.0;
+  r.bad = row16_reduce(fl, [](int x, int y) { return x | y; });
+  r.pad = 0;
+  return r;
+}
+
 // probability of logit x under a merged row: 2^(x*c - K*) / S, in fp64
 __device__ __forceinline__ double row_prob(float x, float c, float kmax, double S) {
   if (!(S > 0.0)) return 0.0;
@@ -390,20 +435,22 @@ __device__ __forceinline__ double row_prob(float x, float c, float kmax, double 
 
 // Residual p - q of one row pair at fp32 speed, with the elements whose
 // normalised p or q reaches 2^-12 redone in fp64 (their fp32 rounding would
-// show after dividing by a small residual mass).
+// show after dividing by a small residual mass).  The fp32 path takes
+// 2^(x*c - K*) with the row's integer shift K* (the argument rounds once, no
+// error common to the row) times fp32(1/S).
 struct ResidualRows {
-  float c, nbt, nbd, kt, kd;
+  float c, kt, kd, rstf, rsdf;
   double rst, rsd;  // 1 / S of the target and draft rows
   __device__ ResidualRows(float c_, float kt_, double st, float kd_, double sd)
       : c(c_), kt(kt_), kd(kd_) {
     rst = 1.0 / st;
     rsd = 1.0 / sd;
-    nbt = (float)(-(double)kt - log2(st));
-    nbd = (float)(-(double)kd - log2(sd));
+    rstf = (float)rst;
+    rsdf = (float)rsd;
   }
   __device__ __forceinline__ float fast(float xt, float xd, float& big) const {
-    const float p = fast_exp2(fmaf(xt, c, nbt));
-    const float q = fast_exp2(fmaf(xd, c, nbd));
+    const float p = fast_exp2(fmaf(xt, c, -kt)) * rstf;
+    const float q = fast_exp2(fmaf(xd, c, -kd)) * rsdf;
     big = fmaxf(p, q);
     return fmaxf(p - q, 0.f);
   }
@@ -462,32 +509,62 @@ __device__ double residual_chunk_mass(const ResidualRows& rr, const char* tchunk
 #pragma unroll
   for (int v = 0; v < U; ++v) {
     float r[P];
-    float hv = 0.f;
+    uint32_t hm = 0;  // this lane's heavy elements of vector v
 #pragma unroll
     for (int e = 0; e < P; ++e) {
       float big;
       const float x = rr.fast(tt.at(v, e), td.at(v, e), big);
-      hv = fmaxf(hv, big);
-      r[e] = big >= kHeavy ? 0.f : x;
+      const bool h = big >= kHeavy;
+      hm |= h ? 1u << e : 0u;
+      r[e] = h ? 0.f : x;
     }
     const bool ok = tt.valid(v);
     float s4 = (r[0] + r[1]) + (r[2] + r[3]);
     if constexpr (P == 8) s4 += (r[4] + r[5]) + (r[6] + r[7]);
     light += ok ? s4 : 0.f;
-    if (ok && hv >= kHeavy) {
+    if (!ok) hm = 0;
+    if (hm) {
+      // each lane walks its own heavy elements (usually one)
       const uint32_t wt[4] = {tt.w[v][0], tt.w[v][1], tt.w[v][2], tt.w[v][3]};
       const uint32_t wd[4] = {td.w[v][0], td.w[v][1], td.w[v][2], td.w[v][3]};
-#pragma unroll 1
-      for (int e = 0; e < P; ++e) {
-        const float xt = vec_elem<DT>(wt, e), xd = vec_elem<DT>(wd, e);
-        float big;
-        rr.fast(xt, xd, big);
-        if (big >= kHeavy) heavy += rr.exact(xt, xd);
+      while (hm) {
+        const int e = __builtin_ctz(hm);
+        hm &= hm - 1;
+        heavy += rr.exact(vec_elem<DT>(wt, e), vec_elem<DT>(wd, e));
       }
     }
     asm volatile("" : "+v"(light), "+v"(heavy));
   }
   return wave_sum((double)light + heavy);
+}
+
+// Inverse CDF over at most 64 non-negative weights, one per lane (lanes past
+// the count hold 0), in lane order: the first lane whose running sum exceeds
+// u * total (and has weight), else the last lane with weight (`past_end`),
+// else -1.  `base` = the sum before it.  Wave-uniform results, no barrier.
+struct Located {
+  int idx;
+  int past_end;
+  double base;
+  double total;
+};
+__device__ __forceinline__ Located wave_locate(double x, double u) {
+  const double incl = wave_incl_scan(x);
+  Located r;
+  r.total = readlane(incl, kWave - 1);
+  const double target = u * r.total;
+  const uint64_t hit = __ballot(incl > target && x > 0.0);
+  const uint64_t pos = __ballot(x > 0.0);
+  if (hit) {
+    r.idx = __builtin_ctzll(hit);
+    r.past_end = 0;
+    r.base = readlane(incl - x, r.idx);
+  } else {
+    r.idx = pos ? 63 - __builtin_clzll(pos) : -1;
+    r.past_end = 1;
+    r.base = r.total;
+  }
+  return r;
 }
 
 // ------------------------------------------------------------------ decide
@@ -501,25 +578,33 @@ __device__ double residual_chunk_mass(const ResidualRows& rr, const char* tchunk
 #ifndef DSPARK_DECIDE_BLOCK
 #define DSPARK_DECIDE_BLOCK 256
 #endif
-#ifndef DSPARK_ROWS_IN_FLIGHT
-#define DSPARK_ROWS_IN_FLIGHT 4
-#endif
 constexpr int kDecideBlock = DSPARK_DECIDE_BLOCK;
 constexpr int kDecideWaves = kDecideBlock / kWave;
-constexpr int kRowsInFlight = DSPARK_ROWS_IN_FLIGHT;
 constexpr int kMaxRows = 2 * 64 + 1;
+// chunk summaries staged in LDS per round of the merges (24 KB)
+constexpr int kStage = 1536;
 
 template <int DT, bool VEC>
 __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
   constexpr int S = Elem<DT>::kBytes;
   constexpr int E = item_elems<DT>();
   __shared__ RowSum s_rows[kMaxRows + 2];  // merged rows, then the rejected pair
+  __shared__ Partial s_part[kStage];       // chunk summaries of the rows being merged
   __shared__ int s_a, s_bad;
   const int b = blockIdx.x / a.groups;
   const int g = blockIdx.x - b * a.groups;
   const int w = uniform((int)(threadIdx.x / kWave));
   const int l = lane_id();
   const int K = a.K;
+  // wave 0, lane l: position l+1's drafted id and accept uniform.  They do
+  // not depend on the length, so they are requested together with it.
+  int y = 0;
+  float u = 0.f;
+  if (w == 0 && l < K) {
+    y = a.drafted[(size_t)b * K + l];
+    if (a.uniforms) u = a.uniforms[(size_t)b * (K + 1) + l];
+  }
+  const float u_draw = a.uniforms ? a.uniforms[(size_t)b * (K + 1) + K] : 0.f;
   const ReqInfo r = req_info(a, b);
   const int L = r.L;
   int32_t* tok = a.tokens + (size_t)b * (K + 1);
@@ -542,63 +627,86 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
   }
   const bool soft = r.kind == kKindSoftmax;
 
-  // wave 0, lane l: position l+1's drafted id, its two logits and uniform,
-  // loaded now so that they arrive during the merges
-  int y = 0;
+  // the drafted tokens' logits, gathered now so that they arrive during the
+  // merges
   bool yok = true;
-  float xt = 0.f, xd = 0.f, u = 0.f;
+  float xt = 0.f, xd = 0.f;
   if (w == 0 && l < L) {
-    y = a.drafted[(size_t)b * K + l];
     yok = y >= 0 && y < a.V;
     if (yok) {
       xt = load_elem<DT>(target_row(a, b, l, S), y);
       if (soft) xd = load_elem<DT>(draft_row(a, b, l, S), y);
     }
-    if (soft) u = a.uniforms[(size_t)b * (K + 1) + l];
   }
 
-  // merges: row index q in [0, nrows): target rows 0..L, then draft rows 0..L-1
+  // Merges.  Row order q: soft requests take target rows 0..L-1 (q = j),
+  // draft rows 0..L-1 (q = L + j), then target row L (q = 2L); greedy
+  // requests target rows 0..L (q = j).  Target row L comes last so that its
+  // summaries are still staged when the bonus chunk is located.
+  const int G = a.G;
   const int nrows = soft ? 2 * L + 1 : L + 1;
-  for (int q0 = w; q0 < nrows; q0 += kDecideWaves * kRowsInFlight) {
-    Partial first[kRowsInFlight];
-    const Partial* base[kRowsInFlight];
+  const int qL = nrows - 1;
+  auto row_of = [&](int q, int& side) -> int {
+    side = (soft && q >= L && q < 2 * L) ? 1 : 0;
+    return side ? q - L : (q == qL ? L : q);
+  };
+  int q_last = 0;  // first row of the last staged round
+  if (G <= kStage) {
+    // all threads stage up to kStage summaries at once, then 16-lane groups
+    // merge one row each
+    const int per_round = kStage / G;
+    const int grp = threadIdx.x >> 4, sub = threadIdx.x & 15;
+    for (int q0 = 0; q0 < nrows; q0 += per_round) {
+      const int nr = min(per_round, nrows - q0);
+      const int cnt = nr * G;
+      q_last = q0;
+      if (q0 > 0) __syncthreads();  // the previous round's merges are done
 #pragma unroll
-    for (int i = 0; i < kRowsInFlight; ++i) {
-      const int q = q0 + i * kDecideWaves;
-      const int side = q <= L ? 0 : 1;
-      const int j = side ? q - L - 1 : q;
-      base[i] = row_parts(a, b, q < nrows ? j : 0, q < nrows ? side : 0);
-      first[i] = l < a.G ? base[i][l] : Partial{-INFINITY, 0x7fffffff, 0.0};
-    }
-#pragma unroll
-    for (int i = 0; i < kRowsInFlight; ++i) {
-      const int q = q0 + i * kDecideWaves;
-      if (q < nrows) {
-        const RowSum m = soft ? merge_softmax(first[i], base[i], a.G)
-                              : merge_argmax(first[i], base[i], a.G);
-        if (l == 0) s_rows[q] = m;
+      for (int k = 0; k < kStage / kDecideBlock; ++k) {
+        const int i = k * kDecideBlock + (int)threadIdx.x;
+        if (i < cnt) {
+          const int rr = i / G;
+          int side;
+          const int j = row_of(q0 + rr, side);
+          s_part[i] = row_parts(a, b, j, side)[i - rr * G];
+        }
       }
+      __syncthreads();
+      for (int rr = grp; rr < nr; rr += kDecideBlock / 16) {
+        const RowSum m = soft ? merge_softmax16(s_part + rr * G, G, sub)
+                              : merge_argmax16(s_part + rr * G, G, sub);
+        if (sub == 0) s_rows[q0 + rr] = m;
+      }
+    }
+  } else {
+    // very long rows: waves merge whole rows straight from global memory
+    for (int q = w; q < nrows; q += kDecideWaves) {
+      int side;
+      const int j = row_of(q, side);
+      const Partial* base = row_parts(a, b, j, side);
+      const Partial first = l < G ? base[l] : Partial{-INFINITY, 0x7fffffff, 0.0};
+      const RowSum m = soft ? merge_softmax(first, base, G) : merge_argmax(first, base, G);
+      if (l == 0) s_rows[q] = m;
     }
   }
   __syncthreads();
 
   if (w == 0) {
-    int bad = r.bad;
+    const RowSum rL = s_rows[qL];  // target row L: the bonus row
     RowSum rt{}, rd{};
-    if (l <= L) rt = s_rows[l];
-    if (soft && l < L) rd = s_rows[L + 1 + l];
-    RowSum r64{};
-    if (L == 64) r64 = s_rows[64];  // the row past lane 63
+    if (l < L) {
+      rt = s_rows[l];
+      if (soft) rd = s_rows[L + l];
+    }
+    int bad = r.bad;
     if (!yok) bad |= DSPARK_DEV_BAD_TOKEN;
-    if (l <= L) bad |= rt.bad;
-    if (l < L) bad |= rd.bad;
-    if (L == 64 && l == 0) bad |= r64.bad;
+    if (l < L) bad |= rt.bad | rd.bad;
+    if (l == 0) bad |= rL.bad;
     bool acc = false;
     float pf = 0.f, qf = 0.f;
     if (soft) {
-      if (l <= L && !(rt.s > 0.0)) bad |= DSPARK_DEV_NONFINITE;  // no finite logit
       if (l < L) {
-        if (!(rd.s > 0.0)) bad |= DSPARK_DEV_NONFINITE;
+        if (!(rt.s > 0.0) || !(rd.s > 0.0)) bad |= DSPARK_DEV_NONFINITE;  // no finite logit
         if (!(u >= 0.f && u < 1.f)) bad |= DSPARK_DEV_BAD_UNIFORM;
         if (yok) {
           const double p = row_prob(xt, r.c, rt.k, rt.s);
@@ -610,13 +718,12 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
         }
       }
       if (l == 0) {
-        if (L == 64 && !(r64.s > 0.0)) bad |= DSPARK_DEV_NONFINITE;
-        const float uf = a.uniforms[(size_t)b * (K + 1) + K];
-        if (!(uf >= 0.f && uf < 1.f)) bad |= DSPARK_DEV_BAD_UNIFORM;
+        if (!(rL.s > 0.0)) bad |= DSPARK_DEV_NONFINITE;
+        if (!(u_draw >= 0.f && u_draw < 1.f)) bad |= DSPARK_DEV_BAD_UNIFORM;
       }
     } else {
-      if (l <= L && rt.k == -INFINITY) bad |= DSPARK_DEV_NONFINITE;  // no finite logit
-      if (l == 0 && L == 64 && r64.k == -INFINITY) bad |= DSPARK_DEV_NONFINITE;
+      if (l < L && rt.k == -INFINITY) bad |= DSPARK_DEV_NONFINITE;  // no finite logit
+      if (l == 0 && rL.k == -INFINITY) bad |= DSPARK_DEV_NONFINITE;
       acc = l < L && yok && y == rt.idx;
     }
     const uint64_t m = __ballot(acc);
@@ -626,7 +733,7 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
     bad = wave_or(bad);
     if (lead) {
       int gtok = 0;
-      if (!soft) gtok = an < 64 ? readlane(rt.idx, an) : readlane(r64.idx, 0);
+      if (!soft) gtok = an < L ? readlane(rt.idx, an) : rL.idx;
       if (l < K) {
         if (a.p_tok) a.p_tok[(size_t)b * K + l] = pf;
         if (a.q_tok) a.q_tok[(size_t)b * K + l] = qf;
@@ -637,8 +744,17 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
       }
       // draw state: the target row of the draw and, on a rejection, the
       // draft row's shift and sum as well
-      const RowSum dt = an < 64 ? RowSum{readlane(rt.s, an), readlane(rt.k, an), 0, 0, 0} : r64;
+      const RowSum dt = an < L ? RowSum{readlane(rt.s, an), readlane(rt.k, an), 0, 0, 0} : rL;
       const RowSum dd = an < L ? RowSum{readlane(rd.s, an), readlane(rd.k, an), 0, 0, 0} : RowSum{};
+      // the bonus draw's chunk, located now from the staged summaries of
+      // target row L (the last row staged)
+      Located bonus{-1, 0, 0.0, 0.0};
+      const bool located = soft && an == L && G <= kWave && G <= kStage;
+      if (located) {
+        const Partial pc = l < G ? s_part[(qL - q_last) * G + l] : Partial{-INFINITY, 0, 0.0};
+        const double mass = l < G && pc.s > 0.0 ? ldexp(pc.s, shift_amount(pc.k - rL.k)) : 0.0;
+        bonus = wave_locate(mass, (double)u_draw);
+      }
       if (l == 0) {
         a.accepted[b] = an;
         if (bad) flag(a.dev_status, bad);
@@ -653,6 +769,10 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
         st.st = dt.s;
         st.kd = dd.k;
         st.sd = dd.s;
+        st.cstar = bonus.idx;
+        st.past_end = bonus.past_end;
+        st.base = bonus.base;
+        st.total = bonus.total;
         a.req[b] = st;
       }
     }
@@ -685,171 +805,165 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
 
 // ------------------------------------------------------------------ draw
 
-// Block-wide helpers for kBlock threads (4 waves); every thread must call
-// them (they synchronise).
-__device__ __forceinline__ double block_sum(double x, double* s_w) {
-  const double t = wave_sum(x);
-  const int w = threadIdx.x / kWave;
-  if (lane_id() == 0) s_w[w] = t;
-  __syncthreads();
-  double s = 0.0;
-#pragma unroll
-  for (int i = 0; i < kWavesPerBlock; ++i) s += s_w[i];
-  __syncthreads();
-  return s;
-}
-
-// Inclusive scan over the block in thread order; also the block total.
-__device__ __forceinline__ double block_incl_scan(double x, double* s_w, double& total) {
-  const double incl = wave_incl_scan(x);
-  const int w = threadIdx.x / kWave;
-  if (lane_id() == kWave - 1) s_w[w] = incl;
-  __syncthreads();
-  double pre = 0.0, tot = 0.0;
-#pragma unroll
-  for (int i = 0; i < kWavesPerBlock; ++i) {
-    const double v = s_w[i];
-    if (i < w) pre += v;
-    tot += v;
-  }
-  __syncthreads();
-  total = tot;
-  return pre + incl;
-}
-
-// lowest thread of the block with `pred` (kBlock if none)
-__device__ __forceinline__ int block_first(bool pred, int* s_i) {
-  const uint64_t bal = __ballot(pred);
-  const int w = threadIdx.x / kWave;
-  if (lane_id() == 0) s_i[w] = bal ? w * kWave + __builtin_ctzll(bal) : kBlock;
-  __syncthreads();
-  int f = kBlock;
-#pragma unroll
-  for (int i = 0; i < kWavesPerBlock; ++i) f = min(f, s_i[i]);
-  __syncthreads();
-  return f;
-}
-
-__device__ __forceinline__ int block_max_i(int x, int* s_i) {
-  const int m = wave_max_i(x);
-  const int w = threadIdx.x / kWave;
-  if (lane_id() == 0) s_i[w] = m;
-  __syncthreads();
-  int f = INT_MIN;
-#pragma unroll
-  for (int i = 0; i < kWavesPerBlock; ++i) f = max(f, s_i[i]);
-  __syncthreads();
-  return f;
-}
-
 struct DrawShared {
   double w[kWavesPerBlock];
   int i[kWavesPerBlock];
-  double base;
-  int found;
+  double base, total;
+  int idx, past_end, found;
 };
 
-// Inverse CDF over n non-negative weights f(0..n-1), in index order: the first
-// index whose running sum exceeds u * total (and has weight), else the last
-// index with weight (`past_end`), else -1.  `base` = the sum before it.
+// Inverse CDF over n > 64 weights f(0..n-1) for the whole block, in index
+// order (same rule as wave_locate), in rounds of kBlock weights.  Every
+// thread must call it.
 template <typename F>
-__device__ int block_locate(F f, int n, double u, double& total, double& base, bool& past_end,
-                            DrawShared& sh) {
-  const int tid = threadIdx.x;
-  const double x0 = tid < n ? f(tid) : 0.0;
-  double part = x0;
-  for (int i = tid + kBlock; i < n; i += kBlock) part += f(i);
-  total = block_sum(part, sh.w);
+__device__ Located block_locate(F f, int n, double u, DrawShared& sh) {
+  const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
+  double part = 0.0;
+  for (int i = tid; i < n; i += kBlock) part += f(i);
+  const double pw = wave_sum(part);
+  if (l == 0) sh.w[w] = pw;
+  __syncthreads();
+  double total = 0.0;
+#pragma unroll
+  for (int k = 0; k < kWavesPerBlock; ++k) total += sh.w[k];
+  __syncthreads();
   const double target = u * total;
   double run = 0.0;
   int last = -1;
   for (int r0 = 0; r0 < n; r0 += kBlock) {
     const int i = r0 + tid;
-    const double x = r0 == 0 ? x0 : (i < n ? f(i) : 0.0);
-    double rtot;
-    const double incl = block_incl_scan(x, sh.w, rtot);
-    const int hit = block_first(run + incl > target && x > 0.0, sh.i);
-    last = max(last, block_max_i(x > 0.0 ? i : -1, sh.i));
-    if (hit < kBlock) {
-      if (tid == hit) sh.base = run + (incl - x);
-      __syncthreads();
-      base = sh.base;
-      past_end = false;
-      return r0 + hit;
+    const double x = i < n ? f(i) : 0.0;
+    const double incl_w = wave_incl_scan(x);
+    const int lpw = wave_max_i(x > 0.0 ? i : -1);
+    if (l == kWave - 1) {
+      sh.w[w] = incl_w;
+      sh.i[w] = lpw;
     }
-    run += rtot;
+    __syncthreads();
+    double pre = run, cum = run;
+    int ws = -1;
+#pragma unroll
+    for (int k = 0; k < kWavesPerBlock; ++k) {
+      const double t = sh.w[k];
+      if (k < w) pre += t;
+      cum += t;
+      if (ws < 0 && cum > target && t > 0.0) ws = k;
+      last = max(last, sh.i[k]);
+    }
+    if (w == ws) {
+      const double incl = pre + incl_w;
+      const uint64_t hit = __ballot(incl > target && x > 0.0);
+      const int hl = hit ? __builtin_ctzll(hit) : 0;
+      const double before = readlane(incl - x, hl);
+      if (l == 0) {
+        sh.idx = hit ? r0 + w * kWave + hl : lpw;
+        sh.base = hit ? before : cum;
+      }
+    }
+    __syncthreads();
+    if (ws >= 0) {
+      Located r;
+      r.idx = sh.idx;
+      r.past_end = 0;
+      r.base = sh.base;
+      r.total = total;
+      return r;
+    }
+    run = cum;
   }
-  base = run;
-  past_end = true;
-  return last;
+  Located r;
+  r.idx = last;
+  r.past_end = 1;
+  r.base = total;
+  r.total = total;
+  return r;
 }
 
-// Inside one chunk (n elements, R per thread in a contiguous run), the first
-// element whose running mass exceeds `target`, else the last with mass, else
-// 0.  mass(i) gives this thread's element i (0..R-1) as a double.
-template <int R, typename M>
-__device__ int block_scan_chunk(M mass, double target, DrawShared& sh) {
-  const int tid = threadIdx.x;
-  double m[R];
+// Inside one chunk whose elements are split into contiguous runs of R per
+// thread (masses m), the first element whose running mass exceeds `target`,
+// else the last element with mass, else 0.  Two barriers: wave totals, then
+// the crossing thread's answer.
+template <int R>
+__device__ int block_scan_run(const double (&m)[R], double target, DrawShared& sh) {
+  const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
   double ls = 0.0;
   int lp = -1;
 #pragma unroll
   for (int i = 0; i < R; ++i) {
-    m[i] = mass(i);
     ls += m[i];
     if (m[i] > 0.0) lp = tid * R + i;
   }
-  double tot;
-  const double incl = block_incl_scan(ls, sh.w, tot);
-  const int x = block_first(incl > target && ls > 0.0, sh.i);
-  if (x < kBlock) {
-    if (tid == x) {
+  const double incl_w = wave_incl_scan(ls);
+  const int lpw = wave_max_i(lp);
+  if (l == kWave - 1) {
+    sh.w[w] = incl_w;
+    sh.i[w] = lpw;
+  }
+  __syncthreads();
+  double pre = 0.0, cum = 0.0;
+  int ws = -1, last = -1;
+#pragma unroll
+  for (int i = 0; i < kWavesPerBlock; ++i) {
+    const double t = sh.w[i];
+    if (i < w) pre += t;
+    cum += t;
+    if (ws < 0 && cum > target && t > 0.0) ws = i;
+    last = max(last, sh.i[i]);
+  }
+  if (w == ws) {
+    const double incl = pre + incl_w;
+    const uint64_t hit = __ballot(incl > target && ls > 0.0);
+    if (!hit) {
+      if (l == 0) sh.found = lpw;  // rounding left no crossing lane
+    } else if (l == __builtin_ctzll(hit)) {
       double run = incl - ls;
-      int found = -1;
+      int f = -1;
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         run += m[i];
-        if (found < 0 && run > target && m[i] > 0.0) found = tid * R + i;
+        if (f < 0 && run > target && m[i] > 0.0) f = tid * R + i;
       }
-      sh.found = found >= 0 ? found : lp;
+      sh.found = f >= 0 ? f : lp;
     }
-    __syncthreads();
-    return sh.found;
   }
-  const int f = block_max_i(lp, sh.i);
+  __syncthreads();
+  const int f = ws >= 0 ? sh.found : last;
   return f >= 0 ? f : 0;
 }
 
 // Draw from the softmax of target row `row` (bonus token, or the fallback of
 // an all-zero residual): chunk masses come from the row's pass-1 summaries
-// scaled to the merged shift kp; the chosen chunk is recomputed with the same
-// fp32 arithmetic as pass 1.
+// scaled to the merged shift kp (the chunk may already be located); the
+// chosen chunk is recomputed with the same fp32 arithmetic as pass 1.
 template <int DT, bool VEC>
 __device__ int draw_from_p(const VerifyArgs& a, int b, int row, float c, float kp, double u,
-                           DrawShared& sh) {
+                           Located loc, DrawShared& sh) {
   constexpr int S = Elem<DT>::kBytes;
   constexpr int E = item_elems<DT>();
   constexpr int R = E / kBlock;
   constexpr int NV = R / Elem<DT>::kPerVec;
   const Partial* pr = row_parts(a, b, row, 0);
-  double total, base;
-  bool past_end;
-  const int cstar = block_locate(
-      [&](int ci) -> double {
-        const Partial p = pr[ci];
-        return p.s > 0.0 ? ldexp(p.s, shift_amount(p.k - kp)) : 0.0;
-      },
-      a.G, u, total, base, past_end, sh);
-  if (cstar < 0) return 0;
-  const int e0 = cstar * E;
+  auto chunk_mass = [&](int ci) -> double {
+    const Partial p = pr[ci];
+    return p.s > 0.0 ? ldexp(p.s, shift_amount(p.k - kp)) : 0.0;
+  };
+  if (loc.idx < 0) {
+    if (a.G <= kWave)
+      loc = wave_locate(lane_id() < a.G ? chunk_mass(lane_id()) : 0.0, u);
+    else
+      loc = block_locate(chunk_mass, a.G, u, sh);
+  }
+  if (loc.idx < 0) return 0;
+  const int e0 = loc.idx * E;
   const int n = min(E, a.V - e0);
   LaneRun<DT, NV> run;
   run.template load<VEC>(target_row(a, b, row, S) + (size_t)e0 * S, n, threadIdx.x);
-  const float kc = pr[cstar].k;
+  const float kc = pr[loc.idx].k;
   const int sh_c = shift_amount(kc - kp);
-  const int f = block_scan_chunk<R>(
-      [&](int i) -> double { return ldexp((double)fast_exp2(fmaf(run.at(i), c, -kc)), sh_c); },
-      past_end ? INFINITY : u * total - base, sh);
+  double m[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) m[i] = ldexp((double)fast_exp2(fmaf(run.at(i), c, -kc)), sh_c);
+  const int f = block_scan_run<R>(m, loc.past_end ? INFINITY : u * loc.total - loc.base, sh);
   return e0 + f;
 }
 
@@ -862,23 +976,27 @@ __global__ void __launch_bounds__(kBlock) k_draw(VerifyArgs a) {
   constexpr int NV = R / Elem<DT>::kPerVec;
   __shared__ DrawShared sh;
   const int b = blockIdx.x;
-  const ReqState st = a.req[b];
-  if (st.mode != kModeResidual && st.mode != kModeBonus) return;
   const int K = a.K;
+  const int l = lane_id();
+  // requested together: the draw state, the final uniform and this
+  // request's residual chunk masses (used only after a rejection)
+  const ReqState st = a.req[b];
   const double u = (double)a.uniforms[(size_t)b * (K + 1) + K];
+  const double* z = a.part2 + (size_t)b * a.G;
+  double zl = l < a.G ? z[l] : 0.0;
+  asm volatile("" : "+v"(zl));
+  if (st.mode != kModeResidual && st.mode != kModeBonus) return;
   int t = 0;
   bool from_p = st.mode == kModeBonus;
   if (!from_p) {
-    const double* z = a.part2 + (size_t)b * a.G;
-    double Z, base;
-    bool past_end;
-    const int pstar = block_locate([&](int ci) -> double { return z[ci]; }, a.G, u, Z, base,
-                                   past_end, sh);
-    if (!(Z > 0.0) || pstar < 0) {
+    const Located loc = a.G <= kWave ? wave_locate(zl, u)
+                                     : block_locate([&](int ci) -> double { return z[ci]; },
+                                                    a.G, u, sh);
+    if (!(loc.total > 0.0) || loc.idx < 0) {
       from_p = true;  // no residual mass: draw from p at the rejected position
     } else {
       const ResidualRows rr(st.c, st.kt, st.st, st.kd, st.sd);
-      const int e0 = pstar * E;
+      const int e0 = loc.idx * E;
       const int n = min(E, a.V - e0);
       LaneRun<DT, NV> rt, rd;
       rt.template load<VEC>(target_row(a, b, st.row, S) + (size_t)e0 * S, n, threadIdx.x);
@@ -900,12 +1018,20 @@ __global__ void __launch_bounds__(kBlock) k_draw(VerifyArgs a) {
         for (int j = 0; j < R; ++j)
           if (j == i) m[j] = ex;
       }
-      const int f = block_scan_chunk<R>([&](int i) -> double { return m[i]; },
-                                        past_end ? INFINITY : u * Z - base, sh);
+      const int f = block_scan_run<R>(m, loc.past_end ? INFINITY : u * loc.total - loc.base, sh);
       t = e0 + f;
     }
   }
-  if (from_p) t = draw_from_p<DT, VEC>(a, b, st.row, st.c, st.kt, u, sh);
+  if (from_p) {
+    Located loc{-1, 0, 0.0, 0.0};
+    if (st.mode == kModeBonus && st.cstar >= 0) {
+      loc.idx = st.cstar;
+      loc.past_end = st.past_end;
+      loc.base = st.base;
+      loc.total = st.total;
+    }
+    t = draw_from_p<DT, VEC>(a, b, st.row, st.c, st.kt, u, loc, sh);
+  }
   if (threadIdx.x == 0) a.tokens[(size_t)b * (K + 1) + st.a] = t;
 }
 

@@ -164,6 +164,18 @@ def test_max_k_and_full_length():
     assert np.array_equal(host(og["tokens"])[:, K], host(am)[:, K])
 
 
+@pytest.mark.parametrize("dtype,V", [("f32", 151936), ("bf16", 300000)])
+def test_more_than_64_chunks_per_row(dtype, V):
+    # rows of more than 64 summaries: the block-wide chunk search of the draws
+    # and the multi-chunk merges; full lengths with q == p give bonus draws,
+    # noisy drafts give residual draws
+    B, K = 4, 3
+    tgt, dft, drafted, L, temp, u = _rand_case(B, K, V, dtype, seed=V % 97, lengths="full", T=1.0)
+    g, _ = _verify_and_compare(tgt, tgt[:, :K].contiguous(), drafted, L, temp, u)
+    assert (g["accepted"] == K).all()
+    _verify_and_compare(tgt, dft, drafted, L, temp, u)
+
+
 def test_batch_larger_than_one_launch():
     # more requests than one launch sequence handles: consecutive sub-batches
     B, K, V = 4500, 3, 520
