@@ -181,11 +181,18 @@ struct TileRef {
 constexpr int kStreamBlock = DSPARK_STREAM_BLOCK;
 constexpr int kStreamWaves = kStreamBlock / kWave;
 
-// Per-workgroup plan in LDS: start[b] = index of request b's first tile,
-// start[B] = total; info[b] = L | kind << 8; cval[b] = log2(e) / T.  Request
-// b's tiles are its rows (target 0..L, then draft 0..L-1) times G chunks,
-// row-major.
-__device__ void build_plan(const VerifyArgs& a, int* start, int* info, float* cval) {
+// The tile list.  Tiles [0, B*G) are target row 0 of every request (chunk c of
+// request b is tile b*G + c): that row is read whatever the length, so these
+// tiles are known before the plan exists.  The rest follow request by
+// request: target rows 1..L and draft rows 0..L-1 of a sampled request,
+// target rows 1..L of a greedy one, nothing for a skipped one, each row as G
+// chunks in order.
+//
+// Per-workgroup plan in LDS: start[b] = index of request b's first tile after
+// row 0, start[B] = total; info[b] = L | kind << 8; cval[b] = log2(e) / T.
+// With `has_pre`, `pre` is this thread's request (one request per thread).
+__device__ __forceinline__ void build_plan(const VerifyArgs& a, int* start, int* info,
+                                           float* cval, bool has_pre, ReqInfo pre) {
   __shared__ int wsum[kStreamWaves];
   const int tid = threadIdx.x;
   const int per = (a.B + kStreamBlock - 1) / kStreamBlock;
@@ -194,8 +201,8 @@ __device__ void build_plan(const VerifyArgs& a, int* start, int* info, float* cv
   for (int i = 0; i < per; ++i) {
     const int b = b0 + i;
     if (b < a.B) {
-      const ReqInfo r = req_info(a, b);
-      const int rows = r.kind == kKindSoftmax ? 2 * r.L + 1 : (r.kind == kKindGreedy ? r.L + 1 : 0);
+      const ReqInfo r = has_pre ? pre : req_info(a, b);
+      const int rows = r.kind == kKindSoftmax ? 2 * r.L : (r.kind == kKindGreedy ? r.L : 0);
       info[b] = r.L | (r.kind << 8);
       cval[b] = r.c;
       start[b] = rows * a.G;  // count for now
@@ -211,7 +218,7 @@ __device__ void build_plan(const VerifyArgs& a, int* start, int* info, float* cv
   }
   if (lane_id() == kWave - 1) wsum[tid / kWave] = incl;
   __syncthreads();
-  int off = incl - local;
+  int off = a.B * a.G + incl - local;
   for (int w = 0; w < tid / kWave; ++w) off += wsum[w];
   for (int i = 0; i < per; ++i) {
     const int b = b0 + i;
@@ -225,26 +232,38 @@ __device__ void build_plan(const VerifyArgs& a, int* start, int* info, float* cv
   __syncthreads();
 }
 
+// Tile t of the list.  Tiles of target row 0 need no plan.
 template <int DT>
 __device__ __forceinline__ TileRef decode_tile(const VerifyArgs& a, const int* start,
                                                const int* info, int t) {
   constexpr int S = Elem<DT>::kBytes;
   constexpr int E = item_elems<DT>();
-  // request: last b with start[b] <= t (binary search; rows with no tiles
-  // have start[b] == start[b+1] and are never chosen)
-  int lo = 0, hi = a.B - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (start[mid] <= t) lo = mid;
-    else hi = mid - 1;
+  const int P0 = a.B * a.G;
+  int b, c, side, j;
+  if (t < P0) {
+    b = t / a.G;
+    c = t - b * a.G;
+    side = 0;
+    j = 0;
+  } else {
+    // request: last b with start[b] <= t (binary search; requests with no
+    // tiles have start[b] == start[b+1] and are never chosen)
+    int lo = 0, hi = a.B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (start[mid] <= t) lo = mid;
+      else hi = mid - 1;
+    }
+    b = uniform(lo);
+    const int q = t - uniform(start[b]);
+    const int row = q / a.G;
+    c = q - row * a.G;
+    const int L = uniform(info[b]) & 0xff;
+    side = row < L ? 0 : 1;
+    j = side ? row - L : row + 1;
   }
-  const int b = uniform(lo);
-  const int q = t - uniform(start[b]);
-  const int row = q / a.G;
-  const int c = q - row * a.G;
-  const int L = uniform(info[b]) & 0xff;
-  const int side = row <= L ? 0 : 1;
-  const int j = side ? row - L - 1 : row;
+  b = uniform(b);
+  c = uniform(c);
   TileRef ref;
   ref.e0 = c * E;
   ref.n = min(E, a.V - ref.e0);
@@ -276,10 +295,12 @@ __device__ __forceinline__ void summarise_tile(const Tile<DT>& t, const TileRef&
   *ref.out = out;
 }
 
-// k_stream_rows: one workgroup per compute unit.  Workgroup g owns the
-// contiguous tile range [T*g/n, T*(g+1)/n) of the plan; its waves take tiles
-// from that range through an LDS counter, so that waves which the compute
-// unit's arbitration serves more slowly simply take fewer tiles.
+// k_stream_rows: one workgroup per compute unit.  Workgroup g takes tiles
+// g, g + n, g + 2n, ... of the list (n workgroups), spreading every
+// workgroup's reads over the whole list; its waves take these tiles in turn
+// through an LDS counter, so that waves which the compute unit's arbitration
+// serves more slowly simply take fewer tiles.  A wave's first tile, when it
+// is a row-0 tile, is requested before the plan is built.
 template <int DT, bool VEC>
 __global__ void __launch_bounds__(kStreamBlock) k_stream_rows(VerifyArgs a) {
   extern __shared__ int plan[];
@@ -287,22 +308,9 @@ __global__ void __launch_bounds__(kStreamBlock) k_stream_rows(VerifyArgs a) {
   int* start = plan;                                        // [B + 1]
   int* info = plan + a.B + 1;                               // [B]
   float* cval = reinterpret_cast<float*>(plan + 2 * a.B + 1);  // [B]
-  build_plan(a, start, info, cval);
-  const int total = uniform(start[a.B]);
   const int n = gridDim.x, g = blockIdx.x;
-  const int per = total / n, rem = total - per * n;
-  const int begin = uniform(g * per + min(g, rem));
-  const int end = uniform(begin + per + (g < rem ? 1 : 0));
-  if (threadIdx.x == 0) s_next = begin + kStreamWaves;
-  __syncthreads();
   const int w = uniform((int)(threadIdx.x / kWave));
-  // next tile index for this wave (one LDS atomic by lane 0)
-  auto grab = [&]() -> int {
-    int x = 0;
-    if (lane_id() == 0) x = atomicAdd(&s_next, 1);
-    return uniform(readlane(x, 0));
-  };
-  int t0 = begin + w;
+  auto tile_of = [&](int k) { return g + n * k; };
   // Two tile buffers: the next tile's loads are in flight while the current
   // one is summarised.  The prefetch is issued unconditionally (past the end
   // of the range a wave re-reads its current tile, a cache hit, and drops
@@ -310,17 +318,42 @@ __global__ void __launch_bounds__(kStreamBlock) k_stream_rows(VerifyArgs a) {
   // wait for the older tile only.
   Tile<DT> A, Bt;
   TileRef ra, rb;
+  int t0 = w;
+  // On the vector path a wave whose first tile is a row-0 tile requests it
+  // at once; with one request per thread the request data follows, so the
+  // two round trips overlap.
+  const bool one_each = a.B <= kStreamBlock;
+  const bool early = VEC && one_each && tile_of(t0) < a.B * a.G;
+  if (early) {
+    ra = decode_tile<DT>(a, start, info, tile_of(t0));
+    A.template load<VEC>(ra.base, ra.n);
+  }
+  ReqInfo mine{0, kKindSkip, 0, 0.f};
+  if (one_each && (int)threadIdx.x < a.B) mine = req_info(a, threadIdx.x);
+  build_plan(a, start, info, cval, one_each, mine);
+  const int total = uniform(start[a.B]);
+  const int end = uniform((total - g + n - 1) / n);  // tiles of this workgroup
+  if (threadIdx.x == 0) s_next = kStreamWaves;
+  __syncthreads();
+  // next tile index for this wave (one LDS atomic by lane 0)
+  auto grab = [&]() -> int {
+    int x = 0;
+    if (lane_id() == 0) x = atomicAdd(&s_next, 1);
+    return uniform(readlane(x, 0));
+  };
   if (t0 >= end) return;
-  ra = decode_tile<DT>(a, start, info, t0);
-  A.template load<VEC>(ra.base, ra.n);
+  if (!early) {
+    ra = decode_tile<DT>(a, start, info, tile_of(t0));
+    A.template load<VEC>(ra.base, ra.n);
+  }
   while (true) {
     const int t1 = grab();
-    rb = decode_tile<DT>(a, start, info, t1 < end ? t1 : t0);
+    rb = decode_tile<DT>(a, start, info, tile_of(t1 < end ? t1 : t0));
     Bt.template load<VEC>(rb.base, rb.n);
     summarise_tile<DT>(A, ra, uniform(info[ra.b]) >> 8, uniform(cval[ra.b]));
     if (t1 >= end) break;
     t0 = grab();
-    ra = decode_tile<DT>(a, start, info, t0 < end ? t0 : t1);
+    ra = decode_tile<DT>(a, start, info, tile_of(t0 < end ? t0 : t1));
     A.template load<VEC>(ra.base, ra.n);
     summarise_tile<DT>(Bt, rb, uniform(info[rb.b]) >> 8, uniform(cval[rb.b]));
     if (t0 >= end) break;
