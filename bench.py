@@ -7,6 +7,13 @@ seeded synthetic inputs resident in HBM).  Six input sets (seed offsets
 0, 100, ..., 500; 641 MB each) rotate so that no step reads logits left in the
 256 MB last-level cache by the step before.
 
+The timed region launches the K steps directly on one stream with nothing
+in between (``--graphs`` replays each step from its own HIP graph instead,
+which is slower on this stack).  Kernel times (schedule, verify, streaming
+pass) come from a separate pass over the same steps with events around each
+call and, recorded by the library on the same stream, around each streaming
+launch.
+
 Prints ONE JSON line on stdout.  ``value`` = sum of verified positions
 (sum_b L_b) per second of schedule + verify.  ``roofline`` reports the
 dominant kernel, the streaming pass (k_stream_rows), against the 8 TB/s HBM
@@ -101,6 +108,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB")
+    ap.add_argument("--graphs", action="store_true",
+                    help="replay each timed step from its own HIP graph (slower on this stack)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this path runs on a "
@@ -139,28 +148,27 @@ def main():
     ws_v = ds.workspace(ds.OP_VERIFY, B, K, V, dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(i):
+    def step(i, cur, ev=None):
+        """One step on stream `cur`; with `ev` = five events: around schedule,
+        around verify, and (recorded by the library) around the streaming
+        launch."""
         w, o = sets[i % len(sets)], outs[i % len(sets)]
+        if ev is not None:
+            ev[0].record(cur)
         ds.schedule(w.conf, w.threshold, w.budget, w.min_len, lengths=o["lengths"], mask=o["mask"],
-                    survival=o["surv"], dev_status=o["st"], ws=ws_s, stream=stream)
+                    survival=o["surv"], dev_status=o["st"], ws=ws_s, stream=cur)
+        if ev is not None:
+            ev[1].record(cur)
+            ds.dspark_set_stream_events(ev[3], ev[4])
         ds.verify(w.target, w.draft, w.drafted, o["lengths"], w.temperature, w.uniforms,
                   accepted=o["acc"], tokens=o["tok"], p_tok=o["pt"], q_tok=o["qt"],
-                  dev_status=o["st"], ws=ws_v, stream=stream)
-
-    def step_events(i, e0, e1, e2, s0, s1):
-        w, o = sets[i % len(sets)], outs[i % len(sets)]
-        e0.record(stream)
-        ds.schedule(w.conf, w.threshold, w.budget, w.min_len, lengths=o["lengths"], mask=o["mask"],
-                    survival=o["surv"], dev_status=o["st"], ws=ws_s, stream=stream)
-        e1.record(stream)
-        ds.dspark_set_stream_events(s0, s1)
-        ds.verify(w.target, w.draft, w.drafted, o["lengths"], w.temperature, w.uniforms,
-                  accepted=o["acc"], tokens=o["tok"], p_tok=o["pt"], q_tok=o["qt"],
-                  dev_status=o["st"], ws=ws_v, stream=stream)
-        e2.record(stream)
+                  dev_status=o["st"], ws=ws_v, stream=cur)
+        if ev is not None:
+            ds.dspark_set_stream_events(None, None)
+            ev[2].record(cur)
 
     for i in range(args.warmup):
-        step(i)
+        step(i, stream)
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
@@ -177,32 +185,60 @@ def main():
         sbytes.append(stream_bytes(w, L, T))
         accs.append((a, L))
 
-    # timed region: K steps; events around each call and, recorded by the
-    # library on the same stream, around each streaming launch
+    # Kernel timing pass: direct launches with events around schedule, around
+    # verify and, recorded by the library on the same stream, around the
+    # streaming launch.
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     for e in ev:
-        for x in e[3:]:
-            x.record(stream)           # creates the HIP events the library records
+        for x in e:
+            x.record(stream)           # creates the HIP events
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, stream, ev[i])
+    torch.cuda.synchronize()
+    sched_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    ver_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    str_ms = [e[3].elapsed_time(e[4]) for e in ev]
+    assert all(0 < t <= v for t, v in zip(str_ms, ver_ms)), "stream events outside verify"
+
+    # Timed region: K steps launched directly on one stream with nothing
+    # between the calls (an event between kernels delays the next one); with
+    # --graphs each step is replayed from its own HIP graph instead.
+    graphs = None
+    if args.graphs:
+        try:
+            graphs = []
+            for i in range(args.steps):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    step(i, torch.cuda.current_stream(dev))
+                graphs.append(g)
+            for g in graphs[: len(sets)]:
+                g.replay()             # first replays are warm-up
+            torch.cuda.synchronize()
+        except Exception as ex:        # no graph support: launch directly
+            log(f"graph capture unavailable ({ex}); timing direct launches")
+            graphs = None
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
-        step_events(i, *ev[i])
+        if graphs is not None:
+            graphs[i].replay()
+        else:
+            step(i, stream)
     t_end.record(stream)
     torch.cuda.synchronize()
-    ds.dspark_set_stream_events(None, None)
     total_ms = t_start.elapsed_time(t_end)
-    sched_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    ver_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    str_ms = [e[3].elapsed_time(e[4]) for e in ev]
     n_pos = sum(pos[i % len(sets)] for i in range(args.steps))
     n_bytes = sum(nbytes[i % len(sets)] for i in range(args.steps))
     s_bytes = sum(sbytes[i % len(sets)] for i in range(args.steps))
     value = n_pos / (total_ms / 1e3)
     verify_gbs = n_bytes / (sum(ver_ms) / 1e3) / 1e9
     stream_gbs = s_bytes / (sum(str_ms) / 1e3) / 1e9
-    log(f"timed {args.steps} steps: {total_ms:.3f} ms; schedule median {np.median(sched_ms)*1e3:.1f} us, "
+    log(f"timed {args.steps} steps ({'graphs' if graphs is not None else 'direct'}): {total_ms:.3f} ms, "
+        f"{total_ms / args.steps * 1e3:.1f} us/step; kernel pass: schedule median {np.median(sched_ms)*1e3:.1f} us, "
         f"verify median {np.median(ver_ms)*1e3:.1f} us ({verify_gbs:.0f} GB/s); streaming pass median "
         f"{np.median(str_ms)*1e3:.1f} us ({stream_gbs:.0f} GB/s)")
     mean_acc = float(np.mean([a.mean() for a, _ in accs]))
@@ -226,6 +262,7 @@ def main():
             "workload": f"{w0.name}: V={V}, B={B}, K={K}, bf16 logits, T=1, threshold 0.2, budget 512",
             "logits": w0.dtype,
             "input_sets": len(sets),
+            "launch": "hip graph per step" if graphs is not None else "direct",
             "positions_per_step": pos,
             "verify_bytes_per_call": nbytes,
             "stream_bytes_per_call": sbytes,
@@ -244,6 +281,8 @@ def main():
             "verify_call_gbs": round(verify_gbs, 1),
             "verify_us_median": round(float(np.median(ver_ms)) * 1e3, 2),
             "schedule_us_median": round(float(np.median(sched_ms)) * 1e3, 2),
+            "kernel_timing": "separate pass over the same steps, events around each call and "
+                             "(library-recorded, same stream) around each streaming launch",
         },
         "accepted_mean": round(mean_acc, 3),
         "waste_ratio": round(waste, 4),
