@@ -420,6 +420,17 @@ template <int DT, int NV> struct LaneRun {
   }
 };
 
+// scalar element fetch as stored bits, and their exact widening
+template <int DT> __device__ __forceinline__ uint32_t load_raw(const void* row, int idx) {
+  if constexpr (DT == DSPARK_BF16)
+    return static_cast<uint32_t>(static_cast<const uint16_t*>(row)[idx]);
+  else
+    return static_cast<const uint32_t*>(row)[idx];
+}
+template <int DT> __device__ __forceinline__ float raw_to_float(uint32_t x) {
+  return DT == DSPARK_BF16 ? __uint_as_float(x << 16) : __uint_as_float(x);
+}
+
 // scalar element fetch (exact widening)
 template <int DT> __device__ __forceinline__ float load_elem(const void* row, int idx) {
   if constexpr (DT == DSPARK_BF16) {

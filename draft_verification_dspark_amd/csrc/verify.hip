@@ -28,9 +28,10 @@
 //                  row summaries (shifts align by exact powers of two), and
 //                  wave 0 forms p(y), q(y), alpha, the accept ballot and the
 //                  first rejection; workgroup 0 writes the outputs and the
-//                  draw state; on a rejection every wave sums the residual
-//                  mass of one 4096-token chunk of the rejected row pair
-//                  (fp32, elements with normalised mass >= 2^-12 in fp64).
+//                  draw state (after its other work); on a rejection every
+//                  pair of waves sums the residual mass of one 4096-token
+//                  chunk of the rejected row pair (fp32, elements with
+//                  normalised mass >= 2^-12 in fp64).
 //   k_draw         one workgroup per request with a pending draw: the bonus
 //                  token (from the pass-1 chunk sums of target row L) or the
 //                  correction token (from the residual chunk masses); a block
@@ -524,19 +525,19 @@ __device__ __forceinline__ float vec_elem(const uint32_t (&w)[4], int e) {
     return __uint_as_float(x);
 }
 
-// Residual mass of one chunk of the rejected row pair (wave total).  Vector
-// by vector: the fp32 terms, then, for a vector holding an element with p or
-// q >= 2^-12, those elements again in fp64 (a rolled loop).  The empty asm
-// statements keep each vector's work in place, so that the compiler does not
-// spread all vectors' conversions over the whole pass.
-template <int DT, bool VEC>
-__device__ double residual_chunk_mass(const ResidualRows& rr, const char* tchunk,
-                                      const char* dchunk, int n) {
+// Residual mass of U of a chunk's kUnroll vectors per lane, starting at
+// vector v0, of the rejected row pair (wave total).  Vector by vector: the
+// fp32 terms, then, for a vector holding an element with p or q >= 2^-12,
+// those elements again in fp64 (a rolled loop).  The empty asm statements
+// keep each vector's work in place, so that the compiler does not spread all
+// vectors' conversions over the whole pass.
+template <int DT, bool VEC, int U>
+__device__ double residual_piece_mass(const ResidualRows& rr, const char* tchunk,
+                                      const char* dchunk, int n, int v0) {
   constexpr int P = Elem<DT>::kPerVec;
-  constexpr int U = kUnroll;
-  Tile<DT> tt, td;
-  tt.template load<VEC>(tchunk, n);
-  td.template load<VEC>(dchunk, n);
+  TileN<DT, U> tt, td;
+  tt.template load<VEC>(tchunk, n, v0);
+  td.template load<VEC>(dchunk, n, v0);
   float light = 0.f;
   double heavy = 0.0;
 #pragma unroll
@@ -603,16 +604,18 @@ __device__ __forceinline__ Located wave_locate(double x, double u) {
 // ------------------------------------------------------------------ decide
 
 // k_decide: `groups` workgroups of kDecideBlock threads per request.  Each
-// merges the request's row summaries (waves take rows in turn, a few rows'
-// loads in flight at once), then wave 0 decides: p(y), q(y), alpha, the
-// accept ballot, the first rejection.  Workgroup 0 writes the outputs and the
-// draw state.  On a rejection every wave then sums the residual mass of one
-// chunk of the rejected row pair.
+// stages the request's chunk summaries in LDS and merges its rows (16-lane
+// groups, one row each), then wave 0 decides: p(y), q(y), alpha, the accept
+// ballot, the first rejection.  On a rejection the workgroup then sums the
+// residual mass of kChunksPerGroup chunks of the rejected row pair, two waves
+// per chunk.  Workgroup 0 finally writes the outputs and the draw state.
 #ifndef DSPARK_DECIDE_BLOCK
-#define DSPARK_DECIDE_BLOCK 256
+#define DSPARK_DECIDE_BLOCK 512
 #endif
 constexpr int kDecideBlock = DSPARK_DECIDE_BLOCK;
 constexpr int kDecideWaves = kDecideBlock / kWave;
+// two waves share each residual chunk, half of its vectors each
+constexpr int kChunksPerGroup = kDecideWaves / 2;
 constexpr int kMaxRows = 2 * 64 + 1;
 // chunk summaries staged in LDS per round of the merges (24 KB)
 constexpr int kStage = 1536;
@@ -624,24 +627,28 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
   __shared__ RowSum s_rows[kMaxRows + 2];  // merged rows, then the rejected pair
   __shared__ Partial s_part[kStage];       // chunk summaries of the rows being merged
   __shared__ int s_a, s_bad;
+  __shared__ double s_half[kDecideWaves];
   const int b = blockIdx.x / a.groups;
   const int g = blockIdx.x - b * a.groups;
   const int w = uniform((int)(threadIdx.x / kWave));
   const int l = lane_id();
   const int K = a.K;
-  // wave 0, lane l: position l+1's drafted id and accept uniform.  They do
-  // not depend on the length, so they are requested together with it.
-  int y = 0;
-  float u = 0.f;
-  if (w == 0 && l < K) {
-    y = a.drafted[(size_t)b * K + l];
-    if (a.uniforms) u = a.uniforms[(size_t)b * (K + 1) + l];
-  }
-  const float u_draw = a.uniforms ? a.uniforms[(size_t)b * (K + 1) + K] : 0.f;
+  // Requested together, before anything waits: the request's length and
+  // temperature, the final uniform and, for wave 0 lane l, the drafted id
+  // and accept uniform of position l+1.  Loads whose value is used later are
+  // kept out of lane-dependent branches (lanes past K re-read column K-1),
+  // so that the compiler does not wait for them on the spot.
+  const int lcol = min(l, K - 1);
+  // (a greedy-only call has no uniforms: the drafted ids stand in, unused)
+  const float* ub = a.uniforms ? a.uniforms + (size_t)b * (K + 1)
+                               : reinterpret_cast<const float*>(a.drafted);
+  const int y = a.drafted[(size_t)b * K + lcol];
+  const float u = ub[a.uniforms ? lcol : 0];
+  const float u_draw = a.uniforms ? ub[K] : 0.f;
   const ReqInfo r = req_info(a, b);
   const int L = r.L;
   int32_t* tok = a.tokens + (size_t)b * (K + 1);
-  const bool lead = g == 0;
+  const bool lead = g == 0;  // writes the request's outputs
 
   if (r.kind == kKindSkip) {
     if (lead && w == 0) {
@@ -660,17 +667,16 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
   }
   const bool soft = r.kind == kKindSoftmax;
 
-  // the drafted tokens' logits, gathered now so that they arrive during the
-  // merges
-  bool yok = true;
-  float xt = 0.f, xd = 0.f;
-  if (w == 0 && l < L) {
-    yok = y >= 0 && y < a.V;
-    if (yok) {
-      xt = load_elem<DT>(target_row(a, b, l, S), y);
-      if (soft) xd = load_elem<DT>(draft_row(a, b, l, S), y);
-    }
-  }
+  // The drafted tokens' logits, gathered with the first staged summaries so
+  // that one round trip covers both.  Lanes past L (and bad ids) read a
+  // scheduled row at id 0 and ignore it: only target rows 0..L and draft
+  // rows 0..L-1 are touched.
+  const bool in_range = y >= 0 && y < a.V;
+  const int yc = in_range ? y : 0;
+  const bool yok = l >= L || in_range;
+  const char* trow = target_row(a, b, min(l, L), S);
+  const char* drow = soft && L > 0 ? draft_row(a, b, min(l, L - 1), S) : trow;  // unused then
+  uint32_t xt_raw = 0, xd_raw = 0;
 
   // Merges.  Row order q: soft requests take target rows 0..L-1 (q = j),
   // draft rows 0..L-1 (q = L + j), then target row L (q = 2L); greedy
@@ -694,15 +700,28 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
       const int cnt = nr * G;
       q_last = q0;
       if (q0 > 0) __syncthreads();  // the previous round's merges are done
+      // every load first (slots past the count re-read the first summary),
+      // then every LDS store, so the loads share one round trip
+      constexpr int kPer = kStage / kDecideBlock;
+      Partial tmp[kPer];
 #pragma unroll
-      for (int k = 0; k < kStage / kDecideBlock; ++k) {
+      for (int k = 0; k < kPer; ++k) {
         const int i = k * kDecideBlock + (int)threadIdx.x;
-        if (i < cnt) {
-          const int rr = i / G;
-          int side;
-          const int j = row_of(q0 + rr, side);
-          s_part[i] = row_parts(a, b, j, side)[i - rr * G];
-        }
+        const int ii = i < cnt ? i : 0;
+        const int rr = ii / G;
+        int side;
+        const int j = row_of(q0 + rr, side);
+        tmp[k] = row_parts(a, b, j, side)[ii - rr * G];
+      }
+      xt_raw = load_raw<DT>(trow, yc);  // (re-gathered in later rounds)
+      xd_raw = load_raw<DT>(drow, yc);
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) asm volatile("" : "+v"(tmp[k].k), "+v"(tmp[k].idx), "+v"(tmp[k].s));
+      asm volatile("" : "+v"(xt_raw), "+v"(xd_raw));
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int i = k * kDecideBlock + (int)threadIdx.x;
+        if (i < cnt) s_part[i] = tmp[k];
       }
       __syncthreads();
       for (int rr = grp; rr < nr; rr += kDecideBlock / 16) {
@@ -713,6 +732,8 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
     }
   } else {
     // very long rows: waves merge whole rows straight from global memory
+    xt_raw = load_raw<DT>(trow, yc);
+    xd_raw = load_raw<DT>(drow, yc);
     for (int q = w; q < nrows; q += kDecideWaves) {
       int side;
       const int j = row_of(q, side);
@@ -723,7 +744,12 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
     }
   }
   __syncthreads();
+  const float xt = raw_to_float<DT>(xt_raw), xd = raw_to_float<DT>(xd_raw);
 
+  // outputs of this request (wave 0), written at the end of the kernel
+  int an = 0, bad = 0, gtok = 0;
+  float pf = 0.f, qf = 0.f;
+  ReqState st{};
   if (w == 0) {
     const RowSum rL = s_rows[qL];  // target row L: the bonus row
     RowSum rt{}, rd{};
@@ -731,12 +757,11 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
       rt = s_rows[l];
       if (soft) rd = s_rows[L + l];
     }
-    int bad = r.bad;
+    bad = r.bad;
     if (!yok) bad |= DSPARK_DEV_BAD_TOKEN;
     if (l < L) bad |= rt.bad | rd.bad;
     if (l == 0) bad |= rL.bad;
     bool acc = false;
-    float pf = 0.f, qf = 0.f;
     if (soft) {
       if (l < L) {
         if (!(rt.s > 0.0) || !(rd.s > 0.0)) bad |= DSPARK_DEV_NONFINITE;  // no finite logit
@@ -762,19 +787,10 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
     const uint64_t m = __ballot(acc);
     const uint64_t want = L >= 64 ? ~0ull : ((1ull << L) - 1ull);
     const uint64_t rej = ~m & want;
-    const int an = rej ? __builtin_ctzll(rej) : L;
+    an = rej ? __builtin_ctzll(rej) : L;
     bad = wave_or(bad);
     if (lead) {
-      int gtok = 0;
       if (!soft) gtok = an < L ? readlane(rt.idx, an) : rL.idx;
-      if (l < K) {
-        if (a.p_tok) a.p_tok[(size_t)b * K + l] = pf;
-        if (a.q_tok) a.q_tok[(size_t)b * K + l] = qf;
-      }
-      for (int i = l; i <= K; i += kWave) {
-        if (i < an) tok[i] = a.drafted[(size_t)b * K + i];
-        else if (i > an || !soft) tok[i] = i == an ? gtok : -1;
-      }
       // draw state: the target row of the draw and, on a rejection, the
       // draft row's shift and sum as well
       const RowSum dt = an < L ? RowSum{readlane(rt.s, an), readlane(rt.k, an), 0, 0, 0} : rL;
@@ -788,26 +804,20 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
         const double mass = l < G && pc.s > 0.0 ? ldexp(pc.s, shift_amount(pc.k - rL.k)) : 0.0;
         bonus = wave_locate(mass, (double)u_draw);
       }
-      if (l == 0) {
-        a.accepted[b] = an;
-        if (bad) flag(a.dev_status, bad);
-        ReqState st;
-        st.mode = (!soft || (bad & (DSPARK_DEV_BAD_TOKEN | DSPARK_DEV_NONFINITE)))
-                      ? kModeNone
-                      : (an == L ? kModeBonus : kModeResidual);
-        st.row = an;
-        st.a = an;
-        st.c = r.c;
-        st.kt = dt.k;
-        st.st = dt.s;
-        st.kd = dd.k;
-        st.sd = dd.s;
-        st.cstar = bonus.idx;
-        st.past_end = bonus.past_end;
-        st.base = bonus.base;
-        st.total = bonus.total;
-        a.req[b] = st;
-      }
+      st.mode = (!soft || (bad & (DSPARK_DEV_BAD_TOKEN | DSPARK_DEV_NONFINITE)))
+                    ? kModeNone
+                    : (an == L ? kModeBonus : kModeResidual);
+      st.row = an;
+      st.a = an;
+      st.c = r.c;
+      st.kt = dt.k;
+      st.st = dt.s;
+      st.kd = dd.k;
+      st.sd = dd.s;
+      st.cstar = bonus.idx;
+      st.past_end = bonus.past_end;
+      st.base = bonus.base;
+      st.total = bonus.total;
     }
     if (an < L && an == l) {
       s_rows[kMaxRows] = rt;  // the rejected target row
@@ -819,20 +829,47 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
     }
   }
   __syncthreads();
-  const int an = s_a;
-  const int bad = s_bad;
-  // greedy requests are complete, faulty ones have unspecified outputs, and
-  // after a full acceptance k_draw draws the bonus token from pass-1 sums
-  if (!soft || (bad & (DSPARK_DEV_BAD_TOKEN | DSPARK_DEV_NONFINITE)) || an == L) return;
-  const RowSum rt = s_rows[kMaxRows], rd = s_rows[kMaxRows + 1];
-  const ResidualRows rr(r.c, rt.k, rt.s, rd.k, rd.s);
-  const int pi = g * kDecideWaves + w;
-  if (pi < a.G) {
-    const int e0 = pi * E;
-    const int n = min(E, a.V - e0);
-    const double z = residual_chunk_mass<DT, VEC>(rr, target_row(a, b, an, S) + (size_t)e0 * S,
-                                                  draft_row(a, b, an, S) + (size_t)e0 * S, n);
-    if (l == 0) a.part2[(size_t)b * a.G + pi] = z;
+  // on a rejection (sampled, no fault) every workgroup of the request sums
+  // the residual of its chunks; greedy requests are complete, faulty ones
+  // have unspecified outputs, and after a full acceptance k_draw draws the
+  // bonus token from the pass-1 sums
+  const int an_all = s_a;
+  const int bad_all = s_bad;
+  if (soft && !(bad_all & (DSPARK_DEV_BAD_TOKEN | DSPARK_DEV_NONFINITE)) && an_all < L) {
+    const int an = an_all;
+    const RowSum rt = s_rows[kMaxRows], rd = s_rows[kMaxRows + 1];
+    const ResidualRows rr(r.c, rt.k, rt.s, rd.k, rd.s);
+    const int cl = w % kChunksPerGroup, half = w / kChunksPerGroup;
+    const int pi = g * kChunksPerGroup + cl;
+    double z = 0.0;
+    if (pi < a.G) {
+      const int e0 = pi * E;
+      const int n = min(E, a.V - e0);
+      z = residual_piece_mass<DT, VEC, kUnroll / 2>(rr, target_row(a, b, an, S) + (size_t)e0 * S,
+                                                    draft_row(a, b, an, S) + (size_t)e0 * S, n,
+                                                    half * (kUnroll / 2));
+    }
+    if (l == 0) s_half[w] = z;
+    __syncthreads();
+    if (half == 0 && pi < a.G && l == 0)
+      a.part2[(size_t)b * a.G + pi] = s_half[w] + s_half[w + kChunksPerGroup];
+  }
+  // the lead workgroup writes the request's outputs last, so that none of its
+  // stores holds up the residual work above
+  if (lead && w == 0) {
+    if (l < K) {
+      if (a.p_tok) a.p_tok[(size_t)b * K + l] = pf;
+      if (a.q_tok) a.q_tok[(size_t)b * K + l] = qf;
+    }
+    for (int i = l; i <= K; i += kWave) {
+      if (i < an) tok[i] = y;  // lane i holds the drafted id of position i+1
+      else if (i > an || !soft) tok[i] = i == an ? gtok : -1;
+    }
+    if (l == 0) {
+      a.accepted[b] = an;
+      if (bad) flag(a.dev_status, bad);
+      a.req[b] = st;
+    }
   }
 }
 
@@ -1078,7 +1115,7 @@ static int launch_verify_t(VerifyArgs& a, hipStream_t st, hipEvent_t ev0, hipEve
   hipLaunchKernelGGL((k_stream_rows<DT, VEC>), dim3((unsigned)grid), dim3(kStreamBlock), lds, st,
                      a);
   if (ev0 && ev1 && hipEventRecord(ev1, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
-  a.groups = (a.G + kDecideWaves - 1) / kDecideWaves;
+  a.groups = (a.G + kChunksPerGroup - 1) / kChunksPerGroup;
   hipLaunchKernelGGL((k_decide<DT, VEC>), dim3((unsigned)((long)a.B * a.groups)),
                      dim3(kDecideBlock), 0, st, a);
   if (!a.greedy_only)
