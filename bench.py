@@ -25,6 +25,11 @@ the HBM bytes per launch that rocprofv3 counters measured for the same kernel
 sources still hash to the recorded value.  ``cpu_baseline`` times the CPU
 oracle on a bounded sample of the same workload.
 
+``rows`` times, apart from the step, the hot-path rows the step does not
+exercise: the greedy rule on the same logits, full-length blocks, the
+schedule with a binding budget and a mixed-temperature batch of 1024
+requests (``--no-rows`` skips them).
+
 --calibrate-copy N runs, after the timed steps, a plain elementwise copy of
 N MiB (read N MiB, write N MiB) five times: the reference kernel of known size
 for the FETCH_SIZE / WRITE_SIZE counter runs.
@@ -98,6 +103,149 @@ def measured_traffic():
     return float(m_t.group(1)), "rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-kernel scaled"
 
 
+def time_calls(fn, reps, stream, torch):
+    """Median and mean of `reps` calls of fn(), each between two events."""
+    ts = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        ts.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ts)
+    return ms[len(ms) // 2], sum(ms) / len(ms)
+
+
+def row_measurements(ds, workloads, sets, outs, ws_v, dev, stream, torch, np, log):
+    """The hot-path rows the headline step does not exercise, each timed
+    apart (not part of `value`): the greedy rule, full-length blocks, a
+    binding budget and a mixed-temperature batch of 1024 requests."""
+    rows = {}
+    n = len(sets)
+    B, K, V = sets[0].B, sets[0].K, sets[0].V
+    s = 2
+
+    def stream_timed(call, reps):
+        """Mean streaming-pass time (events recorded by the library) and
+        median whole-call time over `reps` calls; call(i, before, after)."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+                torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for e in evs:
+            for x in e:
+                x.record(stream)
+        torch.cuda.synchronize()
+        for i, (c0, s0, s1, c1) in enumerate(evs):
+            c0.record(stream)
+            ds.dspark_set_stream_events(s0, s1)
+            call(i)
+            ds.dspark_set_stream_events(None, None)
+            c1.record(stream)
+        torch.cuda.synchronize()
+        st = [s0.elapsed_time(s1) for _, s0, s1, _ in evs]
+        ca = sorted(c0.elapsed_time(c1) for c0, _, _, c1 in evs)
+        return float(np.mean(st)), ca[len(ca) // 2]
+
+    # G1: greedy rule on the same logits and scheduled lengths
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    tok = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    st_ = torch.zeros(1, dtype=torch.int32, device=dev)
+    for i in range(n):
+        ds.verify_greedy(sets[i].target, sets[i].drafted, outs[i]["lengths"], accepted=acc,
+                         tokens=tok, dev_status=st_, ws=ws_v, stream=stream)
+    gb = [s * V * int((outs[i]["lengths"].cpu().numpy().astype(np.int64) + 1).sum()) for i in range(n)]
+    t_s, t_c = stream_timed(lambda i: ds.verify_greedy(
+        sets[i % n].target, sets[i % n].drafted, outs[i % n]["lengths"], accepted=acc, tokens=tok,
+        dev_status=st_, ws=ws_v, stream=stream), 24)
+    gbs = float(np.mean(gb)) / (t_s / 1e3) / 1e9
+    rows["G1_verify_greedy"] = {"workload": "b64-k16-v151936 logits, scheduled lengths",
+                                "stream_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                "stream_us_mean": round(t_s * 1e3, 2), "call_us_median": round(t_c * 1e3, 2)}
+
+    # V1-V5 at full length: every block verified to K
+    full = torch.full((B,), K, dtype=torch.int32, device=dev)
+    accf = torch.empty(B, dtype=torch.int32, device=dev)
+    tokf = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    ptf = torch.empty((B, K), dtype=torch.float32, device=dev)
+    qtf = torch.empty((B, K), dtype=torch.float32, device=dev)
+
+    def vfull(i):
+        w = sets[i % n]
+        ds.verify(w.target, w.draft, w.drafted, full, w.temperature, w.uniforms, accepted=accf,
+                  tokens=tokf, p_tok=ptf, q_tok=qtf, dev_status=st_, ws=ws_v, stream=stream)
+    for i in range(n):
+        vfull(i)
+    fb = s * V * B * (2 * K + 1)
+    t_s, t_c = stream_timed(vfull, 18)
+    gbs = fb / (t_s / 1e3) / 1e9
+    rows["V_full_length"] = {"workload": "b64-k16-v151936, every length = K (641.8 MB per pass)",
+                             "stream_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                             "stream_us_mean": round(t_s * 1e3, 2), "call_us_median": round(t_c * 1e3, 2),
+                             "positions_per_s": round(B * K / (t_c / 1e3), 1)}
+
+    # S3 and the mixed batch: workload b1024-k8-v151936 (temperatures 0 / 0.6 / 1)
+    w5 = workloads.make(5, device=dev)
+    B5, K5, V5 = w5.B, w5.K, w5.V
+    ws_s5 = ds.workspace(ds.OP_SCHEDULE, B5, K5, 1, dev)
+    ws_v5 = ds.workspace(ds.OP_VERIFY, B5, K5, V5, dev)
+    L5 = torch.empty(B5, dtype=torch.int32, device=dev)
+    m5 = torch.empty((B5, K5), dtype=torch.uint8, device=dev)
+    c5 = torch.empty((B5, K5), dtype=torch.float32, device=dev)
+    st5 = torch.zeros(1, dtype=torch.int32, device=dev)
+    ds.schedule(w5.conf, w5.threshold, -1, w5.min_len, lengths=L5, mask=m5, survival=c5,
+                dev_status=st5, ws=ws_s5, stream=stream)
+    l_thr = int(L5.sum().item())
+
+    def sched5():
+        ds.schedule(w5.conf, w5.threshold, w5.budget, w5.min_len, lengths=L5, mask=m5,
+                    survival=c5, dev_status=st5, ws=ws_s5, stream=stream)
+    sched5()
+    t_med, _ = time_calls(sched5, 30, stream, torch)
+    rows["S1_S3_schedule_b1024"] = {"workload": "b1024-k8, threshold 0.3, budget 3072",
+                                    "threshold_lengths_sum": l_thr, "budget": w5.budget,
+                                    "budget_binds": l_thr > w5.budget,
+                                    "call_us_median": round(t_med * 1e3, 2)}
+    # the same confidences under a budget that binds (half the threshold
+    # lengths): the radix select of the budget cut runs
+    half = max(B5 * w5.min_len, l_thr // 2)
+
+    def sched5b():
+        ds.schedule(w5.conf, w5.threshold, half, w5.min_len, lengths=L5, mask=m5,
+                    survival=c5, dev_status=st5, ws=ws_s5, stream=stream)
+    sched5b()
+    t_med, _ = time_calls(sched5b, 30, stream, torch)
+    rows["S3_schedule_binding_b1024"] = {"workload": "b1024-k8, threshold 0.3, budget = half the "
+                                                     "threshold lengths",
+                                         "budget": half, "call_us_median": round(t_med * 1e3, 2)}
+    sched5()  # back to the configured lengths for the verify row
+    a5 = torch.empty(B5, dtype=torch.int32, device=dev)
+    t5 = torch.empty((B5, K5 + 1), dtype=torch.int32, device=dev)
+    p5 = torch.empty((B5, K5), dtype=torch.float32, device=dev)
+    q5 = torch.empty((B5, K5), dtype=torch.float32, device=dev)
+
+    def v5(i):
+        ds.verify(w5.target, w5.draft, w5.drafted, L5, w5.temperature, w5.uniforms, accepted=a5,
+                  tokens=t5, p_tok=p5, q_tok=q5, dev_status=st5, ws=ws_v5, stream=stream)
+    v5(0)
+    torch.cuda.synchronize()
+    L = L5.cpu().numpy().astype(np.int64)
+    T = w5.temperature.cpu().numpy()
+    b5 = s * V5 * int((((2 * L + 1) * (T > 0)) + ((L + 1) * (T == 0))).sum())
+    t_s, t_c = stream_timed(v5, 12)
+    gbs = b5 / (t_s / 1e3) / 1e9
+    rows["V_G1_mixed_b1024"] = {"workload": "b1024-k8-v151936, temperatures 0 / 0.6 / 1, scheduled",
+                                "positions": int(L.sum()), "stream_bytes": b5,
+                                "stream_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                "stream_us_mean": round(t_s * 1e3, 2),
+                                "call_us_median": round(t_c * 1e3, 2),
+                                "positions_per_s": round(int(L.sum()) / (t_c / 1e3), 1)}
+    assert int(st_.item()) == 0 and int(st5.item()) == 0, "device status flags set"
+    log("rows: " + "; ".join(f"{k} {v.get('stream_gbs', v.get('call_us_median'))}" for k, v in rows.items()))
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,6 +256,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the separate timings of the other hot-path rows")
     ap.add_argument("--graphs", action="store_true",
                     help="replay each timed step from its own HIP graph (slower on this stack)")
     args = ap.parse_args()
@@ -286,6 +436,8 @@ def main():
         },
         "accepted_mean": round(mean_acc, 3),
         "waste_ratio": round(waste, 4),
+        "rows": None if args.no_rows else row_measurements(ds, workloads, sets, outs, ws_v, dev,
+                                                             stream, torch, np, log),
     }
 
     if args.calibrate_copy > 0:
