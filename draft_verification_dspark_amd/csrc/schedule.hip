@@ -12,7 +12,8 @@
 //            the free slots go to the candidates (b,k), min_len < k <= Lthr[b],
 //            in order (C desc, b asc, k asc).
 //
-// One workgroup of 1024 threads; thread t owns requests t, t + 1024, ....
+// One workgroup (1024 threads, 256 for at most 256 requests); thread t owns
+// requests t, t + T, t + 2T, ... for T threads.
 // The budget cut is a radix select over one 32-bit key per position: a
 // candidate's key is its survival bit pattern plus one (non-negative floats
 // order like their bits), every other position's key is 0, so that the m-th
@@ -29,8 +30,7 @@
 
 namespace dspark {
 
-constexpr int kSchedThreads = 1024;
-constexpr int kSchedWaves = kSchedThreads / kWave;
+constexpr int kSchedMaxThreads = 1024;
 constexpr int kSchedLds = 12288;  // positions whose keys fit in LDS (48 KB)
 constexpr int kSchedRegs = 8;     // requests per thread kept in registers
 
@@ -42,10 +42,11 @@ __device__ __forceinline__ uint32_t surv_key(float C) {
 // `prefix`: the digit at `shift` that holds the rank-th key counted from the
 // top (desc) or from the bottom (asc), and the rank within that digit, in
 // shared memory for every thread.
-template <typename KeyFn>
+template <int kSchedThreads, typename KeyFn>
 __device__ void radix_pass(int n, KeyFn key_of, int shift, bool desc, uint32_t prefix,
                            uint32_t pmask, long long& rank, int (*cnt)[16], uint32_t* s_digit,
                            long long* s_rank, long long* s_bucket) {
+  constexpr int kSchedWaves = kSchedThreads / kWave;
   const int tid = threadIdx.x;
   const int w = tid / kWave;
   int c[16];
@@ -96,9 +97,13 @@ __device__ void radix_pass(int n, KeyFn key_of, int shift, bool desc, uint32_t p
   rank = *s_rank;
 }
 
+// kSchedThreads threads: 1024, or 256 for small batches (a smaller
+// workgroup starts sooner; one thread per request still covers them)
+template <int kSchedThreads>
 __global__ void __launch_bounds__(kSchedThreads) k_schedule(ScheduleArgs a) {
+  constexpr int kSchedWaves = kSchedThreads / kWave;
   __shared__ long long red[kSchedWaves];
-  __shared__ int cnt[kSchedWaves][16];
+  __shared__ int cnt[kSchedMaxThreads / kWave][16];
   __shared__ uint32_t s_digit;
   __shared__ long long s_rank, s_bucket;
   __shared__ uint32_t s_key[kSchedLds];
@@ -123,18 +128,19 @@ __global__ void __launch_bounds__(kSchedThreads) k_schedule(ScheduleArgs a) {
     for (int k0 = 0; k0 < K; k0 += 8) {
       float ck[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ck[i] = k0 + i < K ? cr[k0 + i] : 1.f;
+      for (int i = 0; i < 8; ++i) ck[i] = cr[min(k0 + i, K - 1)];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int k = k0 + i;  // 0-based position
-        if (k >= K) break;
-        if (!(ck[i] >= 0.f && ck[i] <= 1.f)) bad |= DSPARK_DEV_BAD_CONF;
-        C = k == 0 ? ck[i] : C * ck[i];
-        sr[k] = C;
-        go = go && C >= a.tau;
-        if (go) ++run;
-        // candidate: past the floor and inside the leading run
-        if (keys_in_lds) s_key[(size_t)b * K + k] = (go && k + 1 > ml) ? surv_key(C) + 1u : 0u;
+        if (k < K) {
+          if (!(ck[i] >= 0.f && ck[i] <= 1.f)) bad |= DSPARK_DEV_BAD_CONF;
+          C = k == 0 ? ck[i] : C * ck[i];
+          sr[k] = C;
+          go = go && C >= a.tau;
+          if (go) ++run;
+          // candidate: past the floor and inside the leading run
+          if (keys_in_lds) s_key[(size_t)b * K + k] = (go && k + 1 > ml) ? surv_key(C) + 1u : 0u;
+        }
       }
     }
     const int lt = max(ml, run);
@@ -179,7 +185,7 @@ __global__ void __launch_bounds__(kSchedThreads) k_schedule(ScheduleArgs a) {
     uint32_t prefix = 0, pmask = 0;
     long long rank = m, bucket = 0;
     for (int shift = 28; shift >= 0; shift -= 4) {
-      radix_pass(n, [=](int i, uint32_t& key) {
+      radix_pass<kSchedThreads>(n, [=](int i, uint32_t& key) {
                    key = key_at(i);
                    return true;
                  },
@@ -199,7 +205,7 @@ __global__ void __launch_bounds__(kSchedThreads) k_schedule(ScheduleArgs a) {
       int top = 0;
       while (top < 28 && (((uint32_t)(n - 1)) >> (top + 4)) != 0u) top += 4;
       for (int shift = top; shift >= 0; shift -= 4) {
-        radix_pass(n, [=](int i, uint32_t& key) {
+        radix_pass<kSchedThreads>(n, [=](int i, uint32_t& key) {
                      if (key_at(i) != kstar) return false;
                      key = (uint32_t)i;
                      return true;
@@ -229,13 +235,27 @@ __global__ void __launch_bounds__(kSchedThreads) k_schedule(ScheduleArgs a) {
     a.lengths[b] = len;
     if (a.mask) {
       uint8_t* mr = a.mask + (size_t)b * K;
-      for (int k = 0; k < K; ++k) mr[k] = (uint8_t)(k < len ? 1 : 0);
+      if ((K & 3) == 0 && ((uintptr_t)a.mask & 3) == 0) {
+        // four mask bytes per store
+        uint32_t* mw = reinterpret_cast<uint32_t*>(mr);
+        for (int k = 0; k < K; k += 4) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) word |= (uint32_t)(k + q < len ? 1u : 0u) << (8 * q);
+          mw[k >> 2] = word;
+        }
+      } else {
+        for (int k = 0; k < K; ++k) mr[k] = (uint8_t)(k < len ? 1 : 0);
+      }
     }
   }
 }
 
 int launch_schedule(ScheduleArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_schedule, dim3(1), dim3(kSchedThreads), 0, st, a);
+  if (a.B <= 256)
+    hipLaunchKernelGGL(k_schedule<256>, dim3(1), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_schedule<1024>, dim3(1), dim3(1024), 0, st, a);
   return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_ERR_LAUNCH;
 }
 
