@@ -116,6 +116,7 @@ int dspark_schedule(const float* conf, int B, int K, float threshold, int budget
   a.surv = survival ? survival : reinterpret_cast<float*>(ws + L.surv);
   a.lthr = reinterpret_cast<int32_t*>(ws + L.lthr);
   a.dev_status = dev_status;
+  a.vec4 = (K % 4 == 0) && aligned(conf, 16) && aligned(a.surv, 16);
   return launch_schedule(a, static_cast<hipStream_t>(stream));
 }
 

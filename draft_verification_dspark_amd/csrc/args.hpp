@@ -19,6 +19,7 @@ struct ScheduleArgs {
   float* surv;         // [B,K] survival (the caller's output or workspace)
   int32_t* lthr;       // [B] workspace
   int32_t* dev_status;
+  int vec4;            // K % 4 == 0 and conf, surv 16-byte aligned
 };
 
 struct VerifyArgs {

@@ -18,12 +18,15 @@
 // candidate's key is its survival bit pattern plus one (non-negative floats
 // order like their bits), every other position's key is 0, so that the m-th
 // largest key (m = free slots, fewer than the candidates) is a candidate's.
-// Eight 4-bit passes count digit histograms with wave ballots (no LDS
-// atomics, so equal digits do not serialise); ties at the cut are resolved by
-// a second select on the flat index b*K + (k-1), smallest first.  The keys
-// live in LDS when there are at most kSchedLds positions (else they are
-// recomputed from the stored survival), and each thread keeps the threshold
-// lengths of its first kSchedRegs requests in registers.
+// 4-bit passes start at the highest bit where the candidates' keys differ
+// (the bits above are common to all of them).  Each lane counts digits in
+// 4-bit fields of one 64-bit word (a few instructions per key, no LDS
+// atomics, so equal digits do not serialise) and each wave sums its lanes
+// with a transposing butterfly.  Ties at the cut are resolved by a second
+// select on the flat index b*K + (k-1), smallest first.  The keys live in
+// LDS when there are at most kSchedLds positions (else they are recomputed
+// from the stored survival), and each thread keeps the threshold lengths of
+// its first kSchedRegs requests in registers.
 #include <hip/hip_runtime.h>
 
 #include "args.hpp"
@@ -33,68 +36,183 @@ namespace dspark {
 constexpr int kSchedMaxThreads = 1024;
 constexpr int kSchedLds = 12288;  // positions whose keys fit in LDS (48 KB)
 constexpr int kSchedRegs = 8;     // requests per thread kept in registers
+constexpr int kConfStage = 32;    // confidences per thread loaded at once
 
 __device__ __forceinline__ uint32_t surv_key(float C) {
   return C == 0.f ? 0u : __float_as_uint(C);  // -0 and +0 are one key
 }
 
-// One radix pass over the n keys key_of(i) whose bits under `pmask` equal
-// `prefix`: the digit at `shift` that holds the rank-th key counted from the
-// top (desc) or from the bottom (asc), and the rank within that digit, in
-// shared memory for every thread.
-template <int kSchedThreads, typename KeyFn>
-__device__ void radix_pass(int n, KeyFn key_of, int shift, bool desc, uint32_t prefix,
-                           uint32_t pmask, long long& rank, int (*cnt)[16], uint32_t* s_digit,
-                           long long* s_rank, long long* s_bucket) {
+// Sum over the wave's lanes of 16 per-lane counters c[0..15], by a
+// transposing butterfly: at each exchange a lane keeps half of the counters
+// it still holds and adds its partner's copy of that half.  After four
+// exchanges lane l holds digit ((l>>5)&1)*8 + ((l>>4)&1)*4 + ((l>>3)&1)*2 +
+// ((l>>2)&1), summed over 16 lanes; two more exchanges complete the sum over
+// the four lanes holding each digit.
+__device__ __forceinline__ uint32_t wave_sum16(const uint32_t (&c)[16], int& digit) {
+  const int l = lane_id();
+  uint32_t c8[8], c4[4], c2[2];
+  bool hi = (l >> 5) & 1;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    c8[j] = (hi ? c[j + 8] : c[j]) + (uint32_t)__shfl_xor((int)(hi ? c[j] : c[j + 8]), 32);
+  hi = (l >> 4) & 1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    c4[j] = (hi ? c8[j + 4] : c8[j]) + (uint32_t)__shfl_xor((int)(hi ? c8[j] : c8[j + 4]), 16);
+  hi = (l >> 3) & 1;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    c2[j] = (hi ? c4[j + 2] : c4[j]) + (uint32_t)__shfl_xor((int)(hi ? c4[j] : c4[j + 2]), 8);
+  hi = (l >> 2) & 1;
+  uint32_t c1 = (hi ? c2[1] : c2[0]) + (uint32_t)__shfl_xor((int)(hi ? c2[0] : c2[1]), 4);
+  c1 += (uint32_t)__shfl_xor((int)c1, 2);
+  c1 += (uint32_t)__shfl_xor((int)c1, 1);
+  digit = ((l >> 5) & 1) * 8 + ((l >> 4) & 1) * 4 + ((l >> 3) & 1) * 2 + ((l >> 2) & 1);
+  return c1;
+}
+
+// Key sources of the radix passes.  Key of position i = b*K + (k-1):
+// survival bits + 1 for a candidate, else 0.  LdsKeys reads the keys stored
+// in LDS; MemKeys recomputes them from the stored survival and threshold
+// length.  Both read unconditionally (the caller passes a valid index), so a
+// loop over several keys has all its loads in flight at once.
+struct LdsKeys {
+  const uint32_t* s;
+  __device__ __forceinline__ uint32_t operator()(int i) const { return s[i]; }
+};
+struct MemKeys {
+  const float* surv;
+  const int32_t* lthr;
+  int K, ml;
+  __device__ __forceinline__ uint32_t operator()(int i) const {
+    const int b = i / K, k = i - b * K + 1;
+    const int lt = lthr[b];
+    const uint32_t key = surv_key(surv[i]) + 1u;
+    return (k > ml && k <= lt) ? key : 0u;
+  }
+};
+
+// One radix pass over the n positions whose pass key has the bits under
+// `pmask` equal to `prefix`.  The pass key is the position's key (kIndex
+// false) or, for positions whose key equals `kmatch`, the flat index (kIndex
+// true; other positions do not take part).  Finds the digit at `shift` that
+// holds the rank-th pass key counted from the top (desc) or from the bottom
+// (asc), the rank within that digit and the number of pass keys with that
+// digit, in every thread.  Each lane counts in 4-bit fields of one 64-bit
+// word (field d counts digit d; at most kFlush keys between flushes into
+// 32-bit counters), each wave sums its lanes, and every wave reads the
+// per-wave sums from `cnt` (this pass's buffer: consecutive passes alternate
+// two buffers, so one barrier per pass suffices).
+template <int kSchedThreads, bool kIndex, typename Src>
+__device__ void radix_pass(int n, const Src& src, uint32_t kmatch, int shift, bool desc,
+                           uint32_t prefix, uint32_t pmask, long long& rank, long long& bucket,
+                           uint32_t& digit, int (*cnt)[16]) {
   constexpr int kSchedWaves = kSchedThreads / kWave;
+  constexpr int kGroup = 4;             // keys per lane in flight
+  constexpr int kFlush = 3 * kGroup;    // keys per lane between flushes (<= 15)
   const int tid = threadIdx.x;
-  const int w = tid / kWave;
-  int c[16];
+  const int l = lane_id();
+  uint32_t c[16];
 #pragma unroll
   for (int d = 0; d < 16; ++d) c[d] = 0;
-  for (int base = 0; base < n; base += kSchedThreads) {
-    const int i = base + tid;
-    uint32_t key = 0;
-    bool ok = false;
-    if (i < n) ok = key_of(i, key);
-    ok = ok && ((key & pmask) == prefix);
-    const uint32_t d = (key >> shift) & 15u;
+  for (int b0 = 0; b0 < n; b0 += kFlush * kSchedThreads) {
+    const int lim = min(n, b0 + kFlush * kSchedThreads);
+    uint64_t nib = 0;
+    for (int base = b0; base < lim; base += kGroup * kSchedThreads) {
+      uint32_t kv[kGroup];
 #pragma unroll
-    for (int dd = 0; dd < 16; ++dd) c[dd] += __popcll(__ballot(ok && d == (uint32_t)dd));
-  }
-  if (lane_id() == 0) {
+      for (int r = 0; r < kGroup; ++r) kv[r] = src(min(base + r * kSchedThreads + tid, n - 1));
 #pragma unroll
-    for (int dd = 0; dd < 16; ++dd) cnt[w][dd] = c[dd];
-  }
-  __syncthreads();
-  if (tid < kWave) {
-    // lane s (< 16) holds digit dd = 15 - s (desc) or s (asc), counted over
-    // the waves; an inclusive scan over those 16 lanes finds the digit whose
-    // running count first reaches the rank
-    const int s = tid & 15;
-    const int dd = desc ? 15 - s : s;
-    int tot = 0;
-#pragma unroll
-    for (int ww = 0; ww < kSchedWaves; ++ww) tot += cnt[ww][dd];
-    if (tid >= 16) tot = 0;
-    int incl = tot;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const int t = __shfl_up(incl, o, 16);
-      if (s >= o) incl += t;
+      for (int r = 0; r < kGroup; ++r) {
+        const int i = base + r * kSchedThreads + tid;
+        bool ok = i < lim;
+        uint32_t key = kv[r];
+        if (kIndex) {
+          ok = ok && key == kmatch;
+          key = (uint32_t)i;
+        }
+        ok = ok && ((key & pmask) == prefix);
+        const uint32_t d = (key >> shift) & 15u;
+        nib += (uint64_t)(ok ? 1u : 0u) << (4 * d);
+      }
     }
-    const uint64_t reach = __ballot(tid < 16 && (long long)incl >= rank);
-    const int first = reach ? __builtin_ctzll(reach) : 15;  // rank never exceeds the total
-    const int before = __shfl(incl - tot, first);
-    const int bucket = __shfl(tot, first);
-    if (tid == 0) {
-      *s_digit = (uint32_t)(desc ? 15 - first : first);
-      *s_rank = rank - before;
-      *s_bucket = bucket;
-    }
+#pragma unroll
+    for (int d = 0; d < 16; ++d) c[d] += (uint32_t)(nib >> (4 * d)) & 15u;
   }
+  int dg;
+  const uint32_t sum = wave_sum16(c, dg);
+  if ((l & 3) == 0) cnt[tid / kWave][dg] = (int)sum;
   __syncthreads();
-  rank = *s_rank;
+  // lane s (< 16) holds digit dd = 15 - s (desc) or s (asc), counted over
+  // the waves; an inclusive scan over those 16 lanes finds the digit whose
+  // running count first reaches the rank
+  const int s = l & 15;
+  const int dd = desc ? 15 - s : s;
+  int tot = 0;
+#pragma unroll
+  for (int ww = 0; ww < kSchedWaves; ++ww) tot += cnt[ww][dd];
+  if (l >= 16) tot = 0;
+  int incl = tot;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) {
+    const int t = __shfl_up(incl, o, 16);
+    if (s >= o) incl += t;
+  }
+  const uint64_t reach = __ballot(l < 16 && (long long)incl >= rank);
+  const int first = reach ? __builtin_ctzll(reach) : 15;  // rank never exceeds the total
+  const int before = __shfl(incl - tot, first);
+  bucket = __shfl(tot, first);
+  digit = (uint32_t)(desc ? 15 - first : first);
+  rank -= before;
+}
+
+// The budget cut: the m-th largest key kstar (m < number of candidates, so
+// it is a candidate's; all candidates' keys exceed every other key) and,
+// when the cut splits the positions with key kstar, the largest flat index
+// istar among those taken (else istar = 0xffffffff).  kor / kand: OR and AND
+// of the candidates' keys; ncand: their number.  The candidates share the
+// bits above the highest bit where kor and kand differ, so the passes start
+// at the digit holding that bit.
+template <int kSchedThreads, typename Src>
+__device__ void budget_cut(int n, const Src& src, long long m, long long ncand, uint32_t kor,
+                           uint32_t kand, int (*cnt)[kSchedThreads / kWave][16], uint32_t& kstar,
+                           uint32_t& istar) {
+  int pass = 0;  // selects the count buffer
+  long long rank = m, bucket = ncand;
+  const uint32_t diff = kor ^ kand;
+  if (diff != 0u) {
+    const int s0 = (31 - __builtin_clz(diff)) & ~3;
+    uint32_t pmask = s0 + 4 < 32 ? 0xffffffffu << (s0 + 4) : 0u;
+    uint32_t prefix = kand & pmask;
+    for (int shift = s0; shift >= 0; shift -= 4) {
+      uint32_t dg;
+      radix_pass<kSchedThreads, false>(n, src, 0u, shift, true, prefix, pmask, rank, bucket, dg,
+                                       cnt[pass++ & 1]);
+      prefix |= dg << shift;
+      pmask |= 15u << shift;
+    }
+    kstar = prefix;
+  } else {
+    kstar = kand;  // one key for every candidate
+  }
+  // `bucket` positions share key kstar; take the `rank` of them with the
+  // smallest flat index
+  istar = 0xffffffffu;
+  if (rank < bucket) {
+    uint32_t ip = 0, im = 0;
+    long long b2 = 0;
+    // the flat index has fewer than 32 bits: higher digits are all 0
+    int top = 0;
+    while (top < 28 && (((uint32_t)(n - 1)) >> (top + 4)) != 0u) top += 4;
+    for (int shift = top; shift >= 0; shift -= 4) {
+      uint32_t dg;
+      radix_pass<kSchedThreads, true>(n, src, kstar, shift, false, ip, im, rank, b2, dg,
+                                      cnt[pass++ & 1]);
+      ip |= dg << shift;
+      im |= 15u << shift;
+    }
+    istar = ip;
+  }
 }
 
 // kSchedThreads threads: 1024, or 256 for small batches (a smaller
@@ -103,9 +221,8 @@ template <int kSchedThreads>
 __global__ void __launch_bounds__(kSchedThreads) k_schedule(ScheduleArgs a) {
   constexpr int kSchedWaves = kSchedThreads / kWave;
   __shared__ long long red[kSchedWaves];
-  __shared__ int cnt[kSchedMaxThreads / kWave][16];
-  __shared__ uint32_t s_digit;
-  __shared__ long long s_rank, s_bucket;
+  __shared__ uint32_t red_or[kSchedWaves], red_and[kSchedWaves];
+  __shared__ int cnt[2][kSchedWaves][16];
   __shared__ uint32_t s_key[kSchedLds];
   const int tid = threadIdx.x;
   const int B = a.B, K = a.K;
@@ -117,6 +234,7 @@ __global__ void __launch_bounds__(kSchedThreads) k_schedule(ScheduleArgs a) {
   // candidates' keys go to LDS on the way
   int lt_reg[kSchedRegs];
   long long local = 0;
+  uint32_t kor = 0u, kand = 0xffffffffu;  // OR and AND of the candidates' keys
   int bad = 0;
   for (int j = 0, b = tid; b < B; ++j, b += kSchedThreads) {
     const float* __restrict__ cr = a.conf + (size_t)b * K;
@@ -124,23 +242,51 @@ __global__ void __launch_bounds__(kSchedThreads) k_schedule(ScheduleArgs a) {
     float C = 1.f;
     int run = 0;  // leading positions with C >= tau
     bool go = true;
-    // confidences are loaded 8 at a time ahead of the dependent products
-    for (int k0 = 0; k0 < K; k0 += 8) {
-      float ck[8];
+    // up to kConfStage confidences are loaded at once (16-byte loads when
+    // rows are 16-byte aligned), ahead of the dependent products; the
+    // survival values overwrite them and are stored the same way
+    for (int k0 = 0; k0 < K; k0 += kConfStage) {
+      float ck[kConfStage];
+      if (a.vec4) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ck[i] = cr[min(k0 + i, K - 1)];
+        for (int q = 0; q < kConfStage / 4; ++q) {
+          const float4 v = *reinterpret_cast<const float4*>(cr + min(k0 + 4 * q, K - 4));
+          ck[4 * q] = v.x;
+          ck[4 * q + 1] = v.y;
+          ck[4 * q + 2] = v.z;
+          ck[4 * q + 3] = v.w;
+        }
+      } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < kConfStage; ++i) ck[i] = cr[min(k0 + i, K - 1)];
+      }
+#pragma unroll
+      for (int i = 0; i < kConfStage; ++i) {
         const int k = k0 + i;  // 0-based position
         if (k < K) {
           if (!(ck[i] >= 0.f && ck[i] <= 1.f)) bad |= DSPARK_DEV_BAD_CONF;
           C = k == 0 ? ck[i] : C * ck[i];
-          sr[k] = C;
+          ck[i] = C;
           go = go && C >= a.tau;
           if (go) ++run;
           // candidate: past the floor and inside the leading run
-          if (keys_in_lds) s_key[(size_t)b * K + k] = (go && k + 1 > ml) ? surv_key(C) + 1u : 0u;
+          const bool cand = go && k + 1 > ml;
+          const uint32_t key = surv_key(C) + 1u;
+          if (keys_in_lds) s_key[(size_t)b * K + k] = cand ? key : 0u;
+          kor |= cand ? key : 0u;
+          kand &= cand ? key : 0xffffffffu;
         }
+      }
+      if (a.vec4) {
+#pragma unroll
+        for (int q = 0; q < kConfStage / 4; ++q)
+          if (k0 + 4 * q < K)
+            *reinterpret_cast<float4*>(sr + k0 + 4 * q) =
+                make_float4(ck[4 * q], ck[4 * q + 1], ck[4 * q + 2], ck[4 * q + 3]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < kConfStage; ++i)
+          if (k0 + i < K) sr[k0 + i] = ck[i];
       }
     }
     const int lt = max(ml, run);
@@ -158,64 +304,40 @@ __global__ void __launch_bounds__(kSchedThreads) k_schedule(ScheduleArgs a) {
       if (jj == j) v = lt_reg[jj];
     return j < kSchedRegs ? v : a.lthr[b];
   };
-  // block sum of Lthr (the barrier also publishes the LDS keys and the
-  // stored survival and threshold lengths to the other threads)
-  for (int o = 32; o > 0; o >>= 1) local += __shfl_xor(local, o);
-  if (lane_id() == 0) red[tid / kWave] = local;
+  // block sum of Lthr, OR and AND of the candidates' keys (the barrier also
+  // publishes the LDS keys and the stored survival and threshold lengths to
+  // the other threads)
+  for (int o = 32; o > 0; o >>= 1) {
+    local += __shfl_xor(local, o);
+    kor |= (uint32_t)__shfl_xor((int)kor, o);
+    kand &= (uint32_t)__shfl_xor((int)kand, o);
+  }
+  if (lane_id() == 0) {
+    red[tid / kWave] = local;
+    red_or[tid / kWave] = kor;
+    red_and[tid / kWave] = kand;
+  }
   __syncthreads();
   long long total = 0;
-  for (int w = 0; w < kSchedWaves; ++w) total += red[w];
+  kor = 0u;
+  kand = 0xffffffffu;
+  for (int w = 0; w < kSchedWaves; ++w) {
+    total += red[w];
+    kor |= red_or[w];
+    kand &= red_and[w];
+  }
 
   const long long floor_all = (long long)B * ml;
   const bool binds = a.budget >= 0 && total > a.budget;
   const long long m = binds ? (long long)a.budget - floor_all : 0;  // free slots, >= 0
   uint32_t kstar = 0xffffffffu, istar = 0u;  // no candidate is taken by default
   if (binds && m > 0) {
-    const float* surv = a.surv;
-    const int* lthr_mem = a.lthr;
-    // key of position i: survival bits + 1 for a candidate, else 0 (from
-    // LDS, or recomputed from the stored survival and threshold length)
-    auto key_at = [=](int i) -> uint32_t {
-      if (keys_in_lds) return s_key[i];
-      const int b = i / K, k = i - b * K + 1;
-      const int lt = lthr_mem[b];
-      return (k > ml && k <= lt) ? surv_key(surv[i]) + 1u : 0u;
-    };
-    // m-th largest key (all candidates' keys exceed every other key)
-    uint32_t prefix = 0, pmask = 0;
-    long long rank = m, bucket = 0;
-    for (int shift = 28; shift >= 0; shift -= 4) {
-      radix_pass<kSchedThreads>(n, [=](int i, uint32_t& key) {
-                   key = key_at(i);
-                   return true;
-                 },
-                 shift, true, prefix, pmask, rank, cnt, &s_digit, &s_rank, &s_bucket);
-      prefix |= s_digit << shift;
-      pmask |= 15u << shift;
-      bucket = s_bucket;
-    }
-    kstar = prefix;
-    // `bucket` positions share key kstar; take the `rank` of them with the
-    // smallest flat index
-    istar = 0xffffffffu;
-    if (rank < bucket) {
-      uint32_t ip = 0, im = 0;
-      long long r2 = rank;
-      // the flat index has fewer than 32 bits: higher digits are all 0
-      int top = 0;
-      while (top < 28 && (((uint32_t)(n - 1)) >> (top + 4)) != 0u) top += 4;
-      for (int shift = top; shift >= 0; shift -= 4) {
-        radix_pass<kSchedThreads>(n, [=](int i, uint32_t& key) {
-                     if (key_at(i) != kstar) return false;
-                     key = (uint32_t)i;
-                     return true;
-                   },
-                   shift, false, ip, im, r2, cnt, &s_digit, &s_rank, &s_bucket);
-        ip |= s_digit << shift;
-        im |= 15u << shift;
-      }
-      istar = ip;
-    }
+    if (keys_in_lds)
+      budget_cut<kSchedThreads>(n, LdsKeys{s_key}, m, total - floor_all, kor, kand, cnt, kstar,
+                                istar);
+    else
+      budget_cut<kSchedThreads>(n, MemKeys{a.surv, a.lthr, K, ml}, m, total - floor_all, kor,
+                                kand, cnt, kstar, istar);
   }
   // lengths and mask, each request by its owner thread
   for (int j = 0, b = tid; b < B; ++j, b += kSchedThreads) {

@@ -286,6 +286,22 @@ def test_schedule_random(B, K):
             assert int(g[3].item()) == 0
 
 
+@pytest.mark.parametrize("B,K", [(64, 16), (700, 8), (2000, 8)])
+def test_schedule_equal_and_near_keys(B, K):
+    # every candidate with one survival value (the select reduces to the
+    # flat-index order), and values that differ only in the last mantissa bits
+    ones = np.ones((B, K), np.float32)
+    near = np.ones((B, K), np.float32)
+    rng = np.random.default_rng(B + K)
+    near[:, 1:] = np.float32(1.0) - rng.integers(0, 4, size=(B, K - 1)).astype(np.float32) * np.float32(2.0 ** -24)
+    for conf in (ones, near):
+        ct = torch.from_numpy(conf).to(DEV)
+        for bud in (B + 1, B * K // 2 + 3, B * K - 1):
+            g = ds.schedule(ct, 0.5, bud, 1)
+            torch.cuda.synchronize()
+            compare_schedule((host(g[0]), host(g[1]), host(g[2])), oracle.schedule(conf, 0.5, bud, 1))
+
+
 def test_schedule_golden_and_subnormals():
     import json, os
     with open(os.path.join(os.path.dirname(__file__), "golden", "schedule_cases.json")) as f:
