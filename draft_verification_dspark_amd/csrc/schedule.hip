@@ -42,33 +42,39 @@ __device__ __forceinline__ uint32_t surv_key(float C) {
   return C == 0.f ? 0u : __float_as_uint(C);  // -0 and +0 are one key
 }
 
-// Sum over the wave's lanes of 16 per-lane counters c[0..15], by a
-// transposing butterfly: at each exchange a lane keeps half of the counters
-// it still holds and adds its partner's copy of that half.  After four
-// exchanges lane l holds digit ((l>>5)&1)*8 + ((l>>4)&1)*4 + ((l>>3)&1)*2 +
-// ((l>>2)&1), summed over 16 lanes; two more exchanges complete the sum over
-// the four lanes holding each digit.
-__device__ __forceinline__ uint32_t wave_sum16(const uint32_t (&c)[16], int& digit) {
+// Sums over each 16-lane row of 16 per-lane counters c[0..15], by a
+// transposing butterfly of DPP moves: at each exchange a lane keeps half of
+// the counters it still holds and adds its partner's copy of that half.  The
+// partners (row mirror, half-row mirror, quad xor 2, quad xor 1) differ from
+// the lane in bit 3, 2, 1, 0 of its row position, so lane l ends with the
+// row's sum for digit l & 15.
+__device__ __forceinline__ uint32_t row_sum16(const uint32_t (&c)[16]) {
   const int l = lane_id();
   uint32_t c8[8], c4[4], c2[2];
-  bool hi = (l >> 5) & 1;
+  bool hi = (l >> 3) & 1;
 #pragma unroll
   for (int j = 0; j < 8; ++j)
-    c8[j] = (hi ? c[j + 8] : c[j]) + (uint32_t)__shfl_xor((int)(hi ? c[j] : c[j + 8]), 32);
-  hi = (l >> 4) & 1;
+    c8[j] = (hi ? c[j + 8] : c[j]) + (uint32_t)dpp<kRowMirror>((int)(hi ? c[j] : c[j + 8]));
+  hi = (l >> 2) & 1;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    c4[j] = (hi ? c8[j + 4] : c8[j]) + (uint32_t)__shfl_xor((int)(hi ? c8[j] : c8[j + 4]), 16);
-  hi = (l >> 3) & 1;
+    c4[j] = (hi ? c8[j + 4] : c8[j]) + (uint32_t)dpp<kRowHalfMirror>((int)(hi ? c8[j] : c8[j + 4]));
+  hi = (l >> 1) & 1;
 #pragma unroll
   for (int j = 0; j < 2; ++j)
-    c2[j] = (hi ? c4[j + 2] : c4[j]) + (uint32_t)__shfl_xor((int)(hi ? c4[j] : c4[j + 2]), 8);
-  hi = (l >> 2) & 1;
-  uint32_t c1 = (hi ? c2[1] : c2[0]) + (uint32_t)__shfl_xor((int)(hi ? c2[0] : c2[1]), 4);
-  c1 += (uint32_t)__shfl_xor((int)c1, 2);
-  c1 += (uint32_t)__shfl_xor((int)c1, 1);
-  digit = ((l >> 5) & 1) * 8 + ((l >> 4) & 1) * 4 + ((l >> 3) & 1) * 2 + ((l >> 2) & 1);
-  return c1;
+    c2[j] = (hi ? c4[j + 2] : c4[j]) + (uint32_t)dpp<kQuadXor2>((int)(hi ? c4[j] : c4[j + 2]));
+  hi = l & 1;
+  return (hi ? c2[1] : c2[0]) + (uint32_t)dpp<kQuadXor1>((int)(hi ? c2[0] : c2[1]));
+}
+
+// inclusive prefix sum within each 16-lane row (row_shr 1, 2, 4, 8; lanes
+// without a source add 0)
+__device__ __forceinline__ int row_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);
+  return v;
 }
 
 // Key sources of the radix passes.  Key of position i = b*K + (k-1):
@@ -100,13 +106,13 @@ struct MemKeys {
 // (asc), the rank within that digit and the number of pass keys with that
 // digit, in every thread.  Each lane counts in 4-bit fields of one 64-bit
 // word (field d counts digit d; at most kFlush keys between flushes into
-// 32-bit counters), each wave sums its lanes, and every wave reads the
-// per-wave sums from `cnt` (this pass's buffer: consecutive passes alternate
+// 32-bit counters), each 16-lane row sums its lanes, and every wave reads the
+// per-row sums from `cnt` (this pass's buffer: consecutive passes alternate
 // two buffers, so one barrier per pass suffices).
 template <int kSchedThreads, bool kIndex, typename Src>
 __device__ void radix_pass(int n, const Src& src, uint32_t kmatch, int shift, bool desc,
                            uint32_t prefix, uint32_t pmask, long long& rank, long long& bucket,
-                           uint32_t& digit, int (*cnt)[16]) {
+                           uint32_t& digit, int (*cnt)[16][4]) {
   constexpr int kSchedWaves = kSchedThreads / kWave;
   constexpr int kGroup = 4;             // keys per lane in flight
   constexpr int kFlush = 3 * kGroup;    // keys per lane between flushes (<= 15)
@@ -139,29 +145,26 @@ __device__ void radix_pass(int n, const Src& src, uint32_t kmatch, int shift, bo
 #pragma unroll
     for (int d = 0; d < 16; ++d) c[d] += (uint32_t)(nib >> (4 * d)) & 15u;
   }
-  int dg;
-  const uint32_t sum = wave_sum16(c, dg);
-  if ((l & 3) == 0) cnt[tid / kWave][dg] = (int)sum;
+  // lane l holds its row's count of digit l & 15
+  cnt[tid / kWave][l & 15][l >> 4] = (int)row_sum16(c);
   __syncthreads();
-  // lane s (< 16) holds digit dd = 15 - s (desc) or s (asc), counted over
-  // the waves; an inclusive scan over those 16 lanes finds the digit whose
-  // running count first reaches the rank
+  // lane s (= l & 15, in every row) holds digit dd = 15 - s (desc) or s
+  // (asc), counted over the waves and rows; an inclusive scan over the 16
+  // lanes of a row finds the digit whose running count first reaches the
+  // rank
   const int s = l & 15;
   const int dd = desc ? 15 - s : s;
   int tot = 0;
 #pragma unroll
-  for (int ww = 0; ww < kSchedWaves; ++ww) tot += cnt[ww][dd];
-  if (l >= 16) tot = 0;
-  int incl = tot;
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) {
-    const int t = __shfl_up(incl, o, 16);
-    if (s >= o) incl += t;
+  for (int ww = 0; ww < kSchedWaves; ++ww) {
+    const int4 v = *reinterpret_cast<const int4*>(cnt[ww][dd]);
+    tot += (v.x + v.y) + (v.z + v.w);
   }
+  const int incl = row_incl_scan(tot);
   const uint64_t reach = __ballot(l < 16 && (long long)incl >= rank);
   const int first = reach ? __builtin_ctzll(reach) : 15;  // rank never exceeds the total
-  const int before = __shfl(incl - tot, first);
-  bucket = __shfl(tot, first);
+  const int before = __builtin_amdgcn_readlane(incl - tot, first);
+  bucket = __builtin_amdgcn_readlane(tot, first);
   digit = (uint32_t)(desc ? 15 - first : first);
   rank -= before;
 }
@@ -175,7 +178,7 @@ __device__ void radix_pass(int n, const Src& src, uint32_t kmatch, int shift, bo
 // at the digit holding that bit.
 template <int kSchedThreads, typename Src>
 __device__ void budget_cut(int n, const Src& src, long long m, long long ncand, uint32_t kor,
-                           uint32_t kand, int (*cnt)[kSchedThreads / kWave][16], uint32_t& kstar,
+                           uint32_t kand, int (*cnt)[kSchedThreads / kWave][16][4], uint32_t& kstar,
                            uint32_t& istar) {
   int pass = 0;  // selects the count buffer
   long long rank = m, bucket = ncand;
@@ -222,7 +225,7 @@ __global__ void __launch_bounds__(kSchedThreads) k_schedule(ScheduleArgs a) {
   constexpr int kSchedWaves = kSchedThreads / kWave;
   __shared__ long long red[kSchedWaves];
   __shared__ uint32_t red_or[kSchedWaves], red_and[kSchedWaves];
-  __shared__ int cnt[2][kSchedWaves][16];
+  __shared__ __align__(16) int cnt[2][kSchedWaves][16][4];  // [pass & 1][wave][digit][row]
   __shared__ uint32_t s_key[kSchedLds];
   const int tid = threadIdx.x;
   const int B = a.B, K = a.K;
@@ -307,15 +310,14 @@ __global__ void __launch_bounds__(kSchedThreads) k_schedule(ScheduleArgs a) {
   // block sum of Lthr, OR and AND of the candidates' keys (the barrier also
   // publishes the LDS keys and the stored survival and threshold lengths to
   // the other threads)
-  for (int o = 32; o > 0; o >>= 1) {
-    local += __shfl_xor(local, o);
-    kor |= (uint32_t)__shfl_xor((int)kor, o);
-    kand &= (uint32_t)__shfl_xor((int)kand, o);
-  }
+  // (a thread's sum is at most B*K <= 2^30: int)
+  const int wsum = wave_reduce((int)local, [](int x, int y) { return x + y; });
+  const int wor = wave_reduce((int)kor, [](int x, int y) { return x | y; });
+  const int wand = wave_reduce((int)kand, [](int x, int y) { return x & y; });
   if (lane_id() == 0) {
-    red[tid / kWave] = local;
-    red_or[tid / kWave] = kor;
-    red_and[tid / kWave] = kand;
+    red[tid / kWave] = wsum;
+    red_or[tid / kWave] = (uint32_t)wor;
+    red_and[tid / kWave] = (uint32_t)wand;
   }
   __syncthreads();
   long long total = 0;
