@@ -18,12 +18,12 @@
 //                  workgroup lays out the scheduled rows of all requests
 //                  (target rows 0..L, draft rows 0..L-1, or target rows only
 //                  for greedy requests) as a dense list of 4096-token tiles in
-//                  LDS and owns a contiguous range of it; its waves take tiles
-//                  through an LDS counter, double-buffering the 16-byte loads
-//                  of the next tile while summarising the current one: an
-//                  integer exponent shift k = ceil(max * c) and the sum of
-//                  2^(x*c - k) (fp32 terms, fp64 accumulation), or (max,
-//                  lowest index).
+//                  LDS and takes every n-th tile of it (n workgroups); its
+//                  waves take those tiles through an LDS counter,
+//                  double-buffering the 16-byte loads of the next tile while
+//                  summarising the current one: an integer exponent shift
+//                  k = ceil(max * c) and the sum of 2^(x*c - k) (fp32 terms,
+//                  fp64 accumulation), or (max, lowest index).
 //   k_decide       `groups` workgroups per request: each merges the request's
 //                  row summaries (shifts align by exact powers of two), and
 //                  wave 0 forms p(y), q(y), alpha, the accept ballot and the
@@ -607,18 +607,27 @@ __device__ __forceinline__ Located wave_locate(double x, double u) {
 // stages the request's chunk summaries in LDS and merges its rows (16-lane
 // groups, one row each), then wave 0 decides: p(y), q(y), alpha, the accept
 // ballot, the first rejection.  On a rejection the workgroup then sums the
-// residual mass of kChunksPerGroup chunks of the rejected row pair, two waves
-// per chunk.  Workgroup 0 finally writes the outputs and the draw state.
+// residual mass of kChunksPerGroup chunks of the rejected row pair,
+// kWavesPerChunk waves per chunk.  Workgroup 0 finally writes the outputs and
+// the draw state.
 #ifndef DSPARK_DECIDE_BLOCK
-#define DSPARK_DECIDE_BLOCK 512
+#define DSPARK_DECIDE_BLOCK 640
+#endif
+#ifndef DSPARK_WAVES_PER_CHUNK
+#define DSPARK_WAVES_PER_CHUNK 1
 #endif
 constexpr int kDecideBlock = DSPARK_DECIDE_BLOCK;
 constexpr int kDecideWaves = kDecideBlock / kWave;
-// two waves share each residual chunk, half of its vectors each
-constexpr int kChunksPerGroup = kDecideWaves / 2;
+// waves per residual chunk (each takes an equal share of its vectors).  Ten
+// waves with one wave per chunk: a request at 151,936 tokens (38 chunks)
+// needs 4 workgroups, so a batch of 64 requests is one workgroup per compute
+// unit, all resident at once (two waves per chunk measured slower at full
+// length and no faster as scheduled)
+constexpr int kWavesPerChunk = DSPARK_WAVES_PER_CHUNK;
+constexpr int kChunksPerGroup = kDecideWaves / kWavesPerChunk;
 constexpr int kMaxRows = 2 * 64 + 1;
-// chunk summaries staged in LDS per round of the merges (24 KB)
-constexpr int kStage = 1536;
+// chunk summaries staged in LDS per round of the merges (30 KB)
+constexpr int kStage = 3 * kDecideBlock;
 
 template <int DT, bool VEC>
 __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
@@ -839,20 +848,28 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
     const int an = an_all;
     const RowSum rt = s_rows[kMaxRows], rd = s_rows[kMaxRows + 1];
     const ResidualRows rr(r.c, rt.k, rt.s, rd.k, rd.s);
-    const int cl = w % kChunksPerGroup, half = w / kChunksPerGroup;
+    constexpr int kPart = kUnroll / kWavesPerChunk;  // vectors per wave
+    const int cl = w % kChunksPerGroup, part = w / kChunksPerGroup;
     const int pi = g * kChunksPerGroup + cl;
     double z = 0.0;
     if (pi < a.G) {
       const int e0 = pi * E;
       const int n = min(E, a.V - e0);
-      z = residual_piece_mass<DT, VEC, kUnroll / 2>(rr, target_row(a, b, an, S) + (size_t)e0 * S,
-                                                    draft_row(a, b, an, S) + (size_t)e0 * S, n,
-                                                    half * (kUnroll / 2));
+      z = residual_piece_mass<DT, VEC, kPart>(rr, target_row(a, b, an, S) + (size_t)e0 * S,
+                                              draft_row(a, b, an, S) + (size_t)e0 * S, n,
+                                              part * kPart);
     }
-    if (l == 0) s_half[w] = z;
-    __syncthreads();
-    if (half == 0 && pi < a.G && l == 0)
-      a.part2[(size_t)b * a.G + pi] = s_half[w] + s_half[w + kChunksPerGroup];
+    if (kWavesPerChunk == 1) {
+      if (pi < a.G && l == 0) a.part2[(size_t)b * a.G + pi] = z;
+    } else {
+      if (l == 0) s_half[w] = z;
+      __syncthreads();
+      if (part == 0 && pi < a.G && l == 0) {
+        double t = 0.0;
+        for (int h = 0; h < kWavesPerChunk; ++h) t += s_half[w + h * kChunksPerGroup];
+        a.part2[(size_t)b * a.G + pi] = t;
+      }
+    }
   }
   // the lead workgroup writes the request's outputs last, so that none of its
   // stores holds up the residual work above
