@@ -29,9 +29,9 @@
 //                  wave 0 forms p(y), q(y), alpha, the accept ballot and the
 //                  first rejection; workgroup 0 writes the outputs and the
 //                  draw state (after its other work); on a rejection every
-//                  pair of waves sums the residual mass of one 4096-token
-//                  chunk of the rejected row pair (fp32, elements with
-//                  normalised mass >= 2^-12 in fp64).
+//                  wave sums the residual mass of one 4096-token chunk of the
+//                  rejected row pair (fp32, elements with normalised mass
+//                  >= 2^-12 in fp64).
 //   k_draw         one workgroup per request with a pending draw: the bonus
 //                  token (from the pass-1 chunk sums of target row L) or the
 //                  correction token (from the residual chunk masses); a block
