@@ -36,7 +36,10 @@ namespace dspark {
 constexpr int kSchedMaxThreads = 1024;
 constexpr int kSchedLds = 12288;  // positions whose keys fit in LDS (48 KB)
 constexpr int kSchedRegs = 8;     // requests per thread kept in registers
-constexpr int kConfStage = 32;    // confidences per thread loaded at once
+#ifndef DSPARK_CONF_STAGE
+#define DSPARK_CONF_STAGE 8
+#endif
+constexpr int kConfStage = DSPARK_CONF_STAGE;  // confidences per thread loaded at once
 
 __device__ __forceinline__ uint32_t surv_key(float C) {
   return C == 0.f ? 0u : __float_as_uint(C);  // -0 and +0 are one key
@@ -172,14 +175,33 @@ __device__ void radix_pass(int n, const Src& src, uint32_t kmatch, int shift, bo
 // The budget cut: the m-th largest key kstar (m < number of candidates, so
 // it is a candidate's; all candidates' keys exceed every other key) and,
 // when the cut splits the positions with key kstar, the largest flat index
-// istar among those taken (else istar = 0xffffffff).  kor / kand: OR and AND
-// of the candidates' keys; ncand: their number.  The candidates share the
-// bits above the highest bit where kor and kand differ, so the passes start
-// at the digit holding that bit.
+// istar among those taken (else istar = 0xffffffff).  ncand: the number of
+// candidates.  The candidates share the bits above the highest bit where the
+// OR and the AND of their keys differ, so the passes start at the digit
+// holding that bit.  red_or / red_and: per-wave scratch in LDS.
 template <int kSchedThreads, typename Src>
-__device__ void budget_cut(int n, const Src& src, long long m, long long ncand, uint32_t kor,
-                           uint32_t kand, int (*cnt)[kSchedThreads / kWave][16][4], uint32_t& kstar,
-                           uint32_t& istar) {
+__device__ void budget_cut(int n, const Src& src, long long m, long long ncand, uint32_t* red_or,
+                           uint32_t* red_and, int (*cnt)[kSchedThreads / kWave][16][4],
+                           uint32_t& kstar, uint32_t& istar) {
+  constexpr int kSchedWaves = kSchedThreads / kWave;
+  uint32_t kor = 0u, kand = 0xffffffffu;  // candidates' keys are the non-zero ones
+  for (int i = threadIdx.x; i < n; i += kSchedThreads) {
+    const uint32_t key = src(i);
+    kor |= key;
+    kand &= key ? key : 0xffffffffu;
+  }
+  kor = (uint32_t)wave_reduce((int)kor, [](int x, int y) { return x | y; });
+  kand = (uint32_t)wave_reduce((int)kand, [](int x, int y) { return x & y; });
+  if (lane_id() == 0) {
+    red_or[threadIdx.x / kWave] = kor;
+    red_and[threadIdx.x / kWave] = kand;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kSchedWaves; ++w) {
+    kor |= red_or[w];
+    kand &= red_and[w];
+  }
   int pass = 0;  // selects the count buffer
   long long rank = m, bucket = ncand;
   const uint32_t diff = kor ^ kand;
@@ -237,7 +259,6 @@ __global__ void __launch_bounds__(kSchedThreads) k_schedule(ScheduleArgs a) {
   // candidates' keys go to LDS on the way
   int lt_reg[kSchedRegs];
   long long local = 0;
-  uint32_t kor = 0u, kand = 0xffffffffu;  // OR and AND of the candidates' keys
   int bad = 0;
   for (int j = 0, b = tid; b < B; ++j, b += kSchedThreads) {
     const float* __restrict__ cr = a.conf + (size_t)b * K;
@@ -273,11 +294,7 @@ __global__ void __launch_bounds__(kSchedThreads) k_schedule(ScheduleArgs a) {
           go = go && C >= a.tau;
           if (go) ++run;
           // candidate: past the floor and inside the leading run
-          const bool cand = go && k + 1 > ml;
-          const uint32_t key = surv_key(C) + 1u;
-          if (keys_in_lds) s_key[(size_t)b * K + k] = cand ? key : 0u;
-          kor |= cand ? key : 0u;
-          kand &= cand ? key : 0xffffffffu;
+          if (keys_in_lds) s_key[(size_t)b * K + k] = (go && k + 1 > ml) ? surv_key(C) + 1u : 0u;
         }
       }
       if (a.vec4) {
@@ -307,27 +324,14 @@ __global__ void __launch_bounds__(kSchedThreads) k_schedule(ScheduleArgs a) {
       if (jj == j) v = lt_reg[jj];
     return j < kSchedRegs ? v : a.lthr[b];
   };
-  // block sum of Lthr, OR and AND of the candidates' keys (the barrier also
-  // publishes the LDS keys and the stored survival and threshold lengths to
-  // the other threads)
-  // (a thread's sum is at most B*K <= 2^30: int)
+  // block sum of Lthr (the barrier also publishes the LDS keys and the
+  // stored survival and threshold lengths to the other threads; a wave's sum
+  // is at most B*K <= 2^30: int)
   const int wsum = wave_reduce((int)local, [](int x, int y) { return x + y; });
-  const int wor = wave_reduce((int)kor, [](int x, int y) { return x | y; });
-  const int wand = wave_reduce((int)kand, [](int x, int y) { return x & y; });
-  if (lane_id() == 0) {
-    red[tid / kWave] = wsum;
-    red_or[tid / kWave] = (uint32_t)wor;
-    red_and[tid / kWave] = (uint32_t)wand;
-  }
+  if (lane_id() == 0) red[tid / kWave] = wsum;
   __syncthreads();
   long long total = 0;
-  kor = 0u;
-  kand = 0xffffffffu;
-  for (int w = 0; w < kSchedWaves; ++w) {
-    total += red[w];
-    kor |= red_or[w];
-    kand &= red_and[w];
-  }
+  for (int w = 0; w < kSchedWaves; ++w) total += red[w];
 
   const long long floor_all = (long long)B * ml;
   const bool binds = a.budget >= 0 && total > a.budget;
@@ -335,11 +339,11 @@ __global__ void __launch_bounds__(kSchedThreads) k_schedule(ScheduleArgs a) {
   uint32_t kstar = 0xffffffffu, istar = 0u;  // no candidate is taken by default
   if (binds && m > 0) {
     if (keys_in_lds)
-      budget_cut<kSchedThreads>(n, LdsKeys{s_key}, m, total - floor_all, kor, kand, cnt, kstar,
-                                istar);
+      budget_cut<kSchedThreads>(n, LdsKeys{s_key}, m, total - floor_all, red_or, red_and, cnt,
+                                kstar, istar);
     else
-      budget_cut<kSchedThreads>(n, MemKeys{a.surv, a.lthr, K, ml}, m, total - floor_all, kor,
-                                kand, cnt, kstar, istar);
+      budget_cut<kSchedThreads>(n, MemKeys{a.surv, a.lthr, K, ml}, m, total - floor_all, red_or,
+                                red_and, cnt, kstar, istar);
   }
   // lengths and mask, each request by its owner thread
   for (int j = 0, b = tid; b < B; ++j, b += kSchedThreads) {
