@@ -26,6 +26,13 @@ Sources (page title, then section):
   truncate at the first k with C_k < tau; the tutorial code keeps at least one).
 * "DSpark shows why fast AI inference is a scheduling problem, not a model
   trick": the prefix survival probability, truncated below a threshold.
+* Load-aware scheduling: the Guide, "Dynamic Verification Scheduling
+  Algorithm" (load factor from queue depth and GPU memory in use, threshold
+  rising with its square; the code listing's threshold line) and the Deep
+  Dive, "The Throughput Curve", "The Optimization Logic" and "GPU-Resident
+  Scheduling" (a pre-measured curve of tokens/s against tokens per forward
+  pass, kept in GPU memory; a slot is worth adding while its marginal gain
+  covers its cost).
 
 Readings where the pages are silent (each also listed in the design notes):
 the bonus token on full acceptance is drawn from target row L_b; a zero
@@ -58,6 +65,8 @@ DEV_NONFINITE = 2
 DEV_BAD_TEMP = 4
 DEV_BAD_UNIFORM = 8
 DEV_BAD_CONF = 16
+DEV_BAD_LOAD = 64
+DEV_BAD_CURVE = 128
 
 
 def widen(a) -> np.ndarray:
@@ -126,6 +135,92 @@ def schedule(conf, threshold, budget, min_len=1):
             L[b] += 1
     mask = (np.arange(1, K + 1)[None, :] <= L[:, None]).astype(np.uint8)
     return L.astype(np.int32), mask, C
+
+
+# ----------------------------------------------------------------------------
+# Load-aware threshold and throughput-curve budget
+# ----------------------------------------------------------------------------
+
+MAX_CURVE = 64  # curve points the library accepts
+
+
+def load_factor(q, q_max, m, m_max):
+    """Return (LF float32, flags).  LF = 0.6 * Q/Q_max + 0.4 * M/M_max, kept
+    in [0, 1] (Guide, "Dynamic Verification Scheduling Algorithm", step 1:
+    queue depth Q, GPU memory in use M).
+
+    Readings: the computation is fp32 in this order (the two ratios, the two
+    products, the sum), then clamped to [0, 1], which the page states as the
+    range; a queue depth or memory figure that is NaN, infinite or negative is
+    flagged and read as full load (LF = 1, the conservative end)."""
+    f32 = np.float32
+    q, m = f32(q), f32(m)
+    if not (np.isfinite(q) and np.isfinite(m) and q >= 0 and m >= 0):
+        return f32(1.0), DEV_BAD_LOAD
+    lf = f32(0.6) * (q / f32(q_max)) + f32(0.4) * (m / f32(m_max))
+    return f32(min(max(lf, f32(0.0)), f32(1.0))), 0
+
+
+def load_threshold(lf, tau_min, tau_max):
+    """tau = tau_min + (tau_max - tau_min) * LF^2 (Guide, "Dynamic
+    Verification Scheduling Algorithm", step 2; the Guide's code listing has
+    the same form with 0.25 and 0.50).  fp32 in this order: the difference,
+    the square, their product, the sum.  The pages give tau_min as 0.20 in
+    the prose and 0.25 in the code, so both ends are arguments."""
+    f32 = np.float32
+    lf = f32(lf)
+    return f32(f32(tau_min) + (f32(tau_max) - f32(tau_min)) * (lf * lf))
+
+
+def curve_budget(curve, slot_cost, B, min_len):
+    """Return (budget int, flags): the verify-token budget from a throughput
+    curve (Deep Dive, "The Throughput Curve": tokens/s measured at a range of
+    batch sizes; "The Optimization Logic": keep adding tokens while the
+    marginal gain of one more covers its cost).
+
+    ``curve`` is [n, 2]: (x_i tokens per target forward pass, T_i tokens/s),
+    x strictly ascending whole numbers >= 1.  Readings: between x_{i-1} and
+    x_i every added token gains the segment's slope
+    g_i = (T_i - T_{i-1}) / (x_i - x_{i-1}) (fp64); the pass grows up to x_j,
+    where segment j+1 is the first whose gain is below ``slot_cost`` (the last
+    point if none is); a forward pass carries one position per request that
+    is not a drafted token, so the budget on drafted positions is x* - B,
+    floored at B * min_len.  No curve (n = 0) means no budget (-1); a curve
+    that breaks the rules above is flagged and also means no budget."""
+    curve = np.asarray(curve, dtype=np.float32).reshape(-1, 2)
+    n = curve.shape[0]
+    if n == 0:
+        return -1, 0
+    x = curve[:, 0].astype(np.float64)
+    t = curve[:, 1].astype(np.float64)
+    ok = n <= MAX_CURVE and np.all(np.isfinite(x)) and np.all(np.isfinite(t))
+    ok = ok and np.all(x >= 1) and np.all(x <= 2.0 ** 24) and np.all(np.floor(x) == x)
+    ok = ok and np.all(np.diff(x) > 0)
+    if not ok:
+        return -1, DEV_BAD_CURVE
+    cost = float(np.float32(slot_cost))
+    xstar = x[-1]
+    for i in range(1, n):
+        g = (t[i] - t[i - 1]) / (x[i] - x[i - 1])
+        if g < cost:
+            xstar = x[i - 1]
+            break
+    return max(int(B) * int(min_len), int(xstar) - int(B)), 0
+
+
+def schedule_load_aware(conf, load, q_max, m_max, tau_min, tau_max, curve, slot_cost,
+                        min_len=1):
+    """The schedule with its threshold and budget set from the load and the
+    throughput curve (Deep Dive, "GPU-Resident Scheduling": the scheduler
+    reads the confidences and the stored curve and writes one length per
+    request).  Returns (lengths, mask, survival, tau, budget, flags)."""
+    conf = np.asarray(conf, dtype=np.float32)
+    B = conf.shape[0]
+    lf, f1 = load_factor(load[0], q_max, load[1], m_max)
+    tau = load_threshold(lf, tau_min, tau_max)
+    budget, f2 = curve_budget(curve, slot_cost, B, min_len)
+    L, mask, C = schedule(conf, tau, budget, min_len)
+    return L, mask, C, tau, budget, f1 | f2
 
 
 # ----------------------------------------------------------------------------

@@ -445,3 +445,126 @@ def test_nonfinite_row_rules():
     dn[0, 0, 0] = np.nan
     assert oracle.verify(t, dn, y, None, np.zeros(B, np.float32), u)["flags"] == 0
     assert oracle.verify(t, dn, y, None, T, u)["flags"] == oracle.DEV_NONFINITE
+
+
+# ------------------------------------------------- load-aware threshold, budget
+
+CURVE = _load("throughput_curve.json")
+
+
+def test_curve_slopes_reproduce_the_printed_gains():
+    # the page's marginal-gain column for batch sizes 2..32 is the segment
+    # slope rounded to a whole number; 64 and 128 are documented misprints
+    c = np.array(CURVE["curve"], dtype=np.float64)
+    slopes = np.diff(c[:, 1]) / np.diff(c[:, 0])
+    printed = CURVE["printed_marginal_gain"][1:]
+    for i in range(5):
+        assert round(slopes[i] + 1e-9) == printed[i], (i, slopes[i], printed[i])
+    assert slopes[5] == 4.0625 and slopes[6] == 1.09375
+
+
+@pytest.mark.parametrize("case", CURVE["budget_cases"], ids=lambda c: f"cost{c['slot_cost']}")
+def test_curve_budget_page_table(case):
+    budget, flags = oracle.curve_budget(CURVE["curve"], case["slot_cost"], case["B"], case["min_len"])
+    assert flags == 0
+    assert budget == case["budget"]
+    assert budget == max(case["B"] * case["min_len"], case["xstar"] - case["B"])
+
+
+def _token_scan_budget(curve, cost, B, min_len):
+    # one token at a time along the piecewise-linear curve (exact fractions):
+    # the pass grows while the next token's gain covers the cost
+    xs = [Fraction(int(x)) for x, _ in curve]
+    ts = [Fraction(float(t)) for _, t in curve]
+
+    def T(x):
+        for i in range(1, len(xs)):
+            if x <= xs[i]:
+                return ts[i - 1] + (ts[i] - ts[i - 1]) * (x - xs[i - 1]) / (xs[i] - xs[i - 1])
+        return ts[-1]
+    x = xs[0]
+    cost = Fraction(float(np.float32(cost)))
+    while x < xs[-1] and T(x + 1) - T(x) >= cost:
+        x += 1
+    return max(B * min_len, int(x) - B)
+
+
+def test_curve_budget_equals_token_by_token_scan():
+    rng = np.random.default_rng(5)
+    for _ in range(300):
+        n = int(rng.integers(1, 9))
+        xs = np.cumsum(rng.integers(1, 9, size=n)).astype(np.float32)
+        ts = np.cumsum(rng.uniform(-20, 80, size=n)).astype(np.float32)
+        curve = np.stack([xs, ts], axis=1)
+        cost = float(rng.uniform(-10, 60))
+        B, ml = int(rng.integers(1, 6)), int(rng.integers(0, 3))
+        slopes = np.diff(ts.astype(np.float64)) / np.diff(xs.astype(np.float64))
+        if np.any(np.abs(slopes - np.float32(cost)) < 1e-6):
+            continue  # a slope equal to the cost up to rounding: both readings hold
+        got, flags = oracle.curve_budget(curve, cost, B, ml)
+        assert flags == 0
+        assert got == _token_scan_budget(curve, cost, B, ml)
+
+
+def test_curve_budget_monotone_in_cost_and_edge_cases():
+    c = CURVE["curve"]
+    costs = np.linspace(-5, 50, 111)
+    budgets = [oracle.curve_budget(c, k, 4, 1)[0] for k in costs]
+    assert all(a >= b for a, b in zip(budgets, budgets[1:]))
+    assert oracle.curve_budget(np.zeros((0, 2)), 1.0, 4, 1) == (-1, 0)
+    assert oracle.curve_budget([[3, 10]], 1.0, 2, 1) == (2, 0)          # one point: x* = 3, 3 - 2 = 1 < floor 2
+    for bad in ([[2, 10], [2, 20]], [[0, 10]], [[1.5, 10]], [[1, float("nan")]], [[4, 1], [3, 2]]):
+        assert oracle.curve_budget(bad, 1.0, 2, 1) == (-1, oracle.DEV_BAD_CURVE)
+
+
+def test_load_factor_closed_forms():
+    f32 = np.float32
+    assert oracle.load_factor(10, 10, 0, 4) == (f32(0.6), 0)
+    assert oracle.load_factor(0, 10, 4, 4) == (f32(0.4), 0)
+    assert oracle.load_factor(10, 10, 4, 4) == (f32(1.0), 0)
+    assert oracle.load_factor(0, 10, 0, 4) == (f32(0.0), 0)
+    assert oracle.load_factor(25, 10, 4, 4) == (f32(1.0), 0)             # past Q_max: clamped
+    lf, fl = oracle.load_factor(5, 10, 2, 4)
+    assert fl == 0 and abs(float(lf) - 0.5) < 1e-7                        # 0.6 * 0.5 + 0.4 * 0.5
+    for q, m in ((float("nan"), 1.0), (1.0, float("inf")), (-1.0, 0.0)):
+        assert oracle.load_factor(q, 10, m, 4) == (f32(1.0), oracle.DEV_BAD_LOAD)
+
+
+@pytest.mark.parametrize("case", CURVE["threshold_cases"], ids=lambda c: f"lf{c['lf']}-{c['tau_min']}")
+def test_load_threshold_page_values(case):
+    tau = oracle.load_threshold(case["lf"], case["tau_min"], case["tau_max"])
+    assert abs(float(tau) - case["tau"]) <= 1e-7
+
+
+def test_load_threshold_endpoints_and_monotone():
+    f32 = np.float32
+    for lo, hi in ((0.20, 0.75), (0.25, 0.75), (0.0, 1.0), (0.3, 0.3)):
+        assert oracle.load_threshold(0.0, lo, hi) == f32(lo)
+        assert abs(float(oracle.load_threshold(1.0, lo, hi)) - float(f32(hi))) <= float(np.spacing(f32(hi)))
+        taus = [float(oracle.load_threshold(x, lo, hi)) for x in np.linspace(0, 1, 101, dtype=np.float32)]
+        assert all(a <= b for a, b in zip(taus, taus[1:]))
+    # the code listing's 0.25 + 0.50 * LF^2, in exact arithmetic
+    for x in np.linspace(0, 1, 37, dtype=np.float32):
+        exact = 0.25 + 0.5 * float(x) ** 2
+        assert abs(float(oracle.load_threshold(x, 0.25, 0.75)) - exact) <= 2e-7
+
+
+def test_load_aware_schedule_shortens_under_load():
+    # more load -> a higher threshold -> no request verifies more positions
+    rng = np.random.default_rng(9)
+    conf = rng.uniform(0.6, 1.0, size=(12, 8)).astype(np.float32)
+    curve = CURVE["curve"]
+    prev = None
+    for q in np.linspace(0, 10, 11):
+        L, mask, C, tau, budget, flags = oracle.schedule_load_aware(
+            conf, (q, 2.0), 10.0, 8.0, 0.2, 0.75, curve, 0.0, 1)
+        assert flags == 0 and budget == 128 - 12
+        assert np.array_equal(L, oracle.threshold_lengths(C, tau, 1))  # budget 116 never binds here
+        if prev is not None:
+            assert np.all(L <= prev)
+        prev = L
+    # an idle engine (LF = 0) verifies with tau_min, a saturated one with tau_max
+    L0 = oracle.schedule_load_aware(conf, (0, 0), 10, 8, 0.2, 0.75, [], 0.0, 1)
+    L1 = oracle.schedule_load_aware(conf, (10, 8), 10, 8, 0.2, 0.75, [], 0.0, 1)
+    assert float(L0[3]) == np.float32(0.2) and L0[4] == -1
+    assert abs(float(L1[3]) - 0.75) < 1e-7
