@@ -27,8 +27,9 @@ oracle on a bounded sample of the same workload.
 
 ``rows`` times, apart from the step, the hot-path rows the step does not
 exercise: the greedy rule on the same logits, full-length blocks, the
-schedule with a binding budget and a mixed-temperature batch of 1024
-requests (``--no-rows`` skips them).
+schedule with a binding budget, the load-aware schedule (threshold and budget
+from an engine load and a throughput curve) and a mixed-temperature batch of
+1024 requests (``--no-rows`` skips them).
 
 --calibrate-copy N runs, after the timed steps, a plain elementwise copy of
 N MiB (read N MiB, write N MiB) five times: the reference kernel of known size
@@ -121,7 +122,8 @@ def time_calls(fn, reps, stream, torch):
 def row_measurements(ds, workloads, sets, outs, ws_v, dev, stream, torch, np, log):
     """The hot-path rows the headline step does not exercise, each timed
     apart (not part of `value`): the greedy rule, full-length blocks, a
-    binding budget and a mixed-temperature batch of 1024 requests."""
+    binding budget, the load-aware schedule and a mixed-temperature batch of
+    1024 requests."""
     rows = {}
     n = len(sets)
     B, K, V = sets[0].B, sets[0].K, sets[0].V
@@ -219,6 +221,34 @@ def row_measurements(ds, workloads, sets, outs, ws_v, dev, stream, torch, np, lo
     rows["S3_schedule_binding_b1024"] = {"workload": "b1024-k8, threshold 0.3, budget = half the "
                                                      "threshold lengths",
                                          "budget": half, "call_us_median": round(t_med * 1e3, 2)}
+    # the load-aware schedule: threshold and budget derived on the device from
+    # an engine load and the Deep Dive's throughput-curve table, its batch
+    # sizes scaled 8x to tokens per forward pass
+    curve = torch.tensor([[1, 35], [2, 67], [4, 125], [8, 220], [16, 360], [32, 520], [64, 650],
+                          [128, 720]], dtype=torch.float32, device=dev)
+    curve[:, 0] *= 8
+    curve[:, 1] *= 8
+    load = torch.tensor([48.0, 0.7], dtype=torch.float32, device=dev)  # queue 48 of 128, 70 % memory
+    for name, conf_t, Bx, Kx in (("NEXT1_schedule_load_aware_b64", sets[0].conf, B, K),
+                                 ("NEXT1_schedule_load_aware_b1024", w5.conf, B5, K5)):
+        Lx = torch.empty(Bx, dtype=torch.int32, device=dev)
+        mx = torch.empty((Bx, Kx), dtype=torch.uint8, device=dev)
+        cx = torch.empty((Bx, Kx), dtype=torch.float32, device=dev)
+        tx = torch.empty(1, dtype=torch.float32, device=dev)
+        bx = torch.empty(1, dtype=torch.int32, device=dev)
+        sx = torch.zeros(1, dtype=torch.int32, device=dev)
+        wsx = ds.workspace(ds.OP_SCHEDULE, Bx, Kx, 1, dev)
+
+        def sched_la():
+            ds.schedule_load_aware(conf_t, load, 128.0, 1.0, 0.20, 0.75, curve, 2.0, 1,
+                                   lengths=Lx, mask=mx, survival=cx, tau_out=tx, budget_out=bx,
+                                   dev_status=sx, ws=wsx, stream=stream)
+        sched_la()
+        t_med, _ = time_calls(sched_la, 30, stream, torch)
+        rows[name] = {"workload": f"b{Bx}-k{Kx} confidences, load 48/128 queue and 0.7 memory, "
+                                  "tau 0.20..0.75, throughput curve of the Deep Dive x8, slot cost 2",
+                      "tau": round(float(tx.item()), 6), "budget": int(bx.item()),
+                      "lengths_sum": int(Lx.sum().item()), "call_us_median": round(t_med * 1e3, 2)}
     sched5()  # back to the configured lengths for the verify row
     a5 = torch.empty(B5, dtype=torch.int32, device=dev)
     t5 = torch.empty((B5, K5 + 1), dtype=torch.int32, device=dev)

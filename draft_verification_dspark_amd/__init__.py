@@ -6,8 +6,9 @@ device memory and the current stream.  There is no fallback: if the library
 has not been built (``python -m draft_verification_dspark_amd.build`` or
 ``__graft_entry__.build()``), loading raises.
 
-Names follow the C ABI: ``dspark_schedule``, ``dspark_verify``,
-``dspark_verify_greedy``, ``dspark_workspace_bytes``, ``dspark_status_string``.
+Names follow the C ABI: ``dspark_schedule``, ``dspark_schedule_load_aware``,
+``dspark_verify``, ``dspark_verify_greedy``, ``dspark_workspace_bytes``,
+``dspark_status_string``.
 """
 from __future__ import annotations
 
@@ -29,9 +30,13 @@ DEV_BAD_TEMP = 4
 DEV_BAD_UNIFORM = 8
 DEV_BAD_CONF = 16
 DEV_BAD_LENGTH = 32
+DEV_BAD_LOAD = 64
+DEV_BAD_CURVE = 128
+ERR_PARAM = 7
 
 EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_schedule",
-           "dspark_verify", "dspark_verify_greedy", "dspark_set_stream_events")
+           "dspark_schedule_load_aware", "dspark_verify", "dspark_verify_greedy",
+           "dspark_set_stream_events")
 
 
 class DsparkError(RuntimeError):
@@ -58,6 +63,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dspark_status_string.restype = ctypes.c_char_p
     lib.dspark_schedule.argtypes = [vp, i32, i32, f32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.dspark_schedule.restype = i32
+    lib.dspark_schedule_load_aware.argtypes = [vp, i32, i32, vp, f32, f32, f32, f32, vp, i32, f32,
+                                               i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dspark_schedule_load_aware.restype = i32
     lib.dspark_verify.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                   vp, sz, vp]
     lib.dspark_verify.restype = i32
@@ -181,6 +189,45 @@ def schedule(conf, threshold: float, budget: int, min_len: int = 1, *, lengths=N
                              ws.ptr, ws.nbytes, _stream(stream, dev))
     _check(st)
     return lengths, mask, survival, dev_status
+
+
+def schedule_load_aware(conf, load, q_max: float, m_max: float, tau_min: float, tau_max: float,
+                        curve, slot_cost: float, min_len: int = 1, *, lengths=None, mask=None,
+                        survival=None, tau_out=None, budget_out=None, dev_status=None,
+                        ws: Optional[Workspace] = None, stream=None):
+    """dspark_schedule_load_aware on torch tensors (``load`` float32[2] and
+    ``curve`` float32[n, 2] on the device; ``curve=None`` for no budget).
+    Returns (lengths, mask, survival, tau_out, budget_out, dev_status)."""
+    torch = _torch()
+    lib = load_library()
+    dev = conf.device
+    B, K = conf.shape
+    _req(conf, "conf", torch.float32, (B, K), dev)
+    _req(load, "load", torch.float32, (2,), dev)
+    n_curve = 0
+    if curve is not None:
+        n_curve = curve.shape[0]
+        _req(curve, "curve", torch.float32, (n_curve, 2), dev)
+    lengths = torch.empty(B, dtype=torch.int32, device=dev) if lengths is None else \
+        _req(lengths, "lengths", torch.int32, (B,), dev)
+    mask = torch.empty((B, K), dtype=torch.uint8, device=dev) if mask is None else \
+        _req(mask, "mask", torch.uint8, (B, K), dev)
+    survival = torch.empty((B, K), dtype=torch.float32, device=dev) if survival is None else \
+        _req(survival, "survival", torch.float32, (B, K), dev)
+    tau_out = torch.empty(1, dtype=torch.float32, device=dev) if tau_out is None else \
+        _req(tau_out, "tau_out", torch.float32, (1,), dev)
+    budget_out = torch.empty(1, dtype=torch.int32, device=dev) if budget_out is None else \
+        _req(budget_out, "budget_out", torch.int32, (1,), dev)
+    if dev_status is None:
+        dev_status = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = ws or workspace(OP_SCHEDULE, B, K, 1, dev)
+    st = lib.dspark_schedule_load_aware(
+        _ptr(conf), B, K, _ptr(load), float(q_max), float(m_max), float(tau_min), float(tau_max),
+        _ptr(curve) if curve is not None else None, n_curve, float(slot_cost), int(min_len),
+        _ptr(lengths), _ptr(mask), _ptr(survival), _ptr(tau_out), _ptr(budget_out),
+        _ptr(dev_status), ws.ptr, ws.nbytes, _stream(stream, dev))
+    _check(st)
+    return lengths, mask, survival, tau_out, budget_out, dev_status
 
 
 def verify(target, draft, drafted, lengths, temperature, uniforms, *, accepted=None, tokens=None,

@@ -90,13 +90,15 @@ const char* dspark_status_string(int status) {
     case DSPARK_ERR_BUDGET: return "budget below B*min_len or min_len outside [0,K]";
     case DSPARK_ERR_WORKSPACE: return "workspace too small or misaligned";
     case DSPARK_ERR_LAUNCH: return "kernel launch failed";
+    case DSPARK_ERR_PARAM: return "load-aware parameter out of range";
     default: return "unknown status";
   }
 }
 
-int dspark_schedule(const float* conf, int B, int K, float threshold, int budget, int min_len,
-                    int32_t* lengths, uint8_t* mask, float* survival, int32_t* dev_status,
-                    void* workspace, size_t ws_bytes, void* stream) {
+static int schedule_common(ScheduleArgs& a, const float* conf, int B, int K, float threshold,
+                           int budget, int min_len, int32_t* lengths, uint8_t* mask,
+                           float* survival, int32_t* dev_status, void* workspace,
+                           size_t ws_bytes) {
   if (!conf || !lengths || !dev_status || !workspace) return DSPARK_ERR_NULL;
   if (B < 1 || K < 1 || B > kMaxB || (long long)B * K > (1LL << 30)) return DSPARK_ERR_SHAPE;
   if (min_len < 0 || min_len > K) return DSPARK_ERR_BUDGET;
@@ -104,7 +106,7 @@ int dspark_schedule(const float* conf, int B, int K, float threshold, int budget
   const ScheduleLayout L = schedule_layout(B, K);
   if (ws_bytes < L.total || !aligned(workspace, kAlign)) return DSPARK_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
-  ScheduleArgs a;
+  a = ScheduleArgs{};
   a.conf = conf;
   a.B = B;
   a.K = K;
@@ -117,6 +119,47 @@ int dspark_schedule(const float* conf, int B, int K, float threshold, int budget
   a.lthr = reinterpret_cast<int32_t*>(ws + L.lthr);
   a.dev_status = dev_status;
   a.vec4 = (K % 4 == 0) && aligned(conf, 16) && aligned(a.surv, 16);
+  return DSPARK_OK;
+}
+
+int dspark_schedule(const float* conf, int B, int K, float threshold, int budget, int min_len,
+                    int32_t* lengths, uint8_t* mask, float* survival, int32_t* dev_status,
+                    void* workspace, size_t ws_bytes, void* stream) {
+  ScheduleArgs a;
+  const int st = schedule_common(a, conf, B, K, threshold, budget, min_len, lengths, mask,
+                                 survival, dev_status, workspace, ws_bytes);
+  if (st != DSPARK_OK) return st;
+  return launch_schedule(a, static_cast<hipStream_t>(stream));
+}
+
+static bool finite_f(float x) { return x == x && x - x == 0.f; }
+
+int dspark_schedule_load_aware(const float* conf, int B, int K, const float* load, float q_max,
+                               float m_max, float tau_min, float tau_max, const float* curve,
+                               int n_curve, float slot_cost, int min_len, int32_t* lengths,
+                               uint8_t* mask, float* survival, float* tau_out,
+                               int32_t* budget_out, int32_t* dev_status, void* workspace,
+                               size_t ws_bytes, void* stream) {
+  ScheduleArgs a;
+  const int st = schedule_common(a, conf, B, K, 0.f, -1, min_len, lengths, mask, survival,
+                                 dev_status, workspace, ws_bytes);
+  if (st != DSPARK_OK) return st;
+  if (!load) return DSPARK_ERR_NULL;
+  if (!(finite_f(q_max) && q_max > 0.f && finite_f(m_max) && m_max > 0.f)) return DSPARK_ERR_PARAM;
+  if (!(finite_f(tau_min) && finite_f(tau_max) && tau_min >= 0.f && tau_min <= tau_max))
+    return DSPARK_ERR_PARAM;
+  if (n_curve < 0 || n_curve > 64 || (n_curve > 0 && !curve) || !finite_f(slot_cost))
+    return DSPARK_ERR_PARAM;
+  a.load = load;
+  a.q_max = q_max;
+  a.m_max = m_max;
+  a.tau_min = tau_min;
+  a.tau_max = tau_max;
+  a.curve = curve;
+  a.n_curve = n_curve;
+  a.slot_cost = slot_cost;
+  a.tau_out = tau_out;
+  a.budget_out = budget_out;
   return launch_schedule(a, static_cast<hipStream_t>(stream));
 }
 

@@ -29,6 +29,8 @@
 // its first kSchedRegs requests in registers.
 #include <hip/hip_runtime.h>
 
+#include <cfloat>
+
 #include "args.hpp"
 
 namespace dspark {
@@ -240,6 +242,54 @@ __device__ void budget_cut(int n, const Src& src, long long m, long long ncand, 
   }
 }
 
+// Load-aware threshold and budget (DSpark Guide, "Dynamic Verification
+// Scheduling Algorithm", steps 1-2; DSpark Deep Dive, "The Throughput Curve"
+// and "The Optimization Logic"), worked out by every wave on its own, so no
+// barrier is needed: lane i (1 <= i < n) takes the slope of curve segment i
+// and one ballot finds the first segment whose gain is below the slot cost.
+struct LoadDecision {
+  float tau;
+  int budget;
+  int bad;
+};
+
+__device__ LoadDecision load_decision(const ScheduleArgs& a) {
+  LoadDecision d;
+  d.bad = 0;
+  // load factor in fp32: the two ratios, the products, the sum, then [0, 1];
+  // a bad figure reads as full load
+  const float q = a.load[0], m = a.load[1];
+  float lf = 1.f;
+  if (q >= 0.f && m >= 0.f && q <= FLT_MAX && m <= FLT_MAX) {
+    lf = 0.6f * (q / a.q_max) + 0.4f * (m / a.m_max);
+    lf = fminf(fmaxf(lf, 0.f), 1.f);
+  } else {
+    d.bad |= DSPARK_DEV_BAD_LOAD;
+  }
+  d.tau = a.tau_min + (a.tau_max - a.tau_min) * (lf * lf);
+  const int n = a.n_curve;
+  d.budget = -1;
+  if (n == 0) return d;
+  // curve point l and the one before it (lanes past the curve read point 0)
+  const int l = lane_id();
+  const int i = l < n ? l : 0;
+  const int ip = i > 0 ? i - 1 : 0;
+  const float x = a.curve[2 * i], t = a.curve[2 * i + 1];
+  const float xp = a.curve[2 * ip], tp = a.curve[2 * ip + 1];
+  const bool ok = (x >= 1.f && x <= 16777216.f && floorf(x) == x && fabsf(t) <= FLT_MAX &&
+                   (i == 0 || x > xp));
+  if (__ballot(l < n && !ok)) {
+    d.bad |= DSPARK_DEV_BAD_CURVE;
+    return d;
+  }
+  const double g = ((double)t - (double)tp) / ((double)x - (double)xp);
+  const uint64_t drop = __ballot(l >= 1 && l < n && g < (double)a.slot_cost);
+  const int last = drop ? __builtin_ctzll(drop) - 1 : n - 1;  // the last point kept
+  const int xstar = (int)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), last));
+  d.budget = max(a.B * a.min_len, xstar - a.B);
+  return d;
+}
+
 // kSchedThreads threads: 1024, or 256 for small batches (a smaller
 // workgroup starts sooner; one thread per request still covers them)
 template <int kSchedThreads>
@@ -254,6 +304,18 @@ __global__ void __launch_bounds__(kSchedThreads) k_schedule(ScheduleArgs a) {
   const int n = B * K;
   const int ml = a.min_len;
   const bool keys_in_lds = n <= kSchedLds;
+  float tau = a.tau;
+  int budget = a.budget;
+  if (a.load) {
+    const LoadDecision d = load_decision(a);
+    tau = d.tau;
+    budget = d.budget;
+    if (tid == 0) {
+      if (d.bad) flag(a.dev_status, d.bad);
+      if (a.tau_out) *a.tau_out = tau;
+      if (a.budget_out) *a.budget_out = budget;
+    }
+  }
 
   // survival product and threshold length, one thread per request; the
   // candidates' keys go to LDS on the way
@@ -291,7 +353,7 @@ __global__ void __launch_bounds__(kSchedThreads) k_schedule(ScheduleArgs a) {
           if (!(ck[i] >= 0.f && ck[i] <= 1.f)) bad |= DSPARK_DEV_BAD_CONF;
           C = k == 0 ? ck[i] : C * ck[i];
           ck[i] = C;
-          go = go && C >= a.tau;
+          go = go && C >= tau;
           if (go) ++run;
           // candidate: past the floor and inside the leading run
           if (keys_in_lds) s_key[(size_t)b * K + k] = (go && k + 1 > ml) ? surv_key(C) + 1u : 0u;
@@ -334,8 +396,8 @@ __global__ void __launch_bounds__(kSchedThreads) k_schedule(ScheduleArgs a) {
   for (int w = 0; w < kSchedWaves; ++w) total += red[w];
 
   const long long floor_all = (long long)B * ml;
-  const bool binds = a.budget >= 0 && total > a.budget;
-  const long long m = binds ? (long long)a.budget - floor_all : 0;  // free slots, >= 0
+  const bool binds = budget >= 0 && total > budget;
+  const long long m = binds ? (long long)budget - floor_all : 0;  // free slots, >= 0
   uint32_t kstar = 0xffffffffu, istar = 0u;  // no candidate is taken by default
   if (binds && m > 0) {
     if (keys_in_lds)

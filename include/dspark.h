@@ -13,6 +13,9 @@
  *                         draw; requests with temperature 0 use the greedy rule;
  *   dspark_verify_greedy  the greedy (T = 0) rule for the whole batch.
  *
+ * dspark_schedule_load_aware derives the schedule's threshold and budget on
+ * the device from the engine's load and a stored throughput curve.
+ *
  * Sources (page title, then section):
  *   "DSpark Deep Dive: How DeepSeek Squeezed an 85% Speedup Out of Inference
  *    Without Touching a Single Model Weight" — "Speculative Decoding From First
@@ -77,7 +80,8 @@ typedef enum {
   DSPARK_ERR_DTYPE = 3,     /* unknown logits dtype                               */
   DSPARK_ERR_BUDGET = 4,    /* budget >= 0 but < B*min_len, or min_len not in [0,K] */
   DSPARK_ERR_WORKSPACE = 5, /* ws_bytes too small or workspace misaligned         */
-  DSPARK_ERR_LAUNCH = 6     /* the HIP runtime rejected a launch                  */
+  DSPARK_ERR_LAUNCH = 6,    /* the HIP runtime rejected a launch                  */
+  DSPARK_ERR_PARAM = 7      /* a load-aware parameter out of range (see dspark_schedule_load_aware) */
 } dspark_status;
 
 typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
@@ -89,6 +93,8 @@ typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
 #define DSPARK_DEV_BAD_UNIFORM 8  /* a uniform that is read lies outside [0, 1)          */
 #define DSPARK_DEV_BAD_CONF 16    /* a confidence is NaN or outside [0, 1]               */
 #define DSPARK_DEV_BAD_LENGTH 32  /* lengths[b] outside [0, K] (clamped)                 */
+#define DSPARK_DEV_BAD_LOAD 64    /* queue depth or memory in use NaN, infinite or < 0    */
+#define DSPARK_DEV_BAD_CURVE 128  /* throughput curve breaks the rules of dspark_schedule_load_aware */
 
 #define DSPARK_OP_SCHEDULE 0
 #define DSPARK_OP_VERIFY 1
@@ -130,6 +136,51 @@ DSPARK_API const char* dspark_status_string(int status);
 DSPARK_API int dspark_schedule(const float* conf, int B, int K, float threshold, int budget, int min_len,
                     int32_t* lengths, uint8_t* mask, float* survival,
                     int32_t* dev_status, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * dspark_schedule_load_aware — dspark_schedule with its threshold and budget
+ * derived on the device from the engine's load and a stored throughput
+ * curve, with no host round trip.
+ *
+ * Defines (DSpark Guide, "Dynamic Verification Scheduling Algorithm", steps
+ * 1 and 2, and its code listing's threshold line; DSpark Deep Dive, "The
+ * Throughput Curve", "The Optimization Logic", "GPU-Resident Scheduling"):
+ *   LF  = clamp(0.6 * (Q / q_max) + 0.4 * (M / m_max), 0, 1)     fp32, in this order
+ *   tau = tau_min + (tau_max - tau_min) * (LF * LF)               fp32, in this order
+ *   with curve points (x_i tokens per target forward pass, T_i tokens/s),
+ *   g_i = (T_i - T_{i-1}) / (x_i - x_{i-1}) in fp64 for i >= 1;
+ *   x*  = x_{i-1} for the first i with g_i < slot_cost, else x_{n-1};
+ *   budget = max(B * min_len, x* - B)   (one position per request in a
+ *            forward pass is not a drafted token; no curve: budget = -1);
+ *   then exactly dspark_schedule(conf, B, K, tau, budget, min_len, ...).
+ * A queue depth or memory figure that is NaN, infinite or negative sets
+ * DSPARK_DEV_BAD_LOAD and is read as LF = 1. A curve whose x are not whole
+ * numbers in [1, 2^24], strictly ascending, or whose values are not finite,
+ * sets DSPARK_DEV_BAD_CURVE and means no budget. The pages give tau_min as
+ * 0.20 (prose) and 0.25 (code) and tau_max as 0.75; both are arguments.
+ *
+ *   load       device float32[2]: Q (queue depth) and M (GPU memory in use,
+ *              in the unit of m_max), read when the kernel runs
+ *   q_max, m_max   finite, > 0
+ *   tau_min, tau_max   finite, 0 <= tau_min <= tau_max
+ *   curve      device float32[n_curve][2], (x_i, T_i); may be NULL if n_curve == 0
+ *   n_curve    0..64; 0 = no budget
+ *   slot_cost  finite, tokens/s a token must add to be worth its slot
+ *   tau_out    device float32[1] out, the threshold used; may be NULL
+ *   budget_out device int32[1] out, the budget used (-1 = none); may be NULL
+ *   other arguments as for dspark_schedule (same workspace, op
+ *   DSPARK_OP_SCHEDULE).
+ * Errors: as dspark_schedule (NULL conf/lengths/dev_status/workspace/load,
+ * shape, min_len, workspace), and DSPARK_ERR_PARAM for a parameter above out
+ * of range, n_curve outside 0..64, or n_curve > 0 with a NULL curve.
+ */
+DSPARK_API int dspark_schedule_load_aware(const float* conf, int B, int K, const float* load,
+                                          float q_max, float m_max, float tau_min, float tau_max,
+                                          const float* curve, int n_curve, float slot_cost,
+                                          int min_len, int32_t* lengths, uint8_t* mask,
+                                          float* survival, float* tau_out, int32_t* budget_out,
+                                          int32_t* dev_status, void* workspace, size_t ws_bytes,
+                                          void* stream);
 
 /*
  * dspark_verify — lossless block verification.

@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert ds.dspark_status_string(s)
     assert ds.dspark_status_string(99) == "unknown status"
 
@@ -58,6 +58,27 @@ P = 4096  # any 256-aligned non-null "pointer": the checks never dereference it
 ])
 def test_schedule_argument_errors(args, code):
     assert ds.load_library().dspark_schedule(*args) == code
+
+
+def _la(**kw):
+    a = dict(conf=P, B=4, K=4, load=P, qmax=10.0, mmax=8.0, tmin=0.2, tmax=0.75, curve=P, n=8,
+             cost=1.0, ml=1, L=P, mask=None, surv=None, tout=None, bout=None, st=P, ws=P,
+             nb=10 ** 6, stream=None)
+    a.update(kw)
+    return ds.load_library().dspark_schedule_load_aware(
+        a["conf"], a["B"], a["K"], a["load"], a["qmax"], a["mmax"], a["tmin"], a["tmax"], a["curve"],
+        a["n"], a["cost"], a["ml"], a["L"], a["mask"], a["surv"], a["tout"], a["bout"], a["st"],
+        a["ws"], a["nb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(load=None), 1), (dict(conf=None), 1), (dict(B=0), 2), (dict(ml=5), 4), (dict(nb=8), 5),
+    (dict(qmax=0.0), 7), (dict(mmax=-1.0), 7), (dict(qmax=float("inf")), 7),
+    (dict(tmin=0.8), 7), (dict(tmin=-0.1), 7), (dict(tmax=float("nan")), 7),
+    (dict(n=65), 7), (dict(n=-1), 7), (dict(curve=None), 7), (dict(cost=float("nan")), 7),
+])
+def test_schedule_load_aware_argument_errors(kw, code):
+    assert _la(**kw) == code
 
 
 def _v(**kw):

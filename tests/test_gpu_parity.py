@@ -302,6 +302,74 @@ def test_schedule_equal_and_near_keys(B, K):
             compare_schedule((host(g[0]), host(g[1]), host(g[2])), oracle.schedule(conf, 0.5, bud, 1))
 
 
+def _load_aware_case(conf, load, q_max, m_max, tmin, tmax, curve, cost, ml):
+    ct = torch.from_numpy(np.ascontiguousarray(conf, dtype=np.float32)).to(DEV)
+    lt = torch.tensor(load, dtype=torch.float32, device=DEV)
+    cv = None if curve is None or len(curve) == 0 else \
+        torch.tensor(np.asarray(curve, dtype=np.float32).reshape(-1, 2), device=DEV)
+    L, m, s, tau, bud, st = ds.schedule_load_aware(ct, lt, q_max, m_max, tmin, tmax, cv, cost, ml)
+    torch.cuda.synchronize()
+    rL, rm, rs, rtau, rbud, rflags = oracle.schedule_load_aware(
+        conf, load, q_max, m_max, tmin, tmax, [] if curve is None else curve, cost, ml)
+    compare_schedule((host(L), host(m), host(s)), (rL, rm, rs))
+    assert host(tau).view(np.uint32)[0] == np.float32(rtau).view(np.uint32), (host(tau)[0], rtau)
+    assert int(host(bud)[0]) == rbud
+    assert int(host(st)[0]) == rflags
+
+
+PAGE_CURVE = [[1, 35], [2, 67], [4, 125], [8, 220], [16, 360], [32, 520], [64, 650], [128, 720]]
+
+
+@pytest.mark.parametrize("B,K", [(4, 8), (64, 16), (700, 8), (3000, 8)])
+def test_schedule_load_aware_random(B, K):
+    rng = np.random.default_rng(B * 7 + K)
+    for trial in range(12):
+        conf = (rng.uniform(0, 1, size=(B, K)) ** rng.uniform(0.05, 0.6, size=(B, 1))).astype(np.float32)
+        load = [float(rng.uniform(0, 150)), float(rng.uniform(0, 90))]
+        q_max, m_max = float(rng.uniform(1, 120)), float(rng.uniform(1, 80))
+        tmin = float(rng.uniform(0, 0.4))
+        tmax = float(rng.uniform(tmin, 1.0))
+        if trial % 3 == 0:
+            # the page's curve scaled to the batch, costs around its slopes
+            scale = max(1, (B * (K + 1)) // 128)
+            curve = [[x * scale, t * scale] for x, t in PAGE_CURVE]
+            cost = float(rng.choice([0.0, 2.0, 5.0, 10.0, 18.0, 30.0]))
+        elif trial % 3 == 1:
+            n = int(rng.integers(1, 65))
+            xs = np.cumsum(rng.integers(1, max(2, B * K // n + 2), size=n))
+            ts = np.cumsum(rng.uniform(-5, 50, size=n))
+            curve = np.stack([xs, ts], axis=1).tolist()
+            cost = float(rng.uniform(-5, 40))
+        else:
+            curve, cost = None, 0.0
+        ml = int(rng.integers(0, 2))
+        _load_aware_case(conf, load, q_max, m_max, tmin, tmax, curve, cost, ml)
+
+
+def test_schedule_load_aware_threshold_bits():
+    # fp32 threshold from many load figures, bit for bit
+    rng = np.random.default_rng(3)
+    conf = rng.uniform(0.5, 1, size=(8, 4)).astype(np.float32)
+    for _ in range(60):
+        load = [float(rng.uniform(0, 20)), float(rng.uniform(0, 20))]
+        _load_aware_case(conf, load, float(rng.uniform(0.5, 20)), float(rng.uniform(0.5, 20)),
+                         float(rng.uniform(0, 0.5)), float(rng.uniform(0.5, 1)), PAGE_CURVE, 10.0, 1)
+
+
+def test_schedule_load_aware_bad_inputs():
+    rng = np.random.default_rng(4)
+    conf = rng.uniform(0.5, 1, size=(16, 8)).astype(np.float32)
+    for load in ([float("nan"), 1.0], [1.0, float("inf")], [-2.0, 0.0]):
+        _load_aware_case(conf, load, 10.0, 8.0, 0.2, 0.75, PAGE_CURVE, 10.0, 1)
+    for curve in ([[2, 10], [2, 20]], [[0, 10]], [[1.5, 10]], [[1, float("nan")]], [[4, 1], [3, 2]],
+                  [[1, 10], [2, float("inf")]], [[1, 1], [16777218, 2]]):
+        _load_aware_case(conf, [1.0, 1.0], 10.0, 8.0, 0.2, 0.75, curve, 1.0, 1)
+    # one point, floors, and the page's worked budgets
+    _load_aware_case(conf, [0.0, 0.0], 10.0, 8.0, 0.2, 0.75, [[3, 10]], 1.0, 1)
+    for cost in (0.0, 3.0, 10.0, 12.0, 40.0):
+        _load_aware_case(conf[:4], [5.0, 4.0], 10.0, 8.0, 0.25, 0.75, PAGE_CURVE, cost, 1)
+
+
 def test_schedule_golden_and_subnormals():
     import json, os
     with open(os.path.join(os.path.dirname(__file__), "golden", "schedule_cases.json")) as f:
