@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include "args.hpp"
+#include "schedule_args.hpp"
 
 namespace dspark {
 

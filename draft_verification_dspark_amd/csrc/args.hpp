@@ -1,4 +1,4 @@
-// Argument blocks passed by value to the kernels of one call.
+// Argument block of the verify kernels, passed by value.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -7,29 +7,6 @@
 #include "device.hpp"
 
 namespace dspark {
-
-struct ScheduleArgs {
-  const float* conf;   // [B,K]
-  int B, K;
-  float tau;
-  int budget;
-  int min_len;
-  int32_t* lengths;    // [B]
-  uint8_t* mask;       // [B,K] or null
-  float* surv;         // [B,K] survival (the caller's output or workspace)
-  int32_t* lthr;       // [B] workspace
-  int32_t* dev_status;
-  int vec4;            // K % 4 == 0 and conf, surv 16-byte aligned
-  // load-aware mode (non-null `load`): tau and budget above are replaced by
-  // the values derived on the device from these
-  const float* load;   // [2] queue depth, memory in use
-  float q_max, m_max, tau_min, tau_max;
-  const float* curve;  // [n_curve][2] (tokens per forward pass, tokens/s)
-  int n_curve;
-  float slot_cost;
-  float* tau_out;      // [1] or null
-  int32_t* budget_out; // [1] or null
-};
 
 struct VerifyArgs {
   const void* target;  // [B,K+1,V]
@@ -61,6 +38,5 @@ int compute_units();  // of the current device
 // a per-request plan of this many entries in LDS); larger batches run as
 // consecutive sub-batches on the same stream.
 constexpr int kLaunchBatch = 2048;
-int launch_schedule(ScheduleArgs& a, hipStream_t st);
 
 }  // namespace dspark

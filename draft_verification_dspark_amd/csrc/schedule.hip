@@ -31,7 +31,7 @@
 
 #include <cfloat>
 
-#include "args.hpp"
+#include "schedule_args.hpp"
 
 namespace dspark {
 
