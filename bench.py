@@ -49,6 +49,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+SPIN_CYCLES = 20_000_000  # GPU clock cycles the pre-queued spin kernel runs for
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_stream_rows_b64_k16_v151936_pmc.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "draft_verification_dspark_amd", "csrc", f)
                   for f in ("verify.hip", "device.hpp", "args.hpp")]
@@ -105,8 +106,13 @@ def measured_traffic():
 
 
 def time_calls(fn, reps, stream, torch):
-    """Median and mean of `reps` calls of fn(), each between two events."""
+    """Median and mean of `reps` calls of fn(), each between two events.  A
+    spin kernel queued first keeps the GPU busy while the host queues the
+    calls, so that the events time the GPU work, not the host's launch
+    overhead."""
     ts = []
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(SPIN_CYCLES)
     for _ in range(reps):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -139,6 +145,8 @@ def row_measurements(ds, workloads, sets, outs, ws_v, dev, stream, torch, np, lo
             for x in e:
                 x.record(stream)
         torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(SPIN_CYCLES)  # the host queues ahead of the GPU
         for i, (c0, s0, s1, c1) in enumerate(evs):
             c0.record(stream)
             ds.dspark_set_stream_events(s0, s1)
@@ -373,6 +381,8 @@ def main():
         for x in e:
             x.record(stream)           # creates the HIP events
     torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(SPIN_CYCLES)  # the host queues ahead: events time GPU work only
     for i in range(args.steps):
         step(i, stream, ev[i])
     torch.cuda.synchronize()
