@@ -26,6 +26,12 @@ Sources (page title, then section):
   truncate at the first k with C_k < tau; the tutorial code keeps at least one).
 * "DSpark shows why fast AI inference is a scheduling problem, not a model
   trick": the prefix survival probability, truncated below a threshold.
+* Online calibration: the Deep Dive, "Online Calibration" ("Sequential
+  Temperature Scaling": per-position temperature on the logit of the score;
+  "Online Adaptation" and "The Calibration Loop in Practice": per-position
+  mean predicted confidence and acceptance fraction over a window of rounds,
+  temperature += learning rate * (predicted - actual); ECE as the gap between
+  predicted confidence and observed acceptance).
 * Load-aware scheduling: the Guide, "Dynamic Verification Scheduling
   Algorithm" (load factor from queue depth and GPU memory in use, threshold
   rising with its square; the code listing's threshold line) and the Deep
@@ -54,6 +60,8 @@ brute force, textbook special cases, hand-worked fixtures); no function is
 "parity unpinned".
 """
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -221,6 +229,125 @@ def schedule_load_aware(conf, load, q_max, m_max, tau_min, tau_max, curve, slot_
     budget, f2 = curve_budget(curve, slot_cost, B, min_len)
     L, mask, C = schedule(conf, tau, budget, min_len)
     return L, mask, C, tau, budget, f1 | f2
+
+
+# ----------------------------------------------------------------------------
+# Online calibration of the confidences
+# ----------------------------------------------------------------------------
+
+def calibrate(raw, theta):
+    """Return (calibrated float64[B,K], flags): per-position temperature
+    scaling, sigmoid(logit(raw[b,k]) / theta[k]) (Deep Dive, "Online
+    Calibration", "Sequential Temperature Scaling").  fp64.
+
+    Readings: scores 0 and 1 stay 0 and 1 (logit -inf and +inf); a score that
+    is NaN or outside [0, 1] is flagged and passed through unchanged; a
+    temperature that is NaN, infinite or not positive is flagged and that
+    position is passed through unchanged."""
+    raw = np.asarray(raw, dtype=np.float32).astype(np.float64)
+    theta = np.asarray(theta, dtype=np.float32).astype(np.float64)
+    out = raw.copy()
+    flags = 0
+    B, K = raw.shape
+    for k in range(K):
+        t = theta[k]
+        if not (np.isfinite(t) and t > 0):
+            flags |= DEV_BAD_CONF
+            continue
+        for b in range(B):
+            x = raw[b, k]
+            if not (0.0 <= x <= 1.0):
+                flags |= DEV_BAD_CONF
+                continue
+            if x == 0.0 or x == 1.0:
+                continue
+            z = (math.log(x) - math.log1p(-x)) / t
+            out[b, k] = 1.0 / (1.0 + math.exp(-z))
+    return out, flags
+
+
+def evaluated_positions(lengths, accepted, K):
+    """The positions whose accept test ran in a round, and their outcomes:
+    position k (1-based) of request b ran if k <= lengths[b] and
+    k <= accepted[b] + 1 (the test stops at the first rejection; Deep Dive,
+    "Speculative Decoding From First Principles"), and was accepted if
+    k <= accepted[b].  Returns (ran bool[B,K], ok bool[B,K])."""
+    L = np.asarray(lengths).reshape(-1, 1)
+    a = np.asarray(accepted).reshape(-1, 1)
+    k = np.arange(1, K + 1)[None, :]
+    ran = (k <= L) & (k <= a + 1)
+    return ran, ran & (k <= a)
+
+
+class CalibrationWindow:
+    """Per-position window statistics and binned calibration counts, updated
+    once per round (Deep Dive, "The Calibration Loop in Practice": every N
+    rounds, per position, the mean calibrated score and the fraction of
+    tokens accepted over the window; temperature[i] += learning_rate *
+    (predicted - actual)).
+
+    Readings: the window covers the positions whose accept test ran (see
+    ``evaluated_positions``); a position with no such token in the window
+    keeps its temperature; temperatures are floored at ``theta_min`` (the
+    pages give no bound, and the formula needs a positive temperature); ECE
+    is the usual binned expected calibration error over the window's
+    (score, outcome) pairs, bins of equal width on [0, 1], a score s in bin
+    min(floor(s * n_bins), n_bins - 1)."""
+
+    def __init__(self, K, n_bins=10):
+        self.K, self.n_bins = K, n_bins
+        self.reset()
+
+    def reset(self):
+        K, M = self.K, self.n_bins
+        self.rounds = 0
+        self.n = np.zeros(K, dtype=np.int64)        # tokens whose test ran
+        self.acc = np.zeros(K, dtype=np.int64)      # of them accepted
+        self.pred = np.zeros(K, dtype=np.float64)   # sum of their scores
+        self.bn = np.zeros(M, dtype=np.int64)
+        self.bconf = np.zeros(M, dtype=np.float64)
+        self.bacc = np.zeros(M, dtype=np.int64)
+
+    def observe(self, calibrated, lengths, accepted):
+        c = np.asarray(calibrated, dtype=np.float32).astype(np.float64)
+        ran, ok = evaluated_positions(lengths, accepted, self.K)
+        self.n += ran.sum(axis=0)
+        self.acc += ok.sum(axis=0)
+        for k in range(self.K):
+            self.pred[k] += sum(float(c[b, k]) for b in range(c.shape[0]) if ran[b, k])
+        for b, k in zip(*np.nonzero(ran)):
+            m = min(int(math.floor(c[b, k] * self.n_bins)), self.n_bins - 1)
+            self.bn[m] += 1
+            self.bconf[m] += c[b, k]
+            self.bacc[m] += int(ok[b, k])
+        self.rounds += 1
+
+    def ece(self):
+        N = int(self.bn.sum())
+        if N == 0:
+            return 0.0
+        return float(sum(abs(float(self.bacc[m]) - self.bconf[m]) for m in range(self.n_bins)) / N)
+
+    def update(self, theta, lr, theta_min):
+        """The temperature step; returns the new temperatures (float64)."""
+        th = np.asarray(theta, dtype=np.float32).astype(np.float64).copy()
+        for k in range(self.K):
+            if self.n[k] > 0:
+                err = self.pred[k] / self.n[k] - self.acc[k] / self.n[k]
+                th[k] = max(float(np.float32(theta_min)), th[k] + float(np.float32(lr)) * err)
+        return th
+
+
+def calib_observe(win, theta, calibrated, lengths, accepted, lr, theta_min, window):
+    """One round into the window; at the window's end the temperature step,
+    the window's ECE and a fresh window.  Returns (theta, ece or None)."""
+    win.observe(calibrated, lengths, accepted)
+    if win.rounds < window:
+        return np.asarray(theta, dtype=np.float64), None
+    ece = win.ece()
+    th = win.update(theta, lr, theta_min)
+    win.reset()
+    return th, ece
 
 
 # ----------------------------------------------------------------------------

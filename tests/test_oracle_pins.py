@@ -568,3 +568,93 @@ def test_load_aware_schedule_shortens_under_load():
     L1 = oracle.schedule_load_aware(conf, (10, 8), 10, 8, 0.2, 0.75, [], 0.0, 1)
     assert float(L0[3]) == np.float32(0.2) and L0[4] == -1
     assert abs(float(L1[3]) - 0.75) < 1e-7
+
+
+# ------------------------------------------------------------ online calibration
+
+def test_calibrate_closed_forms():
+    # dyadic scores, exact in fp32: logit(x) = ln r with r = x / (1 - x)
+    x = np.array([[0.75, 0.875, 0.5, 0.2, 0.0, 1.0, 0.37]], dtype=np.float32)
+    c, flags = oracle.calibrate(x, [2.0, 0.5, 7.0, 1.0, 3.0, 3.0, 1.0])
+    assert flags == 0
+    assert abs(c[0, 0] - math.sqrt(3.0) / (1.0 + math.sqrt(3.0))) < 1e-15  # r = 3, temperature 2
+    assert abs(c[0, 1] - 49.0 / 50.0) < 1e-15      # r = 7, temperature 1/2: r^2 / (1 + r^2)
+    assert c[0, 2] == 0.5                            # the midpoint is fixed by every temperature
+    assert abs(c[0, 3] - float(np.float32(0.2))) < 1e-15   # temperature 1: the identity
+    assert c[0, 4] == 0.0 and c[0, 5] == 1.0
+    assert abs(c[0, 6] - float(np.float32(0.37))) < 1e-15
+    # symmetry about 1/2, and a higher temperature pulls scores toward 1/2
+    r = np.random.default_rng(1).uniform(0.01, 0.99, size=(50, 1)).astype(np.float32)
+    lo, _ = oracle.calibrate(r, [1.7])
+    hi, _ = oracle.calibrate((1 - r.astype(np.float64)).astype(np.float32), [1.7])
+    assert np.all(np.abs(lo + hi - 1.0) < 1e-7)
+    t2, _ = oracle.calibrate(r, [2.5])
+    assert np.all(np.abs(t2 - 0.5) <= np.abs(lo - 0.5) + 1e-15)
+    _, f = oracle.calibrate(np.array([[0.5, 1.5]], np.float32), [1.0, 1.0])
+    assert f == oracle.DEV_BAD_CONF
+    _, f = oracle.calibrate(np.array([[0.5]], np.float32), [0.0])
+    assert f == oracle.DEV_BAD_CONF
+
+
+def test_evaluated_positions_by_hand():
+    ran, ok = oracle.evaluated_positions([3, 3, 0, 4], [1, 3, 0, 0], 4)
+    assert ran.astype(int).tolist() == [[1, 1, 0, 0], [1, 1, 1, 0], [0, 0, 0, 0], [1, 0, 0, 0]]
+    assert ok.astype(int).tolist() == [[1, 0, 0, 0], [1, 1, 1, 0], [0, 0, 0, 0], [0, 0, 0, 0]]
+
+
+def test_temperature_step_page_example():
+    # Deep Dive, "Online Adaptation": position 5 predicted 0.70 but accepted
+    # 0.55 -> its temperature goes up (by learning rate * 0.15)
+    K = 5
+    win = oracle.CalibrationWindow(K)
+    cal = np.full((20, K), 0.7, dtype=np.float32)
+    lengths = np.full(20, K, dtype=np.int32)
+    # position 5 runs in every request; 11 of 20 accept it
+    accepted = np.array([5] * 11 + [4] * 9, dtype=np.int32)
+    win.observe(cal, lengths, accepted)
+    th = win.update(np.ones(K, np.float32), 0.015625, 0.05)
+    assert abs(th[4] - (1.0 + 0.015625 * (float(np.float32(0.7)) - 0.55))) < 1e-12
+    assert th[4] > 1.0
+    # positions 1-4 ran and were accepted everywhere: underconfident, so down
+    assert np.all(th[:4] < 1.0)
+
+
+def test_ece_by_hand():
+    win = oracle.CalibrationWindow(1, n_bins=10)
+    win.observe(np.full((10, 1), 0.9, np.float32), np.ones(10, np.int32), np.array([1] * 9 + [0]))
+    assert abs(win.ece() - abs(9 - 10 * float(np.float32(0.9))) / 10) < 1e-12   # ~0
+    win.reset()
+    win.observe(np.full((10, 1), 0.9, np.float32), np.ones(10, np.int32), np.array([1] * 7 + [0] * 3))
+    assert abs(win.ece() - 0.2) < 1e-7
+    # two bins: 4 tokens at 0.25 (1 accepted) and 4 at 0.85 (4 accepted)
+    win = oracle.CalibrationWindow(1, n_bins=10)
+    c = np.array([[0.25]] * 4 + [[0.85]] * 4, np.float32)
+    win.observe(c, np.ones(8, np.int32), np.array([1, 0, 0, 0, 1, 1, 1, 1]))
+    exact = (abs(1 - 4 * float(np.float32(0.25))) + abs(4 - 4 * float(np.float32(0.85)))) / 8
+    assert abs(win.ece() - exact) < 1e-12 and abs(exact - 0.075) < 1e-7
+    assert win.bn.tolist() == [0, 0, 4, 0, 0, 0, 0, 0, 4, 0]
+    # the top edge falls in the last bin
+    win = oracle.CalibrationWindow(1, n_bins=4)
+    win.observe(np.array([[1.0]], np.float32), np.ones(1, np.int32), np.ones(1, np.int32))
+    assert win.bn.tolist() == [0, 0, 0, 1] and win.ece() == 0.0
+
+
+def test_online_loop_converges_to_the_true_temperature():
+    # raw scores are overconfident: a token with raw score s is accepted with
+    # probability sigmoid(logit(s) / 1.6); the loop should find ~1.6 and
+    # bring the ECE down (Deep Dive, "Online Adaptation")
+    rng = np.random.default_rng(7)
+    K, B, true_t = 1, 512, 1.6
+    theta = np.ones(K)
+    win = oracle.CalibrationWindow(K)
+    eces = []
+    for w in range(120):
+        for _ in range(8):
+            raw = rng.uniform(0.55, 0.99, size=(B, K)).astype(np.float32)
+            cal, _ = oracle.calibrate(raw, theta.astype(np.float32))
+            p_true, _ = oracle.calibrate(raw, [true_t])
+            acc = (rng.random((B, K)) < p_true).astype(np.int32)[:, 0]
+            theta, ece = oracle.calib_observe(win, theta, cal, np.ones(B, np.int32), acc, 1.0, 0.05, 8)
+        eces.append(ece)
+    assert abs(theta[0] - true_t) < 0.1, theta
+    assert np.mean(eces[:3]) > 0.05 and np.mean(eces[-40:]) < 0.02, (np.mean(eces[:3]), np.mean(eces[-40:]))
