@@ -7,8 +7,9 @@ has not been built (``python -m draft_verification_dspark_amd.build`` or
 ``__graft_entry__.build()``), loading raises.
 
 Names follow the C ABI: ``dspark_schedule``, ``dspark_schedule_load_aware``,
-``dspark_verify``, ``dspark_verify_greedy``, ``dspark_workspace_bytes``,
-``dspark_status_string``.
+``dspark_verify``, ``dspark_verify_greedy``, ``dspark_calibrate``,
+``dspark_calib_observe``, ``dspark_calib_state_bytes``,
+``dspark_workspace_bytes``, ``dspark_status_string``.
 """
 from __future__ import annotations
 
@@ -35,7 +36,8 @@ DEV_BAD_CURVE = 128
 ERR_PARAM = 7
 
 EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_schedule",
-           "dspark_schedule_load_aware", "dspark_verify", "dspark_verify_greedy",
+           "dspark_schedule_load_aware", "dspark_calibrate", "dspark_calib_state_bytes",
+           "dspark_calib_observe", "dspark_verify", "dspark_verify_greedy",
            "dspark_set_stream_events")
 
 
@@ -66,6 +68,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dspark_schedule_load_aware.argtypes = [vp, i32, i32, vp, f32, f32, f32, f32, vp, i32, f32,
                                                i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.dspark_schedule_load_aware.restype = i32
+    lib.dspark_calibrate.argtypes = [vp, vp, i32, i32, vp, vp, vp]
+    lib.dspark_calibrate.restype = i32
+    lib.dspark_calib_state_bytes.argtypes = [i32, i32]
+    lib.dspark_calib_state_bytes.restype = sz
+    lib.dspark_calib_observe.argtypes = [vp, vp, vp, i32, i32, vp, f32, f32, i32, i32, vp, sz, vp,
+                                         vp, vp]
+    lib.dspark_calib_observe.restype = i32
     lib.dspark_verify.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                   vp, sz, vp]
     lib.dspark_verify.restype = i32
@@ -228,6 +237,58 @@ def schedule_load_aware(conf, load, q_max: float, m_max: float, tau_min: float, 
         _ptr(dev_status), ws.ptr, ws.nbytes, _stream(stream, dev))
     _check(st)
     return lengths, mask, survival, tau_out, budget_out, dev_status
+
+
+def calibrate(raw, theta, *, out=None, dev_status=None, stream=None):
+    """dspark_calibrate on torch tensors.  Returns (calibrated, dev_status)."""
+    torch = _torch()
+    lib = load_library()
+    dev = raw.device
+    B, K = raw.shape
+    _req(raw, "raw", torch.float32, (B, K), dev)
+    _req(theta, "theta", torch.float32, (K,), dev)
+    out = torch.empty((B, K), dtype=torch.float32, device=dev) if out is None else \
+        _req(out, "out", torch.float32, (B, K), dev)
+    if dev_status is None:
+        dev_status = torch.zeros(1, dtype=torch.int32, device=dev)
+    _check(lib.dspark_calibrate(_ptr(raw), _ptr(theta), B, K, _ptr(out), _ptr(dev_status),
+                                _stream(stream, dev)))
+    return out, dev_status
+
+
+def calib_state(K: int, n_bins: int, device):
+    """Zero-filled calibration window state (dspark_calib_state_bytes)."""
+    torch = _torch()
+    nbytes = load_library().dspark_calib_state_bytes(int(K), int(n_bins))
+    if nbytes == 0:
+        raise DsparkError(2, "bad sizes for the calibration state")
+    return torch.zeros(nbytes // 8, dtype=torch.int64, device=device)
+
+
+def calib_observe(calibrated, lengths, accepted, theta, lr: float, theta_min: float, window: int,
+                  n_bins: int, state, *, ece_out=None, dev_status=None, stream=None):
+    """dspark_calib_observe on torch tensors (``theta`` is updated in place at
+    each window's end).  Returns (ece_out, dev_status)."""
+    torch = _torch()
+    lib = load_library()
+    dev = calibrated.device
+    B, K = calibrated.shape
+    _req(calibrated, "calibrated", torch.float32, (B, K), dev)
+    if lengths is not None:
+        _req(lengths, "lengths", torch.int32, (B,), dev)
+    _req(accepted, "accepted", torch.int32, (B,), dev)
+    _req(theta, "theta", torch.float32, (K,), dev)
+    if state.device != dev or not state.is_contiguous():
+        raise ValueError("state: expected a contiguous tensor on the same device")
+    ece_out = torch.zeros(1, dtype=torch.float32, device=dev) if ece_out is None else \
+        _req(ece_out, "ece_out", torch.float32, (1,), dev)
+    if dev_status is None:
+        dev_status = torch.zeros(1, dtype=torch.int32, device=dev)
+    _check(lib.dspark_calib_observe(_ptr(calibrated), _ptr(lengths), _ptr(accepted), B, K,
+                                    _ptr(theta), float(lr), float(theta_min), int(window),
+                                    int(n_bins), _ptr(state), state.numel() * state.element_size(),
+                                    _ptr(ece_out), _ptr(dev_status), _stream(stream, dev)))
+    return ece_out, dev_status
 
 
 def verify(target, draft, drafted, lengths, temperature, uniforms, *, accepted=None, tokens=None,

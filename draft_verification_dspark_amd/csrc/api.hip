@@ -4,6 +4,7 @@
 
 #include "args.hpp"
 #include "schedule_args.hpp"
+#include "calib_args.hpp"
 
 namespace dspark {
 
@@ -239,6 +240,53 @@ int dspark_verify_greedy(const void* target_logits, int dtype, int B, int K, int
   return verify_common(target_logits, nullptr, dtype, B, K, V, drafted, lengths, nullptr, nullptr,
                        accepted, tokens, nullptr, nullptr, dev_status, workspace, ws_bytes, stream,
                        1);
+}
+
+int dspark_calibrate(const float* raw, const float* theta, int B, int K, float* calibrated,
+                     int32_t* dev_status, void* stream) {
+  if (!raw || !theta || !calibrated || !dev_status) return DSPARK_ERR_NULL;
+  if (B < 1 || K < 1 || K > kCalibMax || B > kMaxB) return DSPARK_ERR_SHAPE;
+  CalibArgs a{};
+  a.raw = raw;
+  a.theta = const_cast<float*>(theta);
+  a.B = B;
+  a.K = K;
+  a.calibrated_out = calibrated;
+  a.dev_status = dev_status;
+  return launch_calibrate(a, static_cast<hipStream_t>(stream));
+}
+
+size_t dspark_calib_state_bytes(int K, int n_bins) {
+  if (K < 1 || K > kCalibMax || n_bins < 1 || n_bins > kCalibMax) return 0;
+  return sizeof(long long) * (1 + 3 * (size_t)K + 3 * (size_t)n_bins);
+}
+
+int dspark_calib_observe(const float* calibrated, const int32_t* lengths, const int32_t* accepted,
+                         int B, int K, float* theta, float lr, float theta_min, int window,
+                         int n_bins, void* state, size_t state_bytes, float* ece_out,
+                         int32_t* dev_status, void* stream) {
+  if (!calibrated || !accepted || !theta || !state || !dev_status) return DSPARK_ERR_NULL;
+  if (B < 1 || K < 1 || K > kCalibMax || B > kMaxB) return DSPARK_ERR_SHAPE;
+  if (!(finite_f(lr) && finite_f(theta_min) && theta_min > 0.f) || window < 1 || n_bins < 1 ||
+      n_bins > kCalibMax)
+    return DSPARK_ERR_PARAM;
+  if (state_bytes < dspark_calib_state_bytes(K, n_bins) || !aligned(state, 8))
+    return DSPARK_ERR_WORKSPACE;
+  CalibArgs a{};
+  a.calibrated = calibrated;
+  a.lengths = lengths;
+  a.accepted = accepted;
+  a.theta = theta;
+  a.B = B;
+  a.K = K;
+  a.lr = lr;
+  a.theta_min = theta_min;
+  a.window = window;
+  a.n_bins = n_bins;
+  a.state = state;
+  a.ece_out = ece_out;
+  a.dev_status = dev_status;
+  return launch_calib_observe(a, static_cast<hipStream_t>(stream));
 }
 
 int dspark_set_stream_events(void* before, void* after) {

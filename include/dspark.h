@@ -14,7 +14,9 @@
  *   dspark_verify_greedy  the greedy (T = 0) rule for the whole batch.
  *
  * dspark_schedule_load_aware derives the schedule's threshold and budget on
- * the device from the engine's load and a stored throughput curve.
+ * the device from the engine's load and a stored throughput curve;
+ * dspark_calibrate and dspark_calib_observe keep the confidences calibrated
+ * online (per-position temperatures updated from the observed acceptance).
  *
  * Sources (page title, then section):
  *   "DSpark Deep Dive: How DeepSeek Squeezed an 85% Speedup Out of Inference
@@ -181,6 +183,71 @@ DSPARK_API int dspark_schedule_load_aware(const float* conf, int B, int K, const
                                           float* survival, float* tau_out, int32_t* budget_out,
                                           int32_t* dev_status, void* workspace, size_t ws_bytes,
                                           void* stream);
+
+/*
+ * dspark_calibrate — per-position temperature scaling of the confidences.
+ *
+ * Defines (DSpark Deep Dive, "Online Calibration", "Sequential Temperature
+ * Scaling"):  calibrated[b,k] = sigmoid(logit(raw[b,k]) / theta[k]),
+ * computed in fp64 and stored as fp32; scores 0 and 1 stay 0 and 1.
+ *
+ *   raw        [B,K] float32 confidence-head scores, expected in [0,1]
+ *   theta      [K] float32 per-position temperatures, expected finite and > 0
+ *   calibrated [B,K] float32 out (may alias raw)
+ * A score that is NaN or outside [0,1], or a temperature that is NaN,
+ * infinite or not positive, sets DSPARK_DEV_BAD_CONF and the score passes
+ * through unchanged.
+ * Errors: NULL raw/theta/calibrated/dev_status; B < 1, K < 1 or K > 64.
+ */
+DSPARK_API int dspark_calibrate(const float* raw, const float* theta, int B, int K,
+                                float* calibrated, int32_t* dev_status, void* stream);
+
+/* Bytes of calibration window state for K positions and n_bins ECE bins. */
+DSPARK_API size_t dspark_calib_state_bytes(int K, int n_bins);
+
+/*
+ * dspark_calib_observe — one verification round into the calibration window,
+ * and at its end the temperature step (DSpark Deep Dive, "Online
+ * Calibration", "Online Adaptation" and "The Calibration Loop in Practice").
+ *
+ * Per round, for every request b and position k (1-based) whose accept test
+ * ran — k <= lengths[b] and k <= accepted[b] + 1 — the window counts the
+ * token, whether it was accepted (k <= accepted[b]) and its calibrated score,
+ * per position and per score bin (n_bins equal-width bins on [0,1], a score
+ * s in bin min(floor(s * n_bins), n_bins - 1), the product taken in fp64).
+ * When this call completes the window (`window` rounds):
+ *   theta[k] = max(theta_min, theta[k] + lr * (mean score - accepted fraction))
+ *              for every position with a token in the window (fp64, stored fp32);
+ *   *ece_out = sum over bins |accepted - sum of scores| / tokens (expected
+ *              calibration error of the window);
+ *   and the window restarts.
+ *
+ *   calibrated [B,K] float32, the scores the round was scheduled with
+ *   lengths    [B] int32 scheduled lengths (NULL: all K)
+ *   accepted   [B] int32 accepted counts from dspark_verify
+ *   theta      [K] float32 in/out temperatures
+ *   lr, theta_min  finite, theta_min > 0
+ *   window     rounds per window, >= 1
+ *   n_bins     1..64
+ *   state      device memory of dspark_calib_state_bytes(K, n_bins) bytes,
+ *              8-byte aligned, zero-filled before the first call; the
+ *              library keeps it between calls and restarts it at each
+ *              window's end. Layout in 8-byte words: rounds; per position
+ *              tokens[K], accepted[K], score sums[K] (double); per bin
+ *              tokens[n_bins], accepted[n_bins], score sums[n_bins] (double).
+ *   ece_out    [1] float32 out, written at each window's end; may be NULL
+ * Lengths or accepted counts out of range set DSPARK_DEV_BAD_LENGTH (then
+ * clamped), scores outside [0,1] DSPARK_DEV_BAD_CONF. Calls that share a
+ * state must be ordered (one stream).
+ * Errors: NULL calibrated/accepted/theta/state/dev_status; B < 1, K < 1 or
+ * K > 64; DSPARK_ERR_PARAM for lr, theta_min, window or n_bins out of range;
+ * DSPARK_ERR_WORKSPACE for a small or misaligned state.
+ */
+DSPARK_API int dspark_calib_observe(const float* calibrated, const int32_t* lengths,
+                                    const int32_t* accepted, int B, int K, float* theta, float lr,
+                                    float theta_min, int window, int n_bins, void* state,
+                                    size_t state_bytes, float* ece_out, int32_t* dev_status,
+                                    void* stream);
 
 /*
  * dspark_verify — lossless block verification.

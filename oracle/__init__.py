@@ -73,6 +73,7 @@ DEV_NONFINITE = 2
 DEV_BAD_TEMP = 4
 DEV_BAD_UNIFORM = 8
 DEV_BAD_CONF = 16
+DEV_BAD_LENGTH = 32
 DEV_BAD_LOAD = 64
 DEV_BAD_CURVE = 128
 
@@ -309,8 +310,20 @@ class CalibrationWindow:
         self.bacc = np.zeros(M, dtype=np.int64)
 
     def observe(self, calibrated, lengths, accepted):
+        """Add one round; returns the flags: lengths outside [0, K] or
+        accepted counts outside [0, length] (then clamped), scores outside
+        [0, 1]."""
         c = np.asarray(calibrated, dtype=np.float32).astype(np.float64)
-        ran, ok = evaluated_positions(lengths, accepted, self.K)
+        L = np.asarray(lengths, dtype=np.int64)
+        a = np.asarray(accepted, dtype=np.int64)
+        flags = 0
+        if np.any((L < 0) | (L > self.K) | (a < 0) | (a > L)):
+            flags |= DEV_BAD_LENGTH
+        L = np.clip(L, 0, self.K)
+        a = np.clip(a, 0, L)
+        ran, ok = evaluated_positions(L, a, self.K)
+        if np.any(ran & ~((c >= 0) & (c <= 1))):
+            flags |= DEV_BAD_CONF
         self.n += ran.sum(axis=0)
         self.acc += ok.sum(axis=0)
         for k in range(self.K):
@@ -321,6 +334,7 @@ class CalibrationWindow:
             self.bconf[m] += c[b, k]
             self.bacc[m] += int(ok[b, k])
         self.rounds += 1
+        return flags
 
     def ece(self):
         N = int(self.bn.sum())

@@ -81,6 +81,38 @@ def test_schedule_load_aware_argument_errors(kw, code):
     assert _la(**kw) == code
 
 
+@pytest.mark.parametrize("args,code", [
+    ((None, P, 4, 4, P, P, None), 1), ((P, None, 4, 4, P, P, None), 1), ((P, P, 4, 4, None, P, None), 1),
+    ((P, P, 0, 4, P, P, None), 2), ((P, P, 4, 0, P, P, None), 2), ((P, P, 4, 65, P, P, None), 2),
+])
+def test_calibrate_argument_errors(args, code):
+    assert ds.load_library().dspark_calibrate(*args) == code
+
+
+def test_calib_state_bytes():
+    f = ds.load_library().dspark_calib_state_bytes
+    assert f(16, 10) == 8 * (1 + 3 * 16 + 3 * 10)
+    assert f(0, 10) == 0 and f(65, 10) == 0 and f(4, 0) == 0 and f(4, 65) == 0
+
+
+def _obs(**kw):
+    a = dict(c=P, L=None, acc=P, B=4, K=4, th=P, lr=0.01, tmin=0.05, win=10, nb=10, st=P,
+             sb=10 ** 4, ece=None, ds_=P, stream=None)
+    a.update(kw)
+    return ds.load_library().dspark_calib_observe(a["c"], a["L"], a["acc"], a["B"], a["K"], a["th"],
+                                                  a["lr"], a["tmin"], a["win"], a["nb"], a["st"],
+                                                  a["sb"], a["ece"], a["ds_"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(c=None), 1), (dict(acc=None), 1), (dict(th=None), 1), (dict(st=None), 1), (dict(ds_=None), 1),
+    (dict(B=0), 2), (dict(K=65), 2), (dict(lr=float("nan")), 7), (dict(tmin=0.0), 7),
+    (dict(win=0), 7), (dict(nb=0), 7), (dict(nb=65), 7), (dict(sb=8), 5), (dict(st=P + 4), 5),
+])
+def test_calib_observe_argument_errors(kw, code):
+    assert _obs(**kw) == code
+
+
 def _v(**kw):
     a = dict(t=P, d=P, dtype=1, B=2, K=4, V=100, y=P, L=None, T=P, u=P, acc=P, tok=P, pt=None,
              qt=None, st=P, ws=P, nb=10 ** 9, stream=None)

@@ -542,3 +542,117 @@ def test_stream_events_bracket_the_streaming_pass():
     torch.cuda.synchronize()
     for k in ("accepted", "tokens", "p_tok", "q_tok"):
         assert torch.equal(out[k], ref[k]), k
+
+
+# ---------------------------------------------------------------- calibration
+
+def _ulps(a, b):
+    a = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
+    b = np.asarray(b, np.float32).view(np.int32).astype(np.int64)
+    return np.abs(a - b)
+
+
+@pytest.mark.parametrize("B,K", [(1, 1), (64, 16), (1024, 8), (333, 64)])
+def test_calibrate_parity(B, K):
+    rng = np.random.default_rng(B + 3 * K)
+    raw = rng.uniform(0, 1, size=(B, K)).astype(np.float32)
+    raw[rng.random((B, K)) < 0.05] = 0.0
+    raw[rng.random((B, K)) < 0.05] = 1.0
+    raw[rng.random((B, K)) < 0.05] = np.float32(1e-30)
+    raw[rng.random((B, K)) < 0.05] = np.float32(1 - 2 ** -24)
+    theta = rng.uniform(0.3, 3.0, size=K).astype(np.float32)
+    out, st = ds.calibrate(torch.from_numpy(raw).to(DEV), torch.from_numpy(theta).to(DEV))
+    torch.cuda.synchronize()
+    ref, flags = oracle.calibrate(raw, theta)
+    u = _ulps(host(out), ref.astype(np.float32))
+    assert u.max() <= 1, u.max()
+    assert (u == 0).mean() >= 0.99
+    assert int(host(st)[0]) == flags == 0
+
+
+def test_calibrate_bad_inputs():
+    raw = np.array([[0.5, 1.5, float("nan"), 0.25]], np.float32)
+    for theta in ([1.0, 1.0, 1.0, 1.0], [0.0, 1.0, 1.0, -1.0], [float("inf"), 1.0, 1.0, 2.0]):
+        th = np.array(theta, np.float32)
+        out, st = ds.calibrate(torch.from_numpy(raw).to(DEV), torch.from_numpy(th).to(DEV))
+        torch.cuda.synchronize()
+        ref, flags = oracle.calibrate(raw, th)
+        assert int(host(st)[0]) == flags == oracle.DEV_BAD_CONF
+        ok = np.isfinite(ref)
+        assert np.all(_ulps(host(out)[ok], ref[ok].astype(np.float32)) <= 1)
+
+
+def _window_state(st, K, M):
+    w = host(st).view(np.int64)
+    n, acc = w[1:1 + K], w[1 + K:1 + 2 * K]
+    pred = w[1 + 2 * K:1 + 3 * K].view(np.float64)
+    bn, bacc = w[1 + 3 * K:1 + 3 * K + M], w[1 + 3 * K + M:1 + 3 * K + 2 * M]
+    bconf = w[1 + 3 * K + 2 * M:1 + 3 * K + 3 * M].view(np.float64)
+    return int(w[0]), n, acc, pred, bn, bacc, bconf
+
+
+@pytest.mark.parametrize("B,K,M,window", [(64, 16, 10, 3), (1024, 8, 15, 2), (5, 64, 64, 4)])
+def test_calib_observe_parity(B, K, M, window):
+    rng = np.random.default_rng(B * K + M)
+    theta = torch.from_numpy(rng.uniform(0.5, 2.0, size=K).astype(np.float32)).to(DEV)
+    th_ref = host(theta).astype(np.float64)
+    state = ds.calib_state(K, M, DEV)
+    win = oracle.CalibrationWindow(K, M)
+    for r in range(2 * window + 1):
+        cal = rng.uniform(0, 1, size=(B, K)).astype(np.float32)
+        cal[rng.random((B, K)) < 0.02] = 1.0
+        L = rng.integers(0, K + 1, size=B).astype(np.int32)
+        acc = np.array([rng.integers(0, l + 1) for l in L], np.int32)
+        ece, st = ds.calib_observe(torch.from_numpy(cal).to(DEV), torch.from_numpy(L).to(DEV),
+                                   torch.from_numpy(acc).to(DEV), theta, 0.05, 0.1, window, M, state)
+        torch.cuda.synchronize()
+        th_ref, ece_ref = oracle.calib_observe(win, th_ref, cal, L, acc, 0.05, 0.1, window)
+        assert int(host(st)[0]) == 0
+        assert np.all(_ulps(host(theta), th_ref.astype(np.float32)) <= 1), (host(theta), th_ref)
+        if ece_ref is not None:
+            assert abs(float(host(ece)[0]) - ece_ref) <= 1e-6 * max(ece_ref, 1e-3)
+        rounds, n, a, pred, bn, bacc, bconf = _window_state(state, K, M)
+        assert rounds == win.rounds
+        assert np.array_equal(n, win.n) and np.array_equal(a, win.acc)
+        assert np.array_equal(bn, win.bn) and np.array_equal(bacc, win.bacc)
+        assert np.allclose(pred, win.pred, rtol=1e-12, atol=1e-12)
+        assert np.allclose(bconf, win.bconf, rtol=1e-12, atol=1e-12)
+
+
+def test_calib_observe_flags_and_lengths_default():
+    K, M = 4, 10
+    state = ds.calib_state(K, M, DEV)
+    theta = torch.ones(K, dtype=torch.float32, device=DEV)
+    cal = torch.full((3, K), 0.5, dtype=torch.float32, device=DEV)
+    bad = torch.tensor([1, 5, -1], dtype=torch.int32, device=DEV)       # 5 > K and -1
+    _, st = ds.calib_observe(cal, None, bad, theta, 0.01, 0.1, 100, M, state)
+    torch.cuda.synchronize()
+    assert int(host(st)[0]) == oracle.DEV_BAD_LENGTH
+    win = oracle.CalibrationWindow(K, M)
+    assert win.observe(host(cal), np.full(3, K), host(bad)) == oracle.DEV_BAD_LENGTH
+    rounds, n, a, *_ = _window_state(state, K, M)
+    assert rounds == 1 and np.array_equal(n, win.n) and np.array_equal(a, win.acc)
+
+
+def test_online_loop_on_gpu_tracks_the_oracle():
+    # the whole loop: calibrate, outcomes drawn from the true (less
+    # confident) acceptance law, observe; the temperatures follow the oracle's
+    rng = np.random.default_rng(11)
+    B, K, M, window, true_t = 256, 4, 10, 4, np.array([1.0, 1.3, 1.6, 2.0])
+    theta = torch.ones(K, dtype=torch.float32, device=DEV)
+    th_ref = np.ones(K)
+    state = ds.calib_state(K, M, DEV)
+    win = oracle.CalibrationWindow(K, M)
+    for r in range(24 * window):
+        raw = rng.uniform(0.55, 0.99, size=(B, K)).astype(np.float32)
+        p_true, _ = oracle.calibrate(raw, true_t.astype(np.float32))
+        ok = rng.random((B, K)) < p_true
+        acc = np.where(ok.all(axis=1), K, np.argmin(ok, axis=1)).astype(np.int32)  # first rejection
+        cal, _ = ds.calibrate(torch.from_numpy(raw).to(DEV), theta)
+        ds.calib_observe(cal, None, torch.from_numpy(acc).to(DEV), theta, 1.0, 0.05, window, M, state)
+        cal_ref, _ = oracle.calibrate(raw, th_ref.astype(np.float32))
+        th_ref, _ = oracle.calib_observe(win, th_ref, cal_ref, np.full(B, K), acc, 1.0, 0.05, window)
+        th_ref = th_ref.astype(np.float32).astype(np.float64)   # the library keeps fp32 temperatures
+    torch.cuda.synchronize()
+    assert np.all(np.abs(host(theta) - th_ref) <= 1e-5), (host(theta), th_ref)
+    assert np.all(np.abs(host(theta)[1:] - 1.0) > 0.05)   # the later positions moved
