@@ -28,8 +28,9 @@ oracle on a bounded sample of the same workload.
 ``rows`` times, apart from the step, the hot-path rows the step does not
 exercise: the greedy rule on the same logits, full-length blocks, the
 schedule with a binding budget, the load-aware schedule (threshold and budget
-from an engine load and a throughput curve) and a mixed-temperature batch of
-1024 requests (``--no-rows`` skips them).
+from an engine load and a throughput curve), online calibration (temperature
+scaling and one round into the calibration window) and a mixed-temperature
+batch of 1024 requests (``--no-rows`` skips them).
 
 --calibrate-copy N runs, after the timed steps, a plain elementwise copy of
 N MiB (read N MiB, write N MiB) five times: the reference kernel of known size
@@ -128,8 +129,8 @@ def time_calls(fn, reps, stream, torch):
 def row_measurements(ds, workloads, sets, outs, ws_v, dev, stream, torch, np, log):
     """The hot-path rows the headline step does not exercise, each timed
     apart (not part of `value`): the greedy rule, full-length blocks, a
-    binding budget, the load-aware schedule and a mixed-temperature batch of
-    1024 requests."""
+    binding budget, the load-aware schedule, online calibration and a
+    mixed-temperature batch of 1024 requests."""
     rows = {}
     n = len(sets)
     B, K, V = sets[0].B, sets[0].K, sets[0].V
@@ -257,6 +258,33 @@ def row_measurements(ds, workloads, sets, outs, ws_v, dev, stream, torch, np, lo
                                   "tau 0.20..0.75, throughput curve of the Deep Dive x8, slot cost 2",
                       "tau": round(float(tx.item()), 6), "budget": int(bx.item()),
                       "lengths_sum": int(Lx.sum().item()), "call_us_median": round(t_med * 1e3, 2)}
+    # online calibration: temperature scaling of the raw scores, and one
+    # round into the calibration window (every 4th call ends a window)
+    for name, conf_t, Bx, Kx, acc_t in (("NEXT2_calibration_b64", sets[0].conf, B, K, outs[0]["acc"]),
+                                       ("NEXT2_calibration_b1024", w5.conf, B5, K5, None)):
+        th = torch.linspace(1.0, 1.5, Kx, dtype=torch.float32, device=dev)
+        calx = torch.empty((Bx, Kx), dtype=torch.float32, device=dev)
+        sx = torch.zeros(1, dtype=torch.int32, device=dev)
+        state = ds.calib_state(Kx, 10, dev)
+        ece = torch.zeros(1, dtype=torch.float32, device=dev)
+        accx = acc_t if acc_t is not None else torch.zeros(Bx, dtype=torch.int32, device=dev)
+        Lx = outs[0]["lengths"] if acc_t is not None else torch.full((Bx,), Kx, dtype=torch.int32,
+                                                                      device=dev)
+
+        def cal_call():
+            ds.calibrate(conf_t, th, out=calx, dev_status=sx, stream=stream)
+
+        def obs_call():
+            ds.calib_observe(calx, Lx, accx, th, 0.01, 0.05, 4, 10, state, ece_out=ece,
+                             dev_status=sx, stream=stream)
+        cal_call()
+        obs_call()
+        t_cal, _ = time_calls(cal_call, 30, stream, torch)
+        t_obs, _ = time_calls(obs_call, 32, stream, torch)
+        rows[name] = {"workload": f"b{Bx}-k{Kx} scores, 10 ECE bins, window 4 rounds",
+                      "calibrate_us_median": round(t_cal * 1e3, 2),
+                      "observe_us_median": round(t_obs * 1e3, 2),
+                      "call_us_median": round((t_cal + t_obs) * 1e3, 2)}
     sched5()  # back to the configured lengths for the verify row
     a5 = torch.empty(B5, dtype=torch.int32, device=dev)
     t5 = torch.empty((B5, K5 + 1), dtype=torch.int32, device=dev)
