@@ -26,6 +26,11 @@ Sources (page title, then section):
   truncate at the first k with C_k < tau; the tutorial code keeps at least one).
 * "DSpark shows why fast AI inference is a scheduling problem, not a model
   trick": the prefix survival probability, truncated below a threshold.
+* Markov logit-bias drafting: the Guide, the Markov logit-bias head (the
+  corrected logits of position k are the parallel logits plus
+  U . V[y_{k-1}]^T, U and V both vocabulary x rank) and its code listing
+  (the bias is scaled by a learnable scalar; the first position's previous
+  token is the last target token; positions are drafted in order).
 * Online calibration: the Deep Dive, "Online Calibration" ("Sequential
   Temperature Scaling": per-position temperature on the logit of the score;
   "Online Adaptation" and "The Calibration Loop in Practice": per-position
@@ -230,6 +235,83 @@ def schedule_load_aware(conf, load, q_max, m_max, tau_min, tau_max, curve, slot_
     budget, f2 = curve_budget(curve, slot_cost, B, min_len)
     L, mask, C = schedule(conf, tau, budget, min_len)
     return L, mask, C, tau, budget, f1 | f2
+
+
+# ----------------------------------------------------------------------------
+# Markov logit-bias drafting
+# ----------------------------------------------------------------------------
+
+def bf16_round(x32) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16), round to nearest even; NaN stays
+    a quiet NaN."""
+    x = np.asarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    nan = np.isnan(np.asarray(x32, dtype=np.float32))
+    r = ((x + 0x7FFF + ((x >> 16) & 1)) >> 16).astype(np.uint16)
+    return np.where(nan, np.uint16(0x7FC0), r)
+
+
+def markov_bias(U64, V64, prev):
+    """bias[v] = sum_j U[v, j] * Vm[prev, j] (Guide, the Markov logit-bias
+    head: U . V[y_{k-1}]^T), U and Vm already widened to fp64; one matrix-
+    vector product.  Products of bf16 values are exact in fp64; the sum is
+    exact too whenever the terms are multiples of a common power of two
+    within 53 bits of each other, as for the fixed-point test weights."""
+    return U64 @ V64[int(prev)]
+
+
+def markov_draft(base, U, Vm, scale, y0, temperature, uniforms, requests=None):
+    """Semi-autoregressive drafting with the Markov logit bias (Guide, the
+    Markov logit-bias head and the drafting loop of its code listing).
+
+    base [B, K, V] parallel logits (bf16 as uint16, or float32); U, Vm
+    [V, r] bf16 (uint16); scale the listing's scalar on the bias; y0 [B] the
+    token before the block (the last target token); temperature [B]; uniforms
+    [B, K].  For k = 1..K, in order:
+      corrected_k = base_k + scale * U . Vm[y_{k-1}]   stored in the base dtype
+      y_k = the inverse-CDF draw at uniforms[b, k-1] from softmax(corrected_k / T)
+            (T = 0: the lowest-index maximum)
+    Readings: the bias is a sum in fp32 (here its exact value, then one
+    rounding; the two agree whenever that sum is exact in fp32, which the
+    fixed-point test weights ensure), scaled and added to the widened base
+    logit in fp32, and stored rounded to nearest even; the draw uses the
+    stored logits, so that the draft distribution is exactly the one the
+    verifier reads back; the listing's greedy/top-p choice is read as the
+    verifier's own rule: sampling at the request's temperature, greedy at
+    T = 0.  Returns (corrected like base, drafted int32[B,K], q float64[B,K],
+    boundary float64[B,K]: distance of each draw from a decision edge, inf
+    for greedy; q is 1 for greedy draws).  ``requests`` limits the work to
+    those rows (the others are left zero)."""
+    base = np.asarray(base)
+    B, K, V = base.shape
+    bf = base.dtype == np.uint16
+    f32 = np.float32
+    corrected = np.empty_like(base)
+    drafted = np.zeros((B, K), dtype=np.int32)
+    q = np.zeros((B, K))
+    dist = np.full((B, K), np.inf)
+    U64, V64 = widen(U), widen(Vm)
+    for b in (range(B) if requests is None else requests):
+        prev = int(y0[b])
+        T = float(np.float32(temperature[b]))
+        for k in range(K):
+            bias32 = markov_bias(U64, V64, prev).astype(np.float32)
+            row32 = widen(base[b, k]).astype(np.float32)
+            c32 = (row32 + (f32(scale) * bias32).astype(np.float32)).astype(np.float32)
+            stored = bf16_round(c32) if bf else c32
+            corrected[b, k] = stored
+            x = widen(stored)
+            if T == 0.0:
+                y = int(np.argmax(x))
+                qy = 1.0
+            else:
+                p = softmax_T(x, T)
+                y, d = inverse_cdf(p, float(np.float32(uniforms[b, k])))
+                qy = float(p[y])
+                dist[b, k] = d
+            drafted[b, k] = y
+            q[b, k] = qy
+            prev = y
+    return corrected, drafted, q, dist
 
 
 # ----------------------------------------------------------------------------

@@ -658,3 +658,108 @@ def test_online_loop_converges_to_the_true_temperature():
         eces.append(ece)
     assert abs(theta[0] - true_t) < 0.1, theta
     assert np.mean(eces[:3]) > 0.05 and np.mean(eces[-40:]) < 0.02, (np.mean(eces[:3]), np.mean(eces[-40:]))
+
+
+# ------------------------------------------------------ Markov logit-bias draft
+
+def _fixed_point(rng, shape):
+    # multiples of 2^-8 in [-1, 1]: bf16-exact, and every sum of up to 256
+    # products is exact in fp32
+    return oracle.bf16_round((rng.integers(-256, 257, size=shape) / 256.0).astype(np.float32))
+
+
+def test_bf16_round_against_exact_rounding():
+    rng = np.random.default_rng(2)
+    x = (rng.normal(size=4000) * 10.0 ** rng.integers(-3, 4, size=4000)).astype(np.float32)
+    x[:4] = [1.00390625, 1.005859375, 1.01171875, -1.00390625]    # ties go to even
+    got = oracle.widen(oracle.bf16_round(x))
+    for v, g in zip(x.astype(np.float64), got):
+        # the two bf16 neighbours of v, and the nearest (even on a tie)
+        m, e = math.frexp(v)
+        step = 2.0 ** (e - 8)
+        lo = math.floor(v / step) * step
+        hi = lo + step
+        want = lo if (v - lo < hi - v or (v - lo == hi - v and int(round(lo / step)) % 2 == 0)) else hi
+        assert g == want, (v, g, want)
+
+
+def test_markov_bias_is_the_exact_sum():
+    rng = np.random.default_rng(3)
+    for fixed in (True, False):
+        U = _fixed_point(rng, (40, 32)) if fixed else oracle.bf16_round(rng.normal(size=(40, 32)).astype(np.float32))
+        Vm = _fixed_point(rng, (40, 32)) if fixed else oracle.bf16_round(rng.normal(size=(40, 32)).astype(np.float32))
+        U64, V64 = oracle.widen(U), oracle.widen(Vm)
+        for prev in (0, 7, 39):
+            got = oracle.markov_bias(U64, V64, prev)
+            exact = np.array([math.fsum(U64[v] * V64[prev]) for v in range(40)])
+            if fixed:
+                assert np.array_equal(got, exact)
+            else:
+                assert np.allclose(got, exact, rtol=1e-12, atol=1e-12)
+
+
+def test_markov_zero_scale_is_plain_sampling():
+    rng = np.random.default_rng(4)
+    B, K, V, r = 3, 4, 60, 16
+    base = oracle.bf16_round(rng.normal(size=(B, K, V)).astype(np.float32) * 3)
+    U, Vm = _fixed_point(rng, (V, r)), _fixed_point(rng, (V, r))
+    u = rng.random((B, K)).astype(np.float32)
+    T = np.array([1.0, 0.7, 1.3], np.float32)
+    c, y, q, _ = oracle.markov_draft(base, U, Vm, 0.0, [1, 2, 3], T, u)
+    assert np.array_equal(c, base)
+    for b in range(B):
+        for k in range(K):
+            p = scipy.special.softmax(oracle.widen(base[b, k]) / float(T[b]))
+            want = int(np.searchsorted(np.cumsum(p), float(u[b, k]) * np.sum(p), side="right"))
+            assert y[b, k] == want and abs(q[b, k] - p[want]) < 1e-12
+
+
+def test_markov_one_hot_rows_give_a_column_bias():
+    # Vm rows one-hot: the bias of the previous token t is the column U[:, j(t)]
+    rng = np.random.default_rng(5)
+    V, r, K = 48, 16, 6
+    j_of = rng.integers(0, r, size=V)
+    Vm = np.zeros((V, r), np.float32)
+    Vm[np.arange(V), j_of] = 1.0
+    Vm = oracle.bf16_round(Vm)
+    U = _fixed_point(rng, (V, r))
+    base = oracle.bf16_round(rng.normal(size=(1, K, V)).astype(np.float32))
+    s = 0.75
+    c, y, q, _ = oracle.markov_draft(base, U, Vm, s, [5], np.zeros(1, np.float32), np.zeros((1, K), np.float32))
+    prev = 5
+    Uw = oracle.widen(U)
+    for k in range(K):
+        row = oracle.widen(base[0, k]).astype(np.float32) + np.float32(s) * Uw[:, j_of[prev]].astype(np.float32)
+        want = oracle.bf16_round(row.astype(np.float32))
+        assert np.array_equal(c[0, k], want)
+        assert y[0, k] == int(np.argmax(oracle.widen(want)))      # greedy: first maximum
+        prev = y[0, k]
+
+
+def test_markov_bias_depends_on_the_previous_token_only():
+    rng = np.random.default_rng(6)
+    V, r, K = 40, 16, 3
+    U, Vm = _fixed_point(rng, (V, r)), _fixed_point(rng, (V, r))
+    base = np.repeat(oracle.bf16_round(rng.normal(size=(1, K, V)).astype(np.float32)), 2, axis=0)
+    c, y, _, _ = oracle.markov_draft(base, U, Vm, 1.0, [9, 9], np.zeros(2, np.float32), np.zeros((2, K), np.float32))
+    assert np.array_equal(c[0], c[1]) and np.array_equal(y[0], y[1])
+    c2, y2, _, _ = oracle.markov_draft(base[:1, 1:], U, Vm, 1.0, [int(y[0, 0])], np.zeros(1, np.float32),
+                                       np.zeros((1, K - 1), np.float32))
+    # the block restarted after its first token reproduces the rest of the block
+    assert np.array_equal(c2[0], c[0, 1:]) and np.array_equal(y2[0], y[0, 1:])
+
+
+def test_markov_draws_follow_the_corrected_softmax():
+    # stratified uniforms: the draw frequencies equal softmax(corrected) to 1/N
+    rng = np.random.default_rng(8)
+    V, r, N = 12, 16, 2048
+    U, Vm = _fixed_point(rng, (V, r)), _fixed_point(rng, (V, r))
+    base = oracle.bf16_round(rng.normal(size=(1, 1, V)).astype(np.float32))
+    counts = np.zeros(V)
+    for i in range(N):
+        _, y, _, _ = oracle.markov_draft(base, U, Vm, 2.0, [3], np.ones(1, np.float32),
+                                         np.array([[(i + 0.5) / N]], np.float32))
+        counts[y[0, 0]] += 1
+    c, _, _, _ = oracle.markov_draft(base, U, Vm, 2.0, [3], np.ones(1, np.float32), np.zeros((1, 1), np.float32))
+    p = scipy.special.softmax(oracle.widen(c[0, 0]))
+    assert np.all(np.abs(counts / N - p) <= 1.0 / N + 1e-9)
