@@ -8,7 +8,7 @@ has not been built (``python -m draft_verification_dspark_amd.build`` or
 
 Names follow the C ABI: ``dspark_schedule``, ``dspark_schedule_load_aware``,
 ``dspark_verify``, ``dspark_verify_greedy``, ``dspark_calibrate``,
-``dspark_calib_observe``, ``dspark_calib_state_bytes``,
+``dspark_calib_observe``, ``dspark_calib_state_bytes``, ``dspark_markov_draft``,
 ``dspark_workspace_bytes``, ``dspark_status_string``.
 """
 from __future__ import annotations
@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(HERE, "libdspark.so")
 DSPARK_OK = 0
 DSPARK_F32 = 0
 DSPARK_BF16 = 1
-OP_SCHEDULE, OP_VERIFY, OP_VERIFY_GREEDY = 0, 1, 2
+OP_SCHEDULE, OP_VERIFY, OP_VERIFY_GREEDY, OP_MARKOV_DRAFT = 0, 1, 2, 3
 
 DEV_BAD_TOKEN = 1
 DEV_NONFINITE = 2
@@ -37,7 +37,7 @@ ERR_PARAM = 7
 
 EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_schedule",
            "dspark_schedule_load_aware", "dspark_calibrate", "dspark_calib_state_bytes",
-           "dspark_calib_observe", "dspark_verify", "dspark_verify_greedy",
+           "dspark_calib_observe", "dspark_markov_draft", "dspark_verify", "dspark_verify_greedy",
            "dspark_set_stream_events")
 
 
@@ -75,6 +75,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dspark_calib_observe.argtypes = [vp, vp, vp, i32, i32, vp, f32, f32, i32, i32, vp, sz, vp,
                                          vp, vp]
     lib.dspark_calib_observe.restype = i32
+    lib.dspark_markov_draft.argtypes = [vp, i32, i32, i32, i32, vp, vp, i32, f32, vp, vp, vp, vp, vp,
+                                        vp, vp, vp, sz, vp]
+    lib.dspark_markov_draft.restype = i32
     lib.dspark_verify.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                   vp, sz, vp]
     lib.dspark_verify.restype = i32
@@ -289,6 +292,39 @@ def calib_observe(calibrated, lengths, accepted, theta, lr: float, theta_min: fl
                                     int(n_bins), _ptr(state), state.numel() * state.element_size(),
                                     _ptr(ece_out), _ptr(dev_status), _stream(stream, dev)))
     return ece_out, dev_status
+
+
+def markov_draft(base, U, Vm, scale: float, y0, temperature, uniforms, *, corrected=None,
+                 drafted=None, q_tok=None, dev_status=None, ws: Optional[Workspace] = None,
+                 stream=None):
+    """dspark_markov_draft on torch tensors (``U``, ``Vm``: [V, r] bfloat16).
+    Returns (corrected, drafted, q_tok, dev_status)."""
+    torch = _torch()
+    lib = load_library()
+    dev = base.device
+    B, K, V = base.shape
+    code = _dtype_code(base)
+    _req(base, "base", base.dtype, (B, K, V), dev)
+    r = U.shape[1]
+    _req(U, "U", torch.bfloat16, (V, r), dev)
+    _req(Vm, "Vm", torch.bfloat16, (V, r), dev)
+    _req(y0, "y0", torch.int32, (B,), dev)
+    _req(temperature, "temperature", torch.float32, (B,), dev)
+    _req(uniforms, "uniforms", torch.float32, (B, K), dev)
+    corrected = torch.empty_like(base) if corrected is None else \
+        _req(corrected, "corrected", base.dtype, (B, K, V), dev)
+    drafted = torch.empty((B, K), dtype=torch.int32, device=dev) if drafted is None else \
+        _req(drafted, "drafted", torch.int32, (B, K), dev)
+    q_tok = torch.empty((B, K), dtype=torch.float32, device=dev) if q_tok is None else \
+        _req(q_tok, "q_tok", torch.float32, (B, K), dev)
+    if dev_status is None:
+        dev_status = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = ws or workspace(OP_MARKOV_DRAFT, B, K, V, dev)
+    _check(lib.dspark_markov_draft(_ptr(base), code, B, K, V, _ptr(U), _ptr(Vm), r, float(scale),
+                                   _ptr(y0), _ptr(temperature), _ptr(uniforms), _ptr(corrected),
+                                   _ptr(drafted), _ptr(q_tok), _ptr(dev_status), ws.ptr, ws.nbytes,
+                                   _stream(stream, dev)))
+    return corrected, drafted, q_tok, dev_status
 
 
 def verify(target, draft, drafted, lengths, temperature, uniforms, *, accepted=None, tokens=None,

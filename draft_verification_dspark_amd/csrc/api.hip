@@ -5,6 +5,7 @@
 #include "args.hpp"
 #include "schedule_args.hpp"
 #include "calib_args.hpp"
+#include "markov_args.hpp"
 
 namespace dspark {
 
@@ -76,6 +77,11 @@ extern "C" {
 size_t dspark_workspace_bytes(int op, int B, int K, int V) {
   if (B < 1 || K < 1 || B > kMaxB) return 0;
   if (op == DSPARK_OP_SCHEDULE) return schedule_layout(B, K).total;
+  if (op == DSPARK_OP_MARKOV_DRAFT) {
+    if (V < 1) return 0;
+    const size_t tiles = ((size_t)V + kMarkovRows - 1) / kMarkovRows;
+    return up(sizeof(Partial) * (size_t)B * tiles);
+  }
   if (op == DSPARK_OP_VERIFY || op == DSPARK_OP_VERIFY_GREEDY) {
     if (V < 1 || K > kMaxK) return 0;
     return verify_layout(B, K, V).total;
@@ -287,6 +293,44 @@ int dspark_calib_observe(const float* calibrated, const int32_t* lengths, const 
   a.ece_out = ece_out;
   a.dev_status = dev_status;
   return launch_calib_observe(a, static_cast<hipStream_t>(stream));
+}
+
+int dspark_markov_draft(const void* base, int dtype, int B, int K, int V, const uint16_t* U,
+                        const uint16_t* Vm, int r, float scale, const int32_t* y0,
+                        const float* temperature, const float* uniforms, void* corrected,
+                        int32_t* drafted, float* q_tok, int32_t* dev_status, void* workspace,
+                        size_t ws_bytes, void* stream) {
+  if (!base || !U || !Vm || !y0 || !temperature || !uniforms || !corrected || !drafted ||
+      !dev_status || !workspace)
+    return DSPARK_ERR_NULL;
+  if (B < 1 || K < 1 || V < 1 || B > kMaxB || V > (1 << 30) ||
+      (long long)B * ((V + kMarkovRows - 1) / kMarkovRows) > (1LL << 31))
+    return DSPARK_ERR_SHAPE;
+  if (r < 16 || r > kMarkovMaxRank || r % 16 != 0) return DSPARK_ERR_SHAPE;
+  if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return DSPARK_ERR_DTYPE;
+  if (!aligned(U, 16) || !aligned(Vm, 16)) return DSPARK_ERR_PARAM;
+  if (ws_bytes < dspark_workspace_bytes(DSPARK_OP_MARKOV_DRAFT, B, K, V) ||
+      !aligned(workspace, kAlign))
+    return DSPARK_ERR_WORKSPACE;
+  MarkovArgs a{};
+  a.base = base;
+  a.U = U;
+  a.Vm = Vm;
+  a.r = r;
+  a.scale = scale;
+  a.y0 = y0;
+  a.temperature = temperature;
+  a.uniforms = uniforms;
+  a.corrected = corrected;
+  a.drafted = drafted;
+  a.q_tok = q_tok;
+  a.dev_status = dev_status;
+  a.part = static_cast<Partial*>(workspace);
+  a.B = B;
+  a.K = K;
+  a.V = V;
+  a.tiles = (V + kMarkovRows - 1) / kMarkovRows;
+  return launch_markov(a, dtype, static_cast<hipStream_t>(stream));
 }
 
 int dspark_set_stream_events(void* before, void* after) {

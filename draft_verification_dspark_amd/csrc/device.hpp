@@ -223,6 +223,11 @@ __device__ __forceinline__ double wave_incl_scan(double v) {
   return v + add;
 }
 
+// Exact power-of-two rescaling between integer shifts (a difference below
+// -2000, -inf included, scales to 0).
+__device__ __forceinline__ int shift_amount(float d) { return d < -2000.f ? -2000 : (int)d; }
+
+
 // ---------------------------------------------------------------- loads
 
 // One work item: kUnroll 16-byte vectors per lane.  Lane l, vector v covers
@@ -463,6 +468,12 @@ __device__ __forceinline__ double exp2_f64(double a) {
   p = fma(p, t, 1.0);
   const double r = ldexp(p, (int)n);
   return a > -2000.0 ? r : 0.0;
+}
+
+// p(x) = 2^(x*c - kmax) / S in fp64, for a row summarised as (kmax, S).
+__device__ __forceinline__ double row_prob(float x, float c, float kmax, double S) {
+  if (!(S > 0.0)) return 0.0;
+  return exp2_f64((double)x * (double)c - (double)kmax) / S;
 }
 
 __device__ __forceinline__ void flag(int32_t* st, int bits) {

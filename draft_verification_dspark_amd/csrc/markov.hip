@@ -1,0 +1,405 @@
+// Semi-autoregressive drafting with the Markov logit bias (DSpark Guide, the
+// Markov logit-bias head and its code listing): for positions k = 1..K in
+// order,
+//   corrected[b,k] = base[b,k] + scale * U . Vm[y_{k-1}]^T   (U, Vm: V x r)
+//   y_k ~ softmax(corrected[b,k] / T_b)  (inverse CDF at uniforms[b,k-1];
+//         the lowest-index maximum at T = 0),  y_0 = the last target token.
+// Two launches per position:
+//   k_markov_bias  an MFMA contraction: a workgroup takes 64 vocabulary rows
+//                  of U and the previous tokens' rows of Vm for 64 requests
+//                  (staged in LDS), four waves of 16 rows each run
+//                  v_mfma_f32_16x16x16_bf16 over the rank, and the epilogue
+//                  adds the scaled bias to the base logits, stores the
+//                  corrected logits in the base dtype and summarises the
+//                  tile per request (integer shift k = ceil(max * c) and the
+//                  sum of 2^(x*c - k) over the stored values, or (max, lowest
+//                  index) at T = 0);
+//   k_markov_draw  one workgroup per request: merges the tile summaries
+//                  (exact power-of-two rescaling), finds the tile holding
+//                  u * S by a scan over contiguous runs of tiles, and the
+//                  token inside it by a wave scan of its 64 stored logits.
+// The bias is an fp32 sum (MFMA accumulation), scaled and added in fp32,
+// and the draw reads the stored logits, so the draft distribution is exactly
+// what the verifier reads back.
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+
+#include "markov_args.hpp"
+
+namespace dspark {
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+namespace {
+
+__device__ __forceinline__ float temp_c(float T) {
+  return (float)(1.4426950408889634 / (double)T);  // log2(e) / T, as the verifier
+}
+
+// previous token of request b before position a.step (checked)
+__device__ __forceinline__ int prev_token(const MarkovArgs& a, int b, int& bad) {
+  const int y = a.step == 1 ? a.y0[b] : a.drafted[(size_t)b * a.K + a.step - 2];
+  if (y < 0 || y >= a.V) {
+    bad |= DSPARK_DEV_BAD_TOKEN;
+    return 0;
+  }
+  return y;
+}
+
+// round to the storage dtype (bf16: nearest even) and back
+template <int DT>
+__device__ __forceinline__ float store_elem(void* row, int v, float x) {
+  if constexpr (DT == DSPARK_BF16) {
+    const uint32_t u = __float_as_uint(x);
+    uint16_t h;
+    if (x != x) h = 0x7fc0;
+    else h = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    static_cast<uint16_t*>(row)[v] = h;
+    return __uint_as_float((uint32_t)h << 16);
+  } else {
+    static_cast<float*>(row)[v] = x;
+    return x;
+  }
+}
+
+}  // namespace
+
+template <int DT>
+__global__ void __launch_bounds__(256) k_markov_bias(MarkovArgs a) {
+  constexpr int kLds = kMarkovMaxRank + 8;  // padded row of a staged Vm row (bf16)
+  __shared__ __align__(16) uint16_t s_w[kMarkovBatch][kLds];
+  __shared__ Partial s_p[4][kMarkovBatch];
+  const int tile = blockIdx.x;
+  const int b0 = blockIdx.y * kMarkovBatch;
+  const int w = threadIdx.x / kWave, l = lane_id();
+  const int r = a.r, rq = r / 4;  // rank entries per lane quarter
+  const int K = a.K, V = a.V, k = a.step;
+  int bad = 0;
+
+  // the previous tokens' rows of Vm, 16 bytes at a time (zero rows past B)
+  const int pieces = r / 8;
+  for (int e = threadIdx.x; e < kMarkovBatch * pieces; e += 256) {
+    const int i = e / pieces, piece = e - i * pieces;
+    const int b = b0 + i;
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (b < a.B) {
+      const int prev = prev_token(a, b, bad);
+      v = *reinterpret_cast<const uint4*>(a.Vm + (size_t)prev * r + piece * 8);
+    }
+    *reinterpret_cast<uint4*>(&s_w[i][piece * 8]) = v;
+  }
+  // this lane's row of U (rows past V re-read row V-1 and are dropped) and
+  // its quarter q of the rank: entries q*r/4 .. (q+1)*r/4 - 1
+  const int row0 = tile * kMarkovRows + w * 16;
+  const int q = l >> 4;
+  const int vrow = min(row0 + (l & 15), V - 1);
+  uint32_t areg[kMarkovMaxRank / 8];
+  const uint16_t* up = a.U + (size_t)vrow * r + q * rq;
+#pragma unroll
+  for (int i = 0; i < kMarkovMaxRank / 32; ++i) {
+    if (i * 8 < rq) {
+      const uint4 v = *reinterpret_cast<const uint4*>(up + i * 8);
+      areg[4 * i] = v.x;
+      areg[4 * i + 1] = v.y;
+      areg[4 * i + 2] = v.z;
+      areg[4 * i + 3] = v.w;
+    } else {
+      areg[4 * i] = areg[4 * i + 1] = areg[4 * i + 2] = areg[4 * i + 3] = 0u;
+    }
+  }
+  __syncthreads();
+  // D[row][request] = sum over the rank of U[row][j] * Vm[prev][j]; MFMA step
+  // ks takes rank entries q*r/4 + 4*ks + (0..3) in lane quarter q for A and B
+  float4_t acc[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) acc[nb] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < kMarkovMaxRank / 16; ++ks) {
+    if (ks * 4 < rq) {
+      short4_t av;
+      av[0] = (short)(areg[2 * ks] & 0xffffu);
+      av[1] = (short)(areg[2 * ks] >> 16);
+      av[2] = (short)(areg[2 * ks + 1] & 0xffffu);
+      av[3] = (short)(areg[2 * ks + 1] >> 16);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const short4_t bv = *reinterpret_cast<const short4_t*>(&s_w[nb * 16 + (l & 15)][q * rq + 4 * ks]);
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, acc[nb], 0, 0, 0);
+      }
+    }
+  }
+  // epilogue: lane l holds rows row0 + 4q + j (j = 0..3) of request
+  // b0 + 16 nb + (l & 15)
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int b = b0 + nb * 16 + (l & 15);
+    const bool bok = b < a.B;
+    const int bb = bok ? b : b0;
+    const float T = a.temperature[bb];
+    const bool greedy = T == 0.f;
+    const float c = greedy ? 0.f : temp_c(T);
+    const size_t roff = ((size_t)bb * K + (k - 1)) * (size_t)V;
+    const void* brow = static_cast<const char*>(a.base) + roff * Elem<DT>::kBytes;
+    void* crow = static_cast<char*>(a.corrected) + roff * Elem<DT>::kBytes;
+    float xs[4];
+    bool ok[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int v = row0 + 4 * q + j;
+      ok[j] = bok && v < V;
+      const float x = load_elem<DT>(brow, ok[j] ? v : 0) + a.scale * acc[nb][j];
+      xs[j] = ok[j] ? store_elem<DT>(crow, v, x) : -INFINITY;
+    }
+    // this wave's 16 rows per request: lanes l, l^16, l^32, l^48 share it
+    float m = fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3]));
+    int mi = 0x7fffffff;
+#pragma unroll
+    for (int j = 3; j >= 0; --j)
+      if (ok[j] && xs[j] == m) mi = row0 + 4 * q + j;
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    if (xs[0] != xs[0] || xs[1] != xs[1] || xs[2] != xs[2] || xs[3] != xs[3] || m == INFINITY)
+      bad |= DSPARK_DEV_NONFINITE;
+    Partial pt;
+    if (greedy) {
+      // lowest row holding the maximum
+      int cand = 0x7fffffff;
+#pragma unroll
+      for (int j = 3; j >= 0; --j)
+        if (ok[j] && xs[j] == m) cand = row0 + 4 * q + j;
+      cand = min(cand, __shfl_xor(cand, 16));
+      cand = min(cand, __shfl_xor(cand, 32));
+      pt.k = m;
+      pt.idx = cand;
+      pt.s = 0.0;
+    } else {
+      const bool none = m == -INFINITY;
+      const float kk = ceilf(m * c);
+      const float nk = none ? 0.f : -kk;
+      float s4 = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s4 += ok[j] ? fast_exp2(fmaf(xs[j], c, nk)) : 0.f;
+      double s = (double)s4;
+      s += __shfl_xor(s, 16);
+      s += __shfl_xor(s, 32);
+      pt.k = none ? -INFINITY : kk;
+      pt.idx = 0;
+      pt.s = s;
+    }
+    (void)mi;
+    if (q == 0) s_p[w][nb * 16 + (l & 15)] = pt;
+  }
+  if (bad) flag(a.dev_status, bad);
+  __syncthreads();
+  // the tile's summary per request: the four waves merged by wave 0
+  if (w == 0) {
+    const int b = b0 + l;
+    if (b < a.B) {
+      const bool greedy = a.temperature[b] == 0.f;
+      Partial out;
+      if (greedy) {
+        out = s_p[0][l];
+#pragma unroll
+        for (int ww = 1; ww < 4; ++ww) {
+          const Partial p = s_p[ww][l];
+          if (p.k > out.k || (p.k == out.k && p.idx < out.idx)) out = p;
+        }
+      } else {
+        float km = s_p[0][l].k;
+#pragma unroll
+        for (int ww = 1; ww < 4; ++ww) km = fmaxf(km, s_p[ww][l].k);
+        double s = 0.0;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+          const Partial p = s_p[ww][l];
+          s += p.s > 0.0 ? ldexp(p.s, shift_amount(p.k - km)) : 0.0;
+        }
+        out.k = km;
+        out.idx = 0;
+        out.s = s;
+      }
+      a.part[(size_t)b * a.tiles + tile] = out;
+    }
+  }
+}
+
+// block-wide helpers of k_markov_draw (256 threads, 4 waves)
+struct DrawLds {
+  double w[4];
+  float f[4];
+  int i[4];
+  int tile, found;
+  double base;
+};
+
+template <int DT>
+__global__ void __launch_bounds__(256) k_markov_draw(MarkovArgs a) {
+  __shared__ DrawLds sh;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
+  const int K = a.K, V = a.V, k = a.step, nt = a.tiles;
+  const Partial* pr = a.part + (size_t)b * nt;
+  const float T = a.temperature[b];
+  const size_t roff = ((size_t)b * K + (k - 1)) * (size_t)V;
+  const void* crow = static_cast<const char*>(a.corrected) + roff * Elem<DT>::kBytes;
+  int y = 0;
+  double qy = 1.0;
+  if (!(T >= 0.f)) {
+    if (tid == 0) flag(a.dev_status, DSPARK_DEV_BAD_TEMP);
+  } else if (T == 0.f) {
+    // the lowest-index maximum over the tiles (tiles in index order)
+    float m = -INFINITY;
+    int mi = 0x7fffffff;
+    for (int t = tid; t < nt; t += 256) {
+      const Partial p = pr[t];
+      if (p.k > m || (p.k == m && p.idx < mi)) {
+        m = p.k;
+        mi = p.idx;
+      }
+    }
+    // wave, then block
+    for (int o = 32; o > 0; o >>= 1) {
+      const float om = __shfl_xor(m, o);
+      const int oi = __shfl_xor(mi, o);
+      if (om > m || (om == m && oi < mi)) {
+        m = om;
+        mi = oi;
+      }
+    }
+    if (l == 0) {
+      sh.f[w] = m;
+      sh.i[w] = mi;
+    }
+    __syncthreads();
+    m = sh.f[0];
+    mi = sh.i[0];
+    for (int ww = 1; ww < 4; ++ww)
+      if (sh.f[ww] > m || (sh.f[ww] == m && sh.i[ww] < mi)) {
+        m = sh.f[ww];
+        mi = sh.i[ww];
+      }
+    y = mi < V ? mi : 0;
+  } else {
+    const float c = temp_c(T);
+    const double u = (double)a.uniforms[(size_t)b * K + (k - 1)];
+    // shift of the row: the largest tile shift
+    float km = -INFINITY;
+    for (int t = tid; t < nt; t += 256) km = fmaxf(km, pr[t].k);
+    km = wave_max(km);
+    if (l == 0) sh.f[w] = km;
+    __syncthreads();
+    km = fmaxf(fmaxf(sh.f[0], sh.f[1]), fmaxf(sh.f[2], sh.f[3]));
+    // each thread owns a contiguous run of tiles; its mass, then a block scan
+    const int per = (nt + 255) / 256;
+    const int t0 = min(tid * per, nt), t1 = min(t0 + per, nt);
+    auto mass = [&](int t) -> double {
+      const Partial p = pr[t];
+      return p.s > 0.0 ? ldexp(p.s, shift_amount(p.k - km)) : 0.0;
+    };
+    double own = 0.0;
+    int lastpos = -1;
+    for (int t = t0; t < t1; ++t) {
+      const double mt = mass(t);
+      own += mt;
+      if (mt > 0.0) lastpos = t;
+    }
+    const double incl = wave_incl_scan(own);
+    const int lastw = wave_max_i(lastpos);
+    if (l == kWave - 1) {
+      sh.w[w] = incl;
+      sh.i[w] = lastw;
+    }
+    __syncthreads();
+    double pre = 0.0, S = 0.0;
+    int last = -1;
+    for (int ww = 0; ww < 4; ++ww) {
+      if (ww < w) pre += sh.w[ww];
+      S += sh.w[ww];
+      last = max(last, sh.i[ww]);
+    }
+    const double target = u * S;
+    // a run's bounds: the previous lane's inclusive sum and its own, so that
+    // consecutive runs meet exactly and one run holds the target
+    double excl = __shfl_up(incl, 1);
+    if (l == 0) excl = 0.0;
+    const double before_me = pre + excl;
+    const double after_me = pre + incl;
+    const bool mine = own > 0.0 && after_me > target && before_me <= target;
+    if (tid == 0) {
+      sh.tile = last;  // rounding left no crossing: the last tile with mass
+      sh.base = -1.0;
+    }
+    __syncthreads();
+    if (mine) {
+      // first tile of this run whose running mass passes the target
+      double run = before_me;
+      int tt = -1;
+      double tb = 0.0;
+      for (int t = t0; t < t1 && tt < 0; ++t) {
+        const double mt = mass(t);
+        if (mt > 0.0 && run + mt > target) {
+          tt = t;
+          tb = run;
+        }
+        run += mt;
+      }
+      if (tt >= 0) {
+        sh.tile = tt;
+        sh.base = tb;
+      }
+    }
+    __syncthreads();
+    const int tile = max(sh.tile, 0);
+    const double base = sh.base;
+    // the tile's 64 tokens, one per lane of wave 0
+    if (w == 0) {
+      const Partial p = pr[tile];
+      const int v = tile * kMarkovRows + l;
+      const float x = v < V ? load_elem<DT>(crow, v) : -INFINITY;
+      const double m = v < V ? ldexp((double)fast_exp2(fmaf(x, c, p.k == -INFINITY ? 0.f : -p.k)),
+                                     shift_amount(p.k - km))
+                             : 0.0;
+      const double inc = wave_incl_scan(m);
+      const bool past = base < 0.0;  // no crossing: the last token with mass
+      const uint64_t hit = __ballot(!past && m > 0.0 && base + inc > target);
+      const int lastm = wave_max_i(m > 0.0 ? l : -1);
+      const int pick = hit ? __builtin_ctzll(hit) : (lastm >= 0 ? lastm : 0);
+      const float xp = __shfl(x, pick);
+      y = tile * kMarkovRows + pick;
+      qy = row_prob(xp, c, km, S);
+      if (l == 0) sh.found = y;
+    }
+    __syncthreads();
+    y = sh.found;
+    qy = 0.0;
+    if (w == 0) {
+      // (recomputed in wave 0 for the stored probability)
+      const float xp = load_elem<DT>(crow, min(y, V - 1));
+      qy = row_prob(xp, c, km, S);
+    }
+  }
+  if (tid == 0) {
+    a.drafted[(size_t)b * K + (k - 1)] = y;
+    if (a.q_tok) a.q_tok[(size_t)b * K + (k - 1)] = (float)qy;
+  }
+}
+
+template <int DT>
+static int launch_markov_t(MarkovArgs& a, hipStream_t st) {
+  const dim3 gb((unsigned)a.tiles, (unsigned)((a.B + kMarkovBatch - 1) / kMarkovBatch));
+  for (int k = 1; k <= a.K; ++k) {
+    a.step = k;
+    hipLaunchKernelGGL(k_markov_bias<DT>, gb, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_markov_draw<DT>, dim3((unsigned)a.B), dim3(256), 0, st, a);
+  }
+  return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_ERR_LAUNCH;
+}
+
+int launch_markov(MarkovArgs& a, int dtype, hipStream_t st) {
+  return dtype == DSPARK_BF16 ? launch_markov_t<DSPARK_BF16>(a, st)
+                              : launch_markov_t<DSPARK_F32>(a, st);
+}
+
+}  // namespace dspark

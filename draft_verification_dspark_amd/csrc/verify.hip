@@ -363,7 +363,6 @@ __global__ void __launch_bounds__(kStreamBlock) k_stream_rows(VerifyArgs a) {
 
 // ------------------------------------------------------------------ merges
 
-__device__ __forceinline__ int shift_amount(float d) { return d < -2000.f ? -2000 : (int)d; }
 
 // Chunk summaries of one row folded into a merged row, wave-cooperatively.
 // Each lane folds the chunks c = lane, lane + 64, ... (the first one passed
@@ -462,10 +461,6 @@ __device__ RowSum merge_argmax16(const Partial* p, int G, int sub) {
 }
 
 // probability of logit x under a merged row: 2^(x*c - K*) / S, in fp64
-__device__ __forceinline__ double row_prob(float x, float c, float kmax, double S) {
-  if (!(S > 0.0)) return 0.0;
-  return exp2_f64((double)x * (double)c - (double)kmax) / S;
-}
 
 // Residual p - q of one row pair at fp32 speed, with the elements whose
 // normalised p or q reaches 2^-12 redone in fp64 (their fp32 rounding would

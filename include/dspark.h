@@ -16,7 +16,8 @@
  * dspark_schedule_load_aware derives the schedule's threshold and budget on
  * the device from the engine's load and a stored throughput curve;
  * dspark_calibrate and dspark_calib_observe keep the confidences calibrated
- * online (per-position temperatures updated from the observed acceptance).
+ * online (per-position temperatures updated from the observed acceptance);
+ * dspark_markov_draft drafts a block with the Markov logit bias.
  *
  * Sources (page title, then section):
  *   "DSpark Deep Dive: How DeepSeek Squeezed an 85% Speedup Out of Inference
@@ -101,6 +102,7 @@ typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
 #define DSPARK_OP_SCHEDULE 0
 #define DSPARK_OP_VERIFY 1
 #define DSPARK_OP_VERIFY_GREEDY 2
+#define DSPARK_OP_MARKOV_DRAFT 3
 
 /* Bytes of workspace `op` needs for these sizes (0 for bad sizes). */
 DSPARK_API size_t dspark_workspace_bytes(int op, int B, int K, int V);
@@ -183,6 +185,47 @@ DSPARK_API int dspark_schedule_load_aware(const float* conf, int B, int K, const
                                           float* survival, float* tau_out, int32_t* budget_out,
                                           int32_t* dev_status, void* workspace, size_t ws_bytes,
                                           void* stream);
+
+/*
+ * dspark_markov_draft — semi-autoregressive drafting with the Markov logit
+ * bias: the block's draft logits and drafted tokens, position by position.
+ *
+ * Defines (DSpark Guide, the Markov logit-bias head and its code listing):
+ * for k = 1..K in order, with y_0 = y0[b] (the last target token),
+ *   corrected[b,k-1,:] = base[b,k-1,:] + scale * U . Vm[y_{k-1},:]^T
+ *       (the rank-r sum accumulated in fp32 on the matrix cores, scaled and
+ *       added to the widened base logit in fp32, stored in `dtype`, bf16
+ *       rounded to nearest even)
+ *   y_k = the smallest token id whose cumulative mass of
+ *       softmax(corrected[b,k-1,:] / T_b) exceeds uniforms[b,k-1] (T_b = 0:
+ *       the lowest-index maximum), drawn from the STORED corrected logits so
+ *       that the draft distribution is exactly what dspark_verify reads as
+ *       draft row k-1.
+ *
+ *   base       [B,K,V] dtype parallel logits
+ *   U, Vm      [V,r] bf16 (uint16 bit patterns) low-rank transition factors,
+ *              16-byte aligned
+ *   r          rank, a multiple of 16 in [16, 256]
+ *   scale      the listing's scalar on the bias
+ *   y0         [B] int32 token before the block
+ *   temperature [B] float32, uniforms [B,K] float32 in [0,1)
+ *   corrected  [B,K,V] dtype out (the draft logits for dspark_verify)
+ *   drafted    [B,K] int32 out, q_tok [B,K] float32 out softmax prob of the
+ *              drafted token (1 at T = 0); q_tok may be NULL
+ *   workspace  dspark_workspace_bytes(DSPARK_OP_MARKOV_DRAFT, B, K, V)
+ * 2K kernel launches (a contraction and a draw per position).
+ * A previous token outside [0,V) sets DSPARK_DEV_BAD_TOKEN (read as 0), a
+ * non-finite corrected logit DSPARK_DEV_NONFINITE, a bad temperature
+ * DSPARK_DEV_BAD_TEMP.
+ * Errors: NULL pointers; B, K, V < 1; r not a multiple of 16 in [16,256];
+ * unknown dtype; U or Vm misaligned (DSPARK_ERR_PARAM); small workspace.
+ */
+DSPARK_API int dspark_markov_draft(const void* base, int dtype, int B, int K, int V,
+                                   const uint16_t* U, const uint16_t* Vm, int r, float scale,
+                                   const int32_t* y0, const float* temperature,
+                                   const float* uniforms, void* corrected, int32_t* drafted,
+                                   float* q_tok, int32_t* dev_status, void* workspace,
+                                   size_t ws_bytes, void* stream);
 
 /*
  * dspark_calibrate — per-position temperature scaling of the confidences.

@@ -41,6 +41,7 @@ def test_workspace_sizes():
     assert w(ds.OP_VERIFY, 128, 16, 151936) > a
     assert w(ds.OP_VERIFY_GREEDY, 64, 16, 151936) == a
     assert w(ds.OP_SCHEDULE, 64, 16, 1) >= 64 * 16 * 4 + 64 * 4
+    assert w(ds.OP_MARKOV_DRAFT, 64, 16, 151936) >= 64 * (151936 // 64) * 16
 
 
 P = 4096  # any 256-aligned non-null "pointer": the checks never dereference it
@@ -111,6 +112,24 @@ def _obs(**kw):
 ])
 def test_calib_observe_argument_errors(kw, code):
     assert _obs(**kw) == code
+
+
+def _md(**kw):
+    a = dict(base=P, dtype=1, B=2, K=3, V=100, U=P, Vm=P, r=64, scale=1.0, y0=P, T=P, u=P, c=P,
+             y=P, q=None, st=P, ws=P, nb=10 ** 9, stream=None)
+    a.update(kw)
+    return ds.load_library().dspark_markov_draft(
+        a["base"], a["dtype"], a["B"], a["K"], a["V"], a["U"], a["Vm"], a["r"], a["scale"], a["y0"],
+        a["T"], a["u"], a["c"], a["y"], a["q"], a["st"], a["ws"], a["nb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(base=None), 1), (dict(U=None), 1), (dict(Vm=None), 1), (dict(y0=None), 1), (dict(c=None), 1),
+    (dict(B=0), 2), (dict(K=0), 2), (dict(V=0), 2), (dict(r=8), 2), (dict(r=24), 2), (dict(r=272), 2),
+    (dict(dtype=5), 3), (dict(U=P + 8), 7), (dict(nb=16), 5),
+])
+def test_markov_draft_argument_errors(kw, code):
+    assert _md(**kw) == code
 
 
 def _v(**kw):

@@ -656,3 +656,109 @@ def test_online_loop_on_gpu_tracks_the_oracle():
     torch.cuda.synchronize()
     assert np.all(np.abs(host(theta) - th_ref) <= 1e-5), (host(theta), th_ref)
     assert np.all(np.abs(host(theta)[1:] - 1.0) > 0.05)   # the later positions moved
+
+
+# --------------------------------------------------------- Markov logit-bias draft
+
+def _fixed_bf16(rng, shape):
+    return oracle.bf16_round((rng.integers(-256, 257, size=shape) / 256.0).astype(np.float32))
+
+
+def _to_bf16_tensor(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def _markov_case(B, K, V, r, dtype, seed, temps, fixed=True, requests=None, scale=0.5):
+    rng = np.random.default_rng(seed)
+    base32 = (rng.normal(size=(B, K, V)) * 3.0).astype(np.float32)
+    heads = rng.integers(0, V, size=(B, K, 8))
+    for b in range(B):
+        for k in range(K):
+            base32[b, k, heads[b, k]] += 12.0          # peaked, LM-like rows
+    base = oracle.bf16_round(base32) if dtype == "bf16" else base32
+    if fixed:
+        U, Vm = _fixed_bf16(rng, (V, r)), _fixed_bf16(rng, (V, r))
+    else:
+        U = oracle.bf16_round(rng.normal(size=(V, r)).astype(np.float32) * 0.3)
+        Vm = oracle.bf16_round(rng.normal(size=(V, r)).astype(np.float32) * 0.3)
+    y0 = rng.integers(0, V, size=B).astype(np.int32)
+    T = np.array([temps[b % len(temps)] for b in range(B)], np.float32)
+    u = rng.random((B, K)).astype(np.float32)
+    base_t = _to_bf16_tensor(base) if dtype == "bf16" else torch.from_numpy(base).to(DEV)
+    c, y, q, st = ds.markov_draft(base_t, _to_bf16_tensor(U), _to_bf16_tensor(Vm), scale,
+                                  torch.from_numpy(y0).to(DEV), torch.from_numpy(T).to(DEV),
+                                  torch.from_numpy(u).to(DEV))
+    torch.cuda.synchronize()
+    rc, ry, rq, dist = oracle.markov_draft(base, U, Vm, scale, y0, T, u, requests=requests)
+    gc = c.view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bf16" else host(c)
+    return gc, host(y), host(q), int(host(st)[0]), rc, ry, rq, dist, T
+
+
+@pytest.mark.parametrize("B,K,V,r,dtype", [(4, 3, 1000, 64, "bf16"), (70, 2, 5000, 128, "bf16"),
+                                           (6, 4, 151936, 256, "bf16"), (3, 3, 4100, 32, "f32")])
+def test_markov_draft_parity(B, K, V, r, dtype):
+    reqs = list(range(B)) if B <= 8 else [0, 1, 33, 63, 64, 69]
+    gc, gy, gq, st, rc, ry, rq, dist, T = _markov_case(B, K, V, r, dtype, seed=B + V, temps=[1.0, 0.0, 0.7],
+                                                       requests=reqs)
+    assert st == 0
+    boundary = 0
+    for b in reqs:
+        for k in range(K):
+            # the corrected logits of position k follow from y_{k-1}: bit for bit
+            assert np.array_equal(gc[b, k], rc[b, k]), (b, k)
+            if gy[b, k] != ry[b, k]:
+                assert dist[b, k] <= oracle.BOUNDARY, (b, k, gy[b, k], ry[b, k], dist[b, k])
+                boundary += 1
+                break
+            if T[b] > 0:
+                assert abs(gq[b, k] - rq[b, k]) <= 1e-5 * rq[b, k] + 1e-30, (b, k, gq[b, k], rq[b, k])
+            else:
+                assert gq[b, k] == 1.0
+    assert boundary <= 1
+
+
+def test_markov_draft_general_weights_within_one_ulp():
+    # weights whose rank sum is not exact in fp32: the corrected logits agree
+    # with the exact-sum oracle to one bf16 step (the first position, whose
+    # previous token is given)
+    B, K, V, r = 4, 1, 3000, 128
+    gc, gy, gq, st, rc, ry, rq, dist, T = _markov_case(B, K, V, r, "bf16", seed=21, temps=[1.0], fixed=False)
+    assert st == 0
+    g = gc.astype(np.int32)
+    o = rc.astype(np.int32)
+    assert np.max(np.abs(g - o)) <= 1
+    assert np.mean(g == o) > 0.999
+
+
+def test_markov_draft_feeds_verify():
+    # the drafted block verifies against its own draft logits: the draft
+    # distribution the sampler used is the one the verifier reads
+    B, K, V, r = 8, 4, 2048, 64
+    rng = np.random.default_rng(31)
+    base = oracle.bf16_round((rng.normal(size=(B, K, V)) * 2.0).astype(np.float32))
+    U, Vm = _fixed_bf16(rng, (V, r)), _fixed_bf16(rng, (V, r))
+    y0 = rng.integers(0, V, size=B).astype(np.int32)
+    T = np.ones(B, np.float32)
+    u = rng.random((B, K)).astype(np.float32)
+    c, y, q, st = ds.markov_draft(_to_bf16_tensor(base), _to_bf16_tensor(U), _to_bf16_tensor(Vm), 1.0,
+                                  torch.from_numpy(y0).to(DEV), torch.from_numpy(T).to(DEV),
+                                  torch.from_numpy(u).to(DEV))
+    target = _to_bf16_tensor(oracle.bf16_round((rng.normal(size=(B, K + 1, V)) * 2.0).astype(np.float32)))
+    uv = torch.from_numpy(rng.random((B, K + 1)).astype(np.float32)).to(DEV)
+    out = ds.verify(target, c, y, None, torch.from_numpy(T).to(DEV), uv)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0 and int(out["dev_status"].item()) == 0
+    # the verifier's q of each drafted token equals the sampler's
+    assert np.allclose(host(out["q_tok"]), host(q), rtol=1e-5, atol=1e-30)
+
+
+def test_markov_draft_bad_token_flag():
+    B, K, V, r = 2, 2, 256, 16
+    rng = np.random.default_rng(5)
+    base = _to_bf16_tensor(oracle.bf16_round(rng.normal(size=(B, K, V)).astype(np.float32)))
+    U = _to_bf16_tensor(_fixed_bf16(rng, (V, r)))
+    y0 = torch.tensor([3, V + 7], dtype=torch.int32, device=DEV)
+    _, _, _, st = ds.markov_draft(base, U, U, 1.0, y0, torch.ones(B, device=DEV),
+                                  torch.full((B, K), 0.5, device=DEV))
+    torch.cuda.synchronize()
+    assert int(st.item()) == oracle.DEV_BAD_TOKEN
