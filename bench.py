@@ -29,8 +29,9 @@ oracle on a bounded sample of the same workload.
 exercise: the greedy rule on the same logits, full-length blocks, the
 schedule with a binding budget, the load-aware schedule (threshold and budget
 from an engine load and a throughput curve), online calibration (temperature
-scaling and one round into the calibration window) and a mixed-temperature
-batch of 1024 requests (``--no-rows`` skips them).
+scaling and one round into the calibration window), Markov logit-bias drafting
+of the workload's block and a mixed-temperature batch of 1024 requests
+(``--no-rows`` skips them).
 
 --calibrate-copy N runs, after the timed steps, a plain elementwise copy of
 N MiB (read N MiB, write N MiB) five times: the reference kernel of known size
@@ -129,8 +130,8 @@ def time_calls(fn, reps, stream, torch):
 def row_measurements(ds, workloads, sets, outs, ws_v, dev, stream, torch, np, log):
     """The hot-path rows the headline step does not exercise, each timed
     apart (not part of `value`): the greedy rule, full-length blocks, a
-    binding budget, the load-aware schedule, online calibration and a
-    mixed-temperature batch of 1024 requests."""
+    binding budget, the load-aware schedule, online calibration, Markov
+    drafting and a mixed-temperature batch of 1024 requests."""
     rows = {}
     n = len(sets)
     B, K, V = sets[0].B, sets[0].K, sets[0].V
@@ -285,6 +286,35 @@ def row_measurements(ds, workloads, sets, outs, ws_v, dev, stream, torch, np, lo
                       "calibrate_us_median": round(t_cal * 1e3, 2),
                       "observe_us_median": round(t_obs * 1e3, 2),
                       "call_us_median": round((t_cal + t_obs) * 1e3, 2)}
+    # Markov logit-bias drafting of the workload's block (rank 256): per
+    # position an MFMA contraction over U (V x r) and a draw per request
+    r_m = 256
+    g = torch.Generator(device=dev)
+    g.manual_seed(4242)
+    Um = ((torch.randint(-256, 257, (V, r_m), generator=g, device=dev).float() / 256.0)
+          .to(torch.bfloat16))
+    Vmm = ((torch.randint(-256, 257, (V, r_m), generator=g, device=dev).float() / 256.0)
+           .to(torch.bfloat16))
+    y0m = torch.randint(0, V, (B,), generator=g, device=dev, dtype=torch.int32)
+    um = torch.rand((B, K), generator=g, device=dev)
+    cm = torch.empty_like(sets[0].draft)
+    ym = torch.empty((B, K), dtype=torch.int32, device=dev)
+    qm = torch.empty((B, K), dtype=torch.float32, device=dev)
+    stm = torch.zeros(1, dtype=torch.int32, device=dev)
+    wsm = ds.workspace(ds.OP_MARKOV_DRAFT, B, K, V, dev)
+
+    def draft_call():
+        ds.markov_draft(sets[0].draft, Um, Vmm, 0.1, y0m, sets[0].temperature, um, corrected=cm,
+                        drafted=ym, q_tok=qm, dev_status=stm, ws=wsm, stream=stream)
+    draft_call()
+    t_med, _ = time_calls(draft_call, 10, stream, torch)
+    step_bytes = V * r_m * 2 + 2 * B * V * s       # U once, base rows read, corrected rows written
+    step_flops = 2.0 * V * r_m * B
+    rows["NEXT3_markov_draft_b64"] = {
+        "workload": f"b{B}-k{K}-v{V}, rank {r_m}, bf16 (U, V fixed-point synthetic), T = 1",
+        "call_us_median": round(t_med * 1e3, 2), "us_per_position": round(t_med * 1e3 / K, 2),
+        "bytes_per_position": step_bytes, "hbm_gbs": round(step_bytes * K / (t_med / 1e3) / 1e9, 1),
+        "mfma_tflops": round(step_flops * K / (t_med / 1e3) / 1e12, 2)}
     sched5()  # back to the configured lengths for the verify row
     a5 = torch.empty(B5, dtype=torch.int32, device=dev)
     t5 = torch.empty((B5, K5 + 1), dtype=torch.int32, device=dev)
@@ -307,7 +337,8 @@ def row_measurements(ds, workloads, sets, outs, ws_v, dev, stream, torch, np, lo
                                 "stream_us_mean": round(t_s * 1e3, 2),
                                 "call_us_median": round(t_c * 1e3, 2),
                                 "positions_per_s": round(int(L.sum()) / (t_c / 1e3), 1)}
-    assert int(st_.item()) == 0 and int(st5.item()) == 0, "device status flags set"
+    flags = {"G1/full": int(st_.item()), "b1024": int(st5.item()), "markov": int(stm.item())}
+    assert not any(flags.values()), f"device status flags set: {flags}"
     log("rows: " + "; ".join(f"{k} {v.get('stream_gbs', v.get('call_us_median'))}" for k, v in rows.items()))
     return rows
 
@@ -462,6 +493,13 @@ def main():
     mean_acc = float(np.mean([a.mean() for a, _ in accs]))
     waste = float(np.mean([1 - a.sum() / max(1, L.sum()) for a, L in accs]))
     traffic, traffic_note = measured_traffic()
+    # every input set scheduled once (short runs leave some unscheduled), so
+    # that the rows read valid lengths
+    for i in range(len(sets)):
+        w, o = sets[i], outs[i]
+        ds.schedule(w.conf, w.threshold, w.budget, w.min_len, lengths=o["lengths"], mask=o["mask"],
+                    survival=o["surv"], dev_status=o["st"], ws=ws_s, stream=stream)
+    torch.cuda.synchronize()
 
     result = {
         "metric": METRIC,

@@ -5,15 +5,19 @@
 //   y_k ~ softmax(corrected[b,k] / T_b)  (inverse CDF at uniforms[b,k-1];
 //         the lowest-index maximum at T = 0),  y_0 = the last target token.
 // Two launches per position:
-//   k_markov_bias  an MFMA contraction: a workgroup takes 64 vocabulary rows
-//                  of U and the previous tokens' rows of Vm for 64 requests
-//                  (staged in LDS), four waves of 16 rows each run
-//                  v_mfma_f32_16x16x16_bf16 over the rank, and the epilogue
-//                  adds the scaled bias to the base logits, stores the
-//                  corrected logits in the base dtype and summarises the
-//                  tile per request (integer shift k = ceil(max * c) and the
-//                  sum of 2^(x*c - k) over the stored values, or (max, lowest
-//                  index) at T = 0);
+//   k_markov_bias  an MFMA contraction: persistent workgroups (three per
+//                  compute unit) stage the previous tokens' rows of Vm for 64
+//                  requests in LDS once and loop over 64-row tiles of U; four
+//                  waves of 16 rows run v_mfma_f32_16x16x16_bf16 over the
+//                  rank (the next tile's rows of U are requested as soon as
+//                  the current ones are consumed), the bias tile goes through
+//                  LDS to [request][row], and each lane finishes 16
+//                  consecutive rows of one request: adds the scaled bias to
+//                  the base logits, stores the corrected logits in the base
+//                  dtype (16-byte accesses) and summarises the tile per
+//                  request over the four lanes that share it (integer shift
+//                  k = ceil(max * c) and the sum of 2^(x*c - k) over the
+//                  stored values, or (max, lowest index) at T = 0);
 //   k_markov_draw  one workgroup per request: merges the tile summaries
 //                  (exact power-of-two rescaling), finds the tile holding
 //                  u * S by a scan over contiguous runs of tiles, and the
@@ -70,15 +74,16 @@ template <int DT>
 __global__ void __launch_bounds__(256) k_markov_bias(MarkovArgs a) {
   constexpr int kLds = kMarkovMaxRank + 8;  // padded row of a staged Vm row (bf16)
   __shared__ __align__(16) uint16_t s_w[kMarkovBatch][kLds];
-  __shared__ Partial s_p[4][kMarkovBatch];
-  const int tile = blockIdx.x;
+  // one tile's bias, [request][row] (rows padded to 68 floats: 16-byte aligned)
+  __shared__ __align__(16) float s_c[kMarkovBatch][kMarkovRows + 4];
   const int b0 = blockIdx.y * kMarkovBatch;
   const int w = threadIdx.x / kWave, l = lane_id();
   const int r = a.r, rq = r / 4;  // rank entries per lane quarter
   const int K = a.K, V = a.V, k = a.step;
   int bad = 0;
 
-  // the previous tokens' rows of Vm, 16 bytes at a time (zero rows past B)
+  // the previous tokens' rows of Vm, 16 bytes at a time (zero rows past B),
+  // staged once for all the tiles this workgroup takes
   const int pieces = r / 8;
   for (int e = threadIdx.x; e < kMarkovBatch * pieces; e += 256) {
     const int i = e / pieces, piece = e - i * pieces;
@@ -90,139 +95,179 @@ __global__ void __launch_bounds__(256) k_markov_bias(MarkovArgs a) {
     }
     *reinterpret_cast<uint4*>(&s_w[i][piece * 8]) = v;
   }
-  // this lane's row of U (rows past V re-read row V-1 and are dropped) and
-  // its quarter q of the rank: entries q*r/4 .. (q+1)*r/4 - 1
-  const int row0 = tile * kMarkovRows + w * 16;
-  const int q = l >> 4;
-  const int vrow = min(row0 + (l & 15), V - 1);
-  uint32_t areg[kMarkovMaxRank / 8];
-  const uint16_t* up = a.U + (size_t)vrow * r + q * rq;
-#pragma unroll
-  for (int i = 0; i < kMarkovMaxRank / 32; ++i) {
-    if (i * 8 < rq) {
-      const uint4 v = *reinterpret_cast<const uint4*>(up + i * 8);
-      areg[4 * i] = v.x;
-      areg[4 * i + 1] = v.y;
-      areg[4 * i + 2] = v.z;
-      areg[4 * i + 3] = v.w;
-    } else {
-      areg[4 * i] = areg[4 * i + 1] = areg[4 * i + 2] = areg[4 * i + 3] = 0u;
-    }
-  }
+  // after each tile, lane l finishes request 16w + l/4 over rows
+  // 16 (l % 4) .. 16 (l % 4) + 15 of the tile
+  const int ri = l >> 2, part = l & 3;
+  const int bl = b0 + w * 16 + ri;
+  const bool bok = bl < a.B;
+  const int bb = bok ? bl : a.B - 1;
+  const float Tl = a.temperature[bb];
+  const bool greedy = Tl == 0.f;
+  const float cl = greedy ? 0.f : temp_c(Tl);
+  const size_t roff = ((size_t)bb * K + (k - 1)) * (size_t)V;
+  const char* brow = static_cast<const char*>(a.base) + roff * Elem<DT>::kBytes;
+  char* crow = static_cast<char*>(a.corrected) + roff * Elem<DT>::kBytes;
+  // 16-byte vector accesses when rows start on 16-byte boundaries
+  constexpr int kVecElems = 16 / Elem<DT>::kBytes;
+  const bool vec = (V % kVecElems) == 0 &&
+                   ((uintptr_t)a.base % 16) == 0 && ((uintptr_t)a.corrected % 16) == 0;
   __syncthreads();
-  // D[row][request] = sum over the rank of U[row][j] * Vm[prev][j]; MFMA step
-  // ks takes rank entries q*r/4 + 4*ks + (0..3) in lane quarter q for A and B
-  float4_t acc[4];
+  const int q = l >> 4;
+  // this lane's row of a tile of U (rows past V re-read row V-1 and are
+  // dropped) and its quarter q of the rank: entries q*r/4 .. (q+1)*r/4 - 1;
+  // the next tile's rows are requested as soon as the current ones are
+  // consumed, so they arrive during the epilogue
+  uint32_t areg[kMarkovMaxRank / 8];
+  auto load_a = [&](int tile) {
+    const int vrow = min(tile * kMarkovRows + w * 16 + (l & 15), V - 1);
+    const uint16_t* up = a.U + (size_t)vrow * r + q * rq;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) acc[nb] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < kMarkovMaxRank / 16; ++ks) {
-    if (ks * 4 < rq) {
-      short4_t av;
-      av[0] = (short)(areg[2 * ks] & 0xffffu);
-      av[1] = (short)(areg[2 * ks] >> 16);
-      av[2] = (short)(areg[2 * ks + 1] & 0xffffu);
-      av[3] = (short)(areg[2 * ks + 1] >> 16);
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const short4_t bv = *reinterpret_cast<const short4_t*>(&s_w[nb * 16 + (l & 15)][q * rq + 4 * ks]);
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, acc[nb], 0, 0, 0);
+    for (int i = 0; i < kMarkovMaxRank / 32; ++i) {
+      if (i * 8 < rq) {
+        const uint4 v = *reinterpret_cast<const uint4*>(up + i * 8);
+        areg[4 * i] = v.x;
+        areg[4 * i + 1] = v.y;
+        areg[4 * i + 2] = v.z;
+        areg[4 * i + 3] = v.w;
+      } else {
+        areg[4 * i] = areg[4 * i + 1] = areg[4 * i + 2] = areg[4 * i + 3] = 0u;
       }
     }
-  }
-  // epilogue: lane l holds rows row0 + 4q + j (j = 0..3) of request
-  // b0 + 16 nb + (l & 15)
+  };
+  if (blockIdx.x < a.tiles) load_a(blockIdx.x);
+  for (int tile = blockIdx.x; tile < a.tiles; tile += gridDim.x) {
+    // this tile's base logits for the epilogue, requested before the MFMAs
+    const int vbeg = tile * kMarkovRows + part * 16;
+    const bool full = vec && vbeg + 16 <= V;
+    float xb[16];
+    if (full) {
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int b = b0 + nb * 16 + (l & 15);
-    const bool bok = b < a.B;
-    const int bb = bok ? b : b0;
-    const float T = a.temperature[bb];
-    const bool greedy = T == 0.f;
-    const float c = greedy ? 0.f : temp_c(T);
-    const size_t roff = ((size_t)bb * K + (k - 1)) * (size_t)V;
-    const void* brow = static_cast<const char*>(a.base) + roff * Elem<DT>::kBytes;
-    void* crow = static_cast<char*>(a.corrected) + roff * Elem<DT>::kBytes;
-    float xs[4];
-    bool ok[4];
+      for (int g = 0; g < 16 / kVecElems; ++g) {
+        const uint4 u4 = *reinterpret_cast<const uint4*>(brow + (size_t)(vbeg + g * kVecElems) *
+                                                             Elem<DT>::kBytes);
+        const uint32_t wd[4] = {u4.x, u4.y, u4.z, u4.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int v = row0 + 4 * q + j;
-      ok[j] = bok && v < V;
-      const float x = load_elem<DT>(brow, ok[j] ? v : 0) + a.scale * acc[nb][j];
-      xs[j] = ok[j] ? store_elem<DT>(crow, v, x) : -INFINITY;
+        for (int e = 0; e < kVecElems; ++e) {
+          if constexpr (DT == DSPARK_BF16)
+            xb[g * kVecElems + e] = __uint_as_float((e & 1) ? (wd[e >> 1] & 0xffff0000u) : (wd[e >> 1] << 16));
+          else
+            xb[g * kVecElems + e] = __uint_as_float(wd[e]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xb[i] = load_elem<DT>(brow, min(vbeg + i, V - 1));
     }
-    // this wave's 16 rows per request: lanes l, l^16, l^32, l^48 share it
-    float m = fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3]));
-    int mi = 0x7fffffff;
+    // D[row][request] = sum over the rank of U[row][j] * Vm[prev][j]; MFMA
+    // step ks takes rank entries q*r/4 + 4*ks + (0..3) in lane quarter q
+    float4_t acc[4];
 #pragma unroll
-    for (int j = 3; j >= 0; --j)
-      if (ok[j] && xs[j] == m) mi = row0 + 4 * q + j;
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
-    if (xs[0] != xs[0] || xs[1] != xs[1] || xs[2] != xs[2] || xs[3] != xs[3] || m == INFINITY)
-      bad |= DSPARK_DEV_NONFINITE;
+    for (int nb = 0; nb < 4; ++nb) acc[nb] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kMarkovMaxRank / 16; ++ks) {
+      if (ks * 4 < rq) {
+        short4_t av;
+        av[0] = (short)(areg[2 * ks] & 0xffffu);
+        av[1] = (short)(areg[2 * ks] >> 16);
+        av[2] = (short)(areg[2 * ks + 1] & 0xffffu);
+        av[3] = (short)(areg[2 * ks + 1] >> 16);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const short4_t bv =
+              *reinterpret_cast<const short4_t*>(&s_w[nb * 16 + (l & 15)][q * rq + 4 * ks]);
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, acc[nb], 0, 0, 0);
+        }
+      }
+    }
+    if (tile + (int)gridDim.x < a.tiles) load_a(tile + gridDim.x);
+    // lane l holds rows 16w + 4q + j of requests 16 nb + (l & 15): through
+    // LDS to [request][row]
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s_c[nb * 16 + (l & 15)][w * 16 + 4 * q + j] = acc[nb][j];
+    __syncthreads();
+    // epilogue: corrected logits of this lane's 16 rows, stored, and the
+    // tile's summary per request over the four lanes that share it
+    float xs[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float x = xb[i] + a.scale * s_c[w * 16 + ri][part * 16 + i];
+      // rounded to the storage dtype (bf16: nearest even)
+      float st;
+      if constexpr (DT == DSPARK_BF16) {
+        const uint32_t u = __float_as_uint(x);
+        const uint32_t h = x != x ? 0x7fc0u : ((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+        st = __uint_as_float(h << 16);
+      } else {
+        st = x;
+      }
+      xs[i] = bok && vbeg + i < V ? st : -INFINITY;
+    }
+    if (bok) {
+      if (full) {
+#pragma unroll
+        for (int g = 0; g < 16 / kVecElems; ++g) {
+          uint32_t wd[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (DT == DSPARK_BF16)
+              wd[e] = (__float_as_uint(xs[g * 8 + 2 * e]) >> 16) |
+                      (__float_as_uint(xs[g * 8 + 2 * e + 1]) & 0xffff0000u);
+            else
+              wd[e] = __float_as_uint(xs[g * 4 + e]);
+          }
+          *reinterpret_cast<uint4*>(crow + (size_t)(vbeg + g * kVecElems) * Elem<DT>::kBytes) =
+              uint4{wd[0], wd[1], wd[2], wd[3]};
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (vbeg + i < V) store_elem<DT>(crow, vbeg + i, xs[i]);
+      }
+    }
+    float m = xs[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) m = fmaxf(m, xs[i]);
+    bool nonfinite = false;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) nonfinite |= xs[i] != xs[i] || xs[i] == INFINITY;
+    if (nonfinite) bad |= DSPARK_DEV_NONFINITE;
+    m = fmaxf(m, dpp<kQuadXor1>(m));
+    m = fmaxf(m, dpp<kQuadXor2>(m));
     Partial pt;
     if (greedy) {
-      // lowest row holding the maximum
-      int cand = 0x7fffffff;
+      int at = 0x7fffffff;
 #pragma unroll
-      for (int j = 3; j >= 0; --j)
-        if (ok[j] && xs[j] == m) cand = row0 + 4 * q + j;
-      cand = min(cand, __shfl_xor(cand, 16));
-      cand = min(cand, __shfl_xor(cand, 32));
+      for (int i = 15; i >= 0; --i)
+        if (xs[i] == m && vbeg + i < V) at = vbeg + i;
+      at = min(at, dpp<kQuadXor1>(at));
+      at = min(at, dpp<kQuadXor2>(at));
       pt.k = m;
-      pt.idx = cand;
+      pt.idx = at;
       pt.s = 0.0;
     } else {
       const bool none = m == -INFINITY;
-      const float kk = ceilf(m * c);
+      const float kk = ceilf(m * cl);
       const float nk = none ? 0.f : -kk;
-      float s4 = 0.f;
+      float e[16];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) s4 += ok[j] ? fast_exp2(fmaf(xs[j], c, nk)) : 0.f;
-      double s = (double)s4;
-      s += __shfl_xor(s, 16);
-      s += __shfl_xor(s, 32);
+      for (int i = 0; i < 16; ++i) e[i] = fast_exp2(fmaf(xs[i], cl, nk));
+      float s8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s8[i] = e[2 * i] + e[2 * i + 1];
+      const float s16 = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
+      double sd = (double)s16;
+      sd += dpp<kQuadXor1>(sd);
+      sd += dpp<kQuadXor2>(sd);
       pt.k = none ? -INFINITY : kk;
       pt.idx = 0;
-      pt.s = s;
+      pt.s = sd;
     }
-    (void)mi;
-    if (q == 0) s_p[w][nb * 16 + (l & 15)] = pt;
+    if (bok && part == 0) a.part[(size_t)bl * a.tiles + tile] = pt;
+    __syncthreads();  // s_c is rewritten by the next tile
   }
   if (bad) flag(a.dev_status, bad);
-  __syncthreads();
-  // the tile's summary per request: the four waves merged by wave 0
-  if (w == 0) {
-    const int b = b0 + l;
-    if (b < a.B) {
-      const bool greedy = a.temperature[b] == 0.f;
-      Partial out;
-      if (greedy) {
-        out = s_p[0][l];
-#pragma unroll
-        for (int ww = 1; ww < 4; ++ww) {
-          const Partial p = s_p[ww][l];
-          if (p.k > out.k || (p.k == out.k && p.idx < out.idx)) out = p;
-        }
-      } else {
-        float km = s_p[0][l].k;
-#pragma unroll
-        for (int ww = 1; ww < 4; ++ww) km = fmaxf(km, s_p[ww][l].k);
-        double s = 0.0;
-#pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
-          const Partial p = s_p[ww][l];
-          s += p.s > 0.0 ? ldexp(p.s, shift_amount(p.k - km)) : 0.0;
-        }
-        out.k = km;
-        out.idx = 0;
-        out.s = s;
-      }
-      a.part[(size_t)b * a.tiles + tile] = out;
-    }
-  }
 }
 
 // block-wide helpers of k_markov_draw (256 threads, 4 waves)
@@ -388,7 +433,10 @@ __global__ void __launch_bounds__(256) k_markov_draw(MarkovArgs a) {
 
 template <int DT>
 static int launch_markov_t(MarkovArgs& a, hipStream_t st) {
-  const dim3 gb((unsigned)a.tiles, (unsigned)((a.B + kMarkovBatch - 1) / kMarkovBatch));
+  // persistent workgroups over the vocabulary tiles, three per compute unit
+  // (51 KB of LDS each)
+  const int wgs = min(a.tiles, 3 * compute_units());
+  const dim3 gb((unsigned)wgs, (unsigned)((a.B + kMarkovBatch - 1) / kMarkovBatch));
   for (int k = 1; k <= a.K; ++k) {
     a.step = k;
     hipLaunchKernelGGL(k_markov_bias<DT>, gb, dim3(256), 0, st, a);

@@ -31,5 +31,6 @@ struct MarkovArgs {
 };
 
 int launch_markov(MarkovArgs& a, int dtype, hipStream_t st);
+int compute_units();  // of the current device
 
 }  // namespace dspark
