@@ -762,3 +762,92 @@ def test_markov_draft_bad_token_flag():
                                   torch.full((B, K), 0.5, device=DEV))
     torch.cuda.synchronize()
     assert int(st.item()) == oracle.DEV_BAD_TOKEN
+
+
+# ------------------------------------------------------ graph capture, next rows
+
+def test_graph_capture_replay_next_rows():
+    # calibrate -> load-aware schedule -> Markov draft -> window observe,
+    # captured once and replayed on fresh inputs: each replay equals the same
+    # calls run eagerly from the same starting window state and temperatures
+    rng = np.random.default_rng(41)
+    B, K, V, r, M, window = 16, 4, 3000, 64, 10, 2
+    f32, i32 = torch.float32, torch.int32
+    raw = torch.empty((B, K), dtype=f32, device=DEV)
+    load = torch.empty(2, dtype=f32, device=DEV)
+    u = torch.empty((B, K), dtype=f32, device=DEV)
+    acc_in = torch.empty(B, dtype=i32, device=DEV)
+    theta = torch.from_numpy(rng.uniform(0.8, 1.5, size=K).astype(np.float32)).to(DEV)
+    curve = torch.tensor(np.asarray(PAGE_CURVE, np.float32), device=DEV)
+    base = _to_bf16_tensor(oracle.bf16_round((rng.normal(size=(B, K, V)) * 3.0).astype(np.float32)))
+    U, Vm = _to_bf16_tensor(_fixed_bf16(rng, (V, r))), _to_bf16_tensor(_fixed_bf16(rng, (V, r)))
+    y0 = torch.from_numpy(rng.integers(0, V, size=B).astype(np.int32)).to(DEV)
+    T = torch.tensor([(1.0, 0.0, 0.7)[b % 3] for b in range(B)], dtype=f32, device=DEV)
+    state = ds.calib_state(K, M, DEV)
+    ws_s = ds.workspace(ds.OP_SCHEDULE, B, K, 1, DEV)
+    ws_m = ds.workspace(ds.OP_MARKOV_DRAFT, B, K, V, DEV)
+
+    def outputs():
+        return {"cal": torch.empty((B, K), dtype=f32, device=DEV),
+                "L": torch.empty(B, dtype=i32, device=DEV),
+                "mask": torch.empty((B, K), dtype=torch.uint8, device=DEV),
+                "surv": torch.empty((B, K), dtype=f32, device=DEV),
+                "tau": torch.empty(1, dtype=f32, device=DEV),
+                "bud": torch.empty(1, dtype=i32, device=DEV),
+                "corr": torch.empty_like(base),
+                "y": torch.empty((B, K), dtype=i32, device=DEV),
+                "q": torch.empty((B, K), dtype=f32, device=DEV),
+                "acc": torch.empty(B, dtype=i32, device=DEV),
+                "ece": torch.zeros(1, dtype=f32, device=DEV),
+                "st": torch.zeros(1, dtype=i32, device=DEV)}
+
+    def step(o, th, sta):
+        o["st"].zero_()
+        ds.calibrate(raw, th, out=o["cal"], dev_status=o["st"])
+        ds.schedule_load_aware(o["cal"], load, 100.0, 60.0, 0.2, 0.8, curve, 10.0, 1,
+                               lengths=o["L"], mask=o["mask"], survival=o["surv"], tau_out=o["tau"],
+                               budget_out=o["bud"], dev_status=o["st"], ws=ws_s)
+        ds.markov_draft(base, U, Vm, 0.5, y0, T, u, corrected=o["corr"], drafted=o["y"],
+                        q_tok=o["q"], dev_status=o["st"], ws=ws_m)
+        torch.minimum(acc_in, o["L"], out=o["acc"])
+        ds.calib_observe(o["cal"], o["L"], o["acc"], th, 0.05, 0.1, window, M, sta,
+                         ece_out=o["ece"], dev_status=o["st"])
+
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(9)
+
+    def fresh_inputs():
+        raw.copy_(torch.rand((B, K), generator=gen, device=DEV) * 0.7 + 0.3)
+        u.copy_(torch.rand((B, K), generator=gen, device=DEV))
+        acc_in.copy_(torch.randint(0, K + 1, (B,), generator=gen, device=DEV, dtype=i32))
+        load.copy_(torch.rand(2, generator=gen, device=DEV) * torch.tensor([150.0, 90.0], device=DEV))
+
+    og, oe = outputs(), outputs()
+    fresh_inputs()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(og, theta, state)                      # warm-up (one window round)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(og, theta, state)
+    moved = 0
+    for rep in range(5):
+        fresh_inputs()
+        th0, s0 = theta.clone(), state.clone()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {k: v.clone() for k, v in og.items()}
+        th_g, s_g = theta.clone(), state.clone()
+        th_e, s_e = th0.clone(), s0.clone()
+        step(oe, th_e, s_e)                          # eager from the same state
+        torch.cuda.synchronize()
+        assert int(got["st"].item()) == 0, rep
+        for k, v in got.items():
+            assert torch.equal(v, oe[k]), (rep, k)
+        assert torch.equal(th_g, th_e) and torch.equal(s_g, s_e), rep
+        moved += int(not torch.equal(th_g, th0))
+    assert moved >= 2                                # window ends fell inside the replays
