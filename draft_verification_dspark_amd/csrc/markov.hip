@@ -8,20 +8,23 @@
 //   k_markov_bias  an MFMA contraction: persistent workgroups (three per
 //                  compute unit) stage the previous tokens' rows of Vm for 64
 //                  requests in LDS once and loop over 64-row tiles of U; four
-//                  waves of 16 rows run v_mfma_f32_16x16x16_bf16 over the
-//                  rank (the next tile's rows of U are requested as soon as
-//                  the current ones are consumed), the bias tile goes through
-//                  LDS to [request][row], and each lane finishes 16
-//                  consecutive rows of one request: adds the scaled bias to
-//                  the base logits, stores the corrected logits in the base
-//                  dtype (16-byte accesses) and summarises the tile per
-//                  request over the four lanes that share it (integer shift
-//                  k = ceil(max * c) and the sum of 2^(x*c - k) over the
-//                  stored values, or (max, lowest index) at T = 0);
-//   k_markov_draw  one workgroup per request: merges the tile summaries
-//                  (exact power-of-two rescaling), finds the tile holding
-//                  u * S by a scan over contiguous runs of tiles, and the
-//                  token inside it by a wave scan of its 64 stored logits.
+//                  waves of 16 rows run v_mfma_f32_16x16x32_bf16 over the
+//                  rank (one 16x16x16 step for a 16-entry remainder). A
+//                  tile's rows of U and base logits are requested one tile
+//                  ahead, and every global access has four lanes on 64
+//                  contiguous bytes of a row. The bias tile goes through LDS
+//                  to [request][row], and each lane finishes 16 rows of one
+//                  request: adds the scaled bias to the base logits, stores
+//                  the corrected logits in the base dtype (16-byte accesses)
+//                  and summarises the tile per request over the four lanes
+//                  that share it (integer shift k = ceil(max * c) and the sum
+//                  of 2^(x*c - k) over the stored values, or (max, lowest
+//                  index) at T = 0);
+//   k_markov_draw  one workgroup per request: each thread reads a
+//                  contiguous run of tile summaries once, the block merges
+//                  them (exact power-of-two rescaling) and scans the runs to
+//                  the tile holding u * S, and wave 0 finds the token inside
+//                  it by a scan of its 64 stored logits.
 // The bias is an fp32 sum (MFMA accumulation), scaled and added in fp32,
 // and the draw reads the stored logits, so the draft distribution is exactly
 // what the verifier reads back.
@@ -35,6 +38,7 @@ namespace dspark {
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 namespace {
 
@@ -78,10 +82,87 @@ __global__ void __launch_bounds__(256) k_markov_bias(MarkovArgs a) {
   __shared__ __align__(16) float s_c[kMarkovBatch][kMarkovRows + 4];
   const int b0 = blockIdx.y * kMarkovBatch;
   const int w = threadIdx.x / kWave, l = lane_id();
-  const int r = a.r, rq = r / 4;  // rank entries per lane quarter
-  const int K = a.K, V = a.V, k = a.step;
+  const int r = a.r, K = a.K, V = a.V, k = a.step;
+  const int r32 = r / 32;               // 16x16x32 steps over the rank
+  const bool tail16 = (r & 31) != 0;    // and one 16x16x16 step on the last 16 entries
   int bad = 0;
-
+  // lane l: row l % 16 of its wave's 16 rows and rank slice q = l / 16 in the
+  // contraction; request 16w + l/4 and quarter part = l % 4 of the tile's
+  // rows in the epilogue
+  const int row16 = l & 15, q = l >> 4, ri = l >> 2, part = l & 3;
+  const int bl = b0 + w * 16 + ri;
+  const bool bok = bl < a.B;
+  const int bb = bok ? bl : a.B - 1;
+  const float Tl = a.temperature[bb];
+  const bool greedy = Tl == 0.f;
+  const float cl = greedy ? 0.f : temp_c(Tl);
+  const size_t roff = ((size_t)bb * K + (k - 1)) * (size_t)V;
+  const char* brow = static_cast<const char*>(a.base) + roff * Elem<DT>::kBytes;
+  char* crow = static_cast<char*>(a.corrected) + roff * Elem<DT>::kBytes;
+  // 16-byte vector accesses when rows start on 16-byte boundaries
+  constexpr int kVecElems = 16 / Elem<DT>::kBytes;
+  constexpr int kPieces = 16 / kVecElems;
+  const bool vec = (V % kVecElems) == 0 &&
+                   ((uintptr_t)a.base % 16) == 0 && ((uintptr_t)a.corrected % 16) == 0;
+  // element i of this lane's 16 rows: 16-byte piece i / kVecElems sits at
+  // rows 4 kVecElems (i / kVecElems) + kVecElems part .. + kVecElems - 1, so
+  // the four lanes of a request cover 64 contiguous bytes per piece
+  auto row_of = [&](int i) {
+    return (i / kVecElems) * 4 * kVecElems + part * kVecElems + (i % kVecElems);
+  };
+  // A tile's operands, requested one tile ahead so that they arrive during
+  // the current tile's MFMAs and epilogue:
+  //   U row (tile row 16w + l % 16; rows past V re-read row V-1 and are
+  //   dropped): rank entries 32 i + 8 q .. + 7 for step i (the 16-entry tail:
+  //   32 i + 4 q .. + 3), so a quarter-wave reads 64 contiguous bytes of
+  //   each of its 16 rows per load;
+  //   the 16 base logits as raw words (whole vector tiles; a ragged tile
+  //   reads them element by element in the epilogue)
+  constexpr int kAw = kMarkovMaxRank / 8;
+  constexpr int kXw = 16 * Elem<DT>::kBytes / 4;
+  uint32_t areg[kAw], anext[kAw], xraw[kXw], xnext[kXw];
+  auto load_a = [&](int tile, uint32_t (&dst)[kAw]) {
+    const int vrow = min(tile * kMarkovRows + w * 16 + row16, V - 1);
+    const uint16_t* up = a.U + (size_t)vrow * r;
+#pragma unroll
+    for (int i = 0; i < kMarkovMaxRank / 32; ++i) {
+      if (i < r32) {
+        const uint4 v = *reinterpret_cast<const uint4*>(up + 32 * i + 8 * q);
+        dst[4 * i] = v.x;
+        dst[4 * i + 1] = v.y;
+        dst[4 * i + 2] = v.z;
+        dst[4 * i + 3] = v.w;
+      } else if (i == r32 && tail16) {
+        const uint2 v = *reinterpret_cast<const uint2*>(up + 32 * i + 4 * q);
+        dst[4 * i] = v.x;
+        dst[4 * i + 1] = v.y;
+        dst[4 * i + 2] = dst[4 * i + 3] = 0u;
+      } else {
+        dst[4 * i] = dst[4 * i + 1] = dst[4 * i + 2] = dst[4 * i + 3] = 0u;
+      }
+    }
+  };
+  auto load_base = [&](int tile, uint32_t (&dst)[kXw]) {
+    const int vt = tile * kMarkovRows;
+    if (vec && vt + kMarkovRows <= V) {
+#pragma unroll
+      for (int g = 0; g < kPieces; ++g) {
+        const uint4 v = *reinterpret_cast<const uint4*>(
+            brow + (size_t)(vt + g * 4 * kVecElems + part * kVecElems) * Elem<DT>::kBytes);
+        dst[4 * g] = v.x;
+        dst[4 * g + 1] = v.y;
+        dst[4 * g + 2] = v.z;
+        dst[4 * g + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kXw; ++i) dst[i] = 0u;
+    }
+  };
+  if (blockIdx.x < a.tiles) {
+    load_a(blockIdx.x, areg);
+    load_base(blockIdx.x, xraw);
+  }
   // the previous tokens' rows of Vm, 16 bytes at a time (zero rows past B),
   // staged once for all the tiles this workgroup takes
   const int pieces = r / 8;
@@ -95,104 +176,72 @@ __global__ void __launch_bounds__(256) k_markov_bias(MarkovArgs a) {
     }
     *reinterpret_cast<uint4*>(&s_w[i][piece * 8]) = v;
   }
-  // after each tile, lane l finishes request 16w + l/4 over rows
-  // 16 (l % 4) .. 16 (l % 4) + 15 of the tile
-  const int ri = l >> 2, part = l & 3;
-  const int bl = b0 + w * 16 + ri;
-  const bool bok = bl < a.B;
-  const int bb = bok ? bl : a.B - 1;
-  const float Tl = a.temperature[bb];
-  const bool greedy = Tl == 0.f;
-  const float cl = greedy ? 0.f : temp_c(Tl);
-  const size_t roff = ((size_t)bb * K + (k - 1)) * (size_t)V;
-  const char* brow = static_cast<const char*>(a.base) + roff * Elem<DT>::kBytes;
-  char* crow = static_cast<char*>(a.corrected) + roff * Elem<DT>::kBytes;
-  // 16-byte vector accesses when rows start on 16-byte boundaries
-  constexpr int kVecElems = 16 / Elem<DT>::kBytes;
-  const bool vec = (V % kVecElems) == 0 &&
-                   ((uintptr_t)a.base % 16) == 0 && ((uintptr_t)a.corrected % 16) == 0;
   __syncthreads();
-  const int q = l >> 4;
-  // this lane's row of a tile of U (rows past V re-read row V-1 and are
-  // dropped) and its quarter q of the rank: entries q*r/4 .. (q+1)*r/4 - 1;
-  // the next tile's rows are requested as soon as the current ones are
-  // consumed, so they arrive during the epilogue
-  uint32_t areg[kMarkovMaxRank / 8];
-  auto load_a = [&](int tile) {
-    const int vrow = min(tile * kMarkovRows + w * 16 + (l & 15), V - 1);
-    const uint16_t* up = a.U + (size_t)vrow * r + q * rq;
-#pragma unroll
-    for (int i = 0; i < kMarkovMaxRank / 32; ++i) {
-      if (i * 8 < rq) {
-        const uint4 v = *reinterpret_cast<const uint4*>(up + i * 8);
-        areg[4 * i] = v.x;
-        areg[4 * i + 1] = v.y;
-        areg[4 * i + 2] = v.z;
-        areg[4 * i + 3] = v.w;
-      } else {
-        areg[4 * i] = areg[4 * i + 1] = areg[4 * i + 2] = areg[4 * i + 3] = 0u;
-      }
-    }
-  };
-  if (blockIdx.x < a.tiles) load_a(blockIdx.x);
   for (int tile = blockIdx.x; tile < a.tiles; tile += gridDim.x) {
-    // this tile's base logits for the epilogue, requested before the MFMAs
-    const int vbeg = tile * kMarkovRows + part * 16;
-    const bool full = vec && vbeg + 16 <= V;
-    float xb[16];
-    if (full) {
-#pragma unroll
-      for (int g = 0; g < 16 / kVecElems; ++g) {
-        const uint4 u4 = *reinterpret_cast<const uint4*>(brow + (size_t)(vbeg + g * kVecElems) *
-                                                             Elem<DT>::kBytes);
-        const uint32_t wd[4] = {u4.x, u4.y, u4.z, u4.w};
-#pragma unroll
-        for (int e = 0; e < kVecElems; ++e) {
-          if constexpr (DT == DSPARK_BF16)
-            xb[g * kVecElems + e] = __uint_as_float((e & 1) ? (wd[e >> 1] & 0xffff0000u) : (wd[e >> 1] << 16));
-          else
-            xb[g * kVecElems + e] = __uint_as_float(wd[e]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) xb[i] = load_elem<DT>(brow, min(vbeg + i, V - 1));
+    const int nxt = tile + (int)gridDim.x;
+    if (nxt < a.tiles) {
+      load_a(nxt, anext);
+      load_base(nxt, xnext);
     }
-    // D[row][request] = sum over the rank of U[row][j] * Vm[prev][j]; MFMA
-    // step ks takes rank entries q*r/4 + 4*ks + (0..3) in lane quarter q
+    const int vt = tile * kMarkovRows;
+    const bool full = vec && vt + kMarkovRows <= V;
+    // D[row][request] = sum over the rank of U[row][j] * Vm[prev][j]: A and
+    // B take the same rank entries in every lane and step, so each product
+    // enters the sum once
     float4_t acc[4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[nb] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < kMarkovMaxRank / 16; ++ks) {
-      if (ks * 4 < rq) {
+    for (int ks = 0; ks < kMarkovMaxRank / 32; ++ks) {
+      if (ks < r32) {
+        const uint4 aw = {areg[4 * ks], areg[4 * ks + 1], areg[4 * ks + 2], areg[4 * ks + 3]};
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, aw);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const bf16x8_t bv =
+              *reinterpret_cast<const bf16x8_t*>(&s_w[nb * 16 + row16][32 * ks + 8 * q]);
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[nb], 0, 0, 0);
+        }
+      } else if (ks == r32 && tail16) {
         short4_t av;
-        av[0] = (short)(areg[2 * ks] & 0xffffu);
-        av[1] = (short)(areg[2 * ks] >> 16);
-        av[2] = (short)(areg[2 * ks + 1] & 0xffffu);
-        av[3] = (short)(areg[2 * ks + 1] >> 16);
+        av[0] = (short)(areg[4 * ks] & 0xffffu);
+        av[1] = (short)(areg[4 * ks] >> 16);
+        av[2] = (short)(areg[4 * ks + 1] & 0xffffu);
+        av[3] = (short)(areg[4 * ks + 1] >> 16);
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
           const short4_t bv =
-              *reinterpret_cast<const short4_t*>(&s_w[nb * 16 + (l & 15)][q * rq + 4 * ks]);
+              *reinterpret_cast<const short4_t*>(&s_w[nb * 16 + row16][32 * ks + 4 * q]);
           acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, acc[nb], 0, 0, 0);
         }
       }
     }
-    if (tile + (int)gridDim.x < a.tiles) load_a(tile + gridDim.x);
-    // lane l holds rows 16w + 4q + j of requests 16 nb + (l & 15): through
+    // lane l holds rows 16w + 4q + j of requests 16 nb + l % 16: through
     // LDS to [request][row]
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) s_c[nb * 16 + (l & 15)][w * 16 + 4 * q + j] = acc[nb][j];
+      for (int j = 0; j < 4; ++j) s_c[nb * 16 + row16][w * 16 + 4 * q + j] = acc[nb][j];
     __syncthreads();
     // epilogue: corrected logits of this lane's 16 rows, stored, and the
     // tile's summary per request over the four lanes that share it
+    float xb[16];
+    if (full) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if constexpr (DT == DSPARK_BF16)
+          xb[i] = __uint_as_float((i & 1) ? (xraw[i >> 1] & 0xffff0000u) : (xraw[i >> 1] << 16));
+        else
+          xb[i] = __uint_as_float(xraw[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xb[i] = load_elem<DT>(brow, min(vt + row_of(i), V - 1));
+    }
     float xs[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float x = xb[i] + a.scale * s_c[w * 16 + ri][part * 16 + i];
+      const float x = xb[i] + a.scale * s_c[w * 16 + ri][row_of(i)];
       // rounded to the storage dtype (bf16: nearest even)
       float st;
       if constexpr (DT == DSPARK_BF16) {
@@ -202,12 +251,12 @@ __global__ void __launch_bounds__(256) k_markov_bias(MarkovArgs a) {
       } else {
         st = x;
       }
-      xs[i] = bok && vbeg + i < V ? st : -INFINITY;
+      xs[i] = bok && vt + row_of(i) < V ? st : -INFINITY;
     }
     if (bok) {
       if (full) {
 #pragma unroll
-        for (int g = 0; g < 16 / kVecElems; ++g) {
+        for (int g = 0; g < kPieces; ++g) {
           uint32_t wd[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -217,13 +266,14 @@ __global__ void __launch_bounds__(256) k_markov_bias(MarkovArgs a) {
             else
               wd[e] = __float_as_uint(xs[g * 4 + e]);
           }
-          *reinterpret_cast<uint4*>(crow + (size_t)(vbeg + g * kVecElems) * Elem<DT>::kBytes) =
+          *reinterpret_cast<uint4*>(
+              crow + (size_t)(vt + g * 4 * kVecElems + part * kVecElems) * Elem<DT>::kBytes) =
               uint4{wd[0], wd[1], wd[2], wd[3]};
         }
       } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (vbeg + i < V) store_elem<DT>(crow, vbeg + i, xs[i]);
+          if (vt + row_of(i) < V) store_elem<DT>(crow, vt + row_of(i), xs[i]);
       }
     }
     float m = xs[0];
@@ -239,8 +289,8 @@ __global__ void __launch_bounds__(256) k_markov_bias(MarkovArgs a) {
     if (greedy) {
       int at = 0x7fffffff;
 #pragma unroll
-      for (int i = 15; i >= 0; --i)
-        if (xs[i] == m && vbeg + i < V) at = vbeg + i;
+      for (int i = 15; i >= 0; --i)  // rows increase with i
+        if (xs[i] == m && vt + row_of(i) < V) at = vt + row_of(i);
       at = min(at, dpp<kQuadXor1>(at));
       at = min(at, dpp<kQuadXor2>(at));
       pt.k = m;
@@ -266,16 +316,21 @@ __global__ void __launch_bounds__(256) k_markov_bias(MarkovArgs a) {
     }
     if (bok && part == 0) a.part[(size_t)bl * a.tiles + tile] = pt;
     __syncthreads();  // s_c is rewritten by the next tile
+#pragma unroll
+    for (int i = 0; i < kAw; ++i) areg[i] = anext[i];
+#pragma unroll
+    for (int i = 0; i < kXw; ++i) xraw[i] = xnext[i];
   }
   if (bad) flag(a.dev_status, bad);
 }
 
 // block-wide helpers of k_markov_draw (256 threads, 4 waves)
+constexpr int kRun = 16;  // tile summaries a draw thread keeps in registers
 struct DrawLds {
   double w[4];
   float f[4];
   int i[4];
-  int tile, found;
+  int tile;
   double base;
 };
 
@@ -329,24 +384,45 @@ __global__ void __launch_bounds__(256) k_markov_draw(MarkovArgs a) {
   } else {
     const float c = temp_c(T);
     const double u = (double)a.uniforms[(size_t)b * K + (k - 1)];
-    // shift of the row: the largest tile shift
+    // each thread owns a contiguous run of tiles, read once: the first kRun
+    // summaries stay in registers (runs are longer only past 2^18 tokens)
+    const int per = (nt + 255) / 256;
+    const int t0 = min(tid * per, nt), t1 = min(t0 + per, nt);
+    float rk[kRun];
+    double rs[kRun];
     float km = -INFINITY;
-    for (int t = tid; t < nt; t += 256) km = fmaxf(km, pr[t].k);
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) {
+      rk[j] = -INFINITY;
+      rs[j] = 0.0;
+      if (t0 + j < t1) {
+        const Partial p = pr[t0 + j];
+        rk[j] = p.k;
+        rs[j] = p.s;
+        km = fmaxf(km, p.k);
+      }
+    }
+    for (int t = t0 + kRun; t < t1; ++t) km = fmaxf(km, pr[t].k);
+    // shift of the row: the largest tile shift
     km = wave_max(km);
     if (l == 0) sh.f[w] = km;
     __syncthreads();
     km = fmaxf(fmaxf(sh.f[0], sh.f[1]), fmaxf(sh.f[2], sh.f[3]));
-    // each thread owns a contiguous run of tiles; its mass, then a block scan
-    const int per = (nt + 255) / 256;
-    const int t0 = min(tid * per, nt), t1 = min(t0 + per, nt);
-    auto mass = [&](int t) -> double {
-      const Partial p = pr[t];
-      return p.s > 0.0 ? ldexp(p.s, shift_amount(p.k - km)) : 0.0;
+    auto scaled = [&](float pk, double ps) -> double {
+      return ps > 0.0 ? ldexp(ps, shift_amount(pk - km)) : 0.0;
     };
+    // the run's mass, then a block scan
     double own = 0.0;
     int lastpos = -1;
-    for (int t = t0; t < t1; ++t) {
-      const double mt = mass(t);
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) {
+      const double mt = scaled(rk[j], rs[j]);
+      own += mt;
+      if (mt > 0.0) lastpos = t0 + j;
+    }
+    for (int t = t0 + kRun; t < t1; ++t) {
+      const Partial p = pr[t];
+      const double mt = scaled(p.k, p.s);
       own += mt;
       if (mt > 0.0) lastpos = t;
     }
@@ -382,8 +458,18 @@ __global__ void __launch_bounds__(256) k_markov_draw(MarkovArgs a) {
       double run = before_me;
       int tt = -1;
       double tb = 0.0;
-      for (int t = t0; t < t1 && tt < 0; ++t) {
-        const double mt = mass(t);
+#pragma unroll
+      for (int j = 0; j < kRun; ++j) {
+        const double mt = scaled(rk[j], rs[j]);
+        if (tt < 0 && mt > 0.0 && run + mt > target) {
+          tt = t0 + j;
+          tb = run;
+        }
+        run += mt;
+      }
+      for (int t = t0 + kRun; t < t1 && tt < 0; ++t) {
+        const Partial p = pr[t];
+        const double mt = scaled(p.k, p.s);
         if (mt > 0.0 && run + mt > target) {
           tt = t;
           tb = run;
@@ -396,34 +482,25 @@ __global__ void __launch_bounds__(256) k_markov_draw(MarkovArgs a) {
       }
     }
     __syncthreads();
+    // the tile's 64 tokens, one per lane of wave 0, which also stores the
+    // result
+    if (w != 0) return;
     const int tile = max(sh.tile, 0);
     const double base = sh.base;
-    // the tile's 64 tokens, one per lane of wave 0
-    if (w == 0) {
-      const Partial p = pr[tile];
-      const int v = tile * kMarkovRows + l;
-      const float x = v < V ? load_elem<DT>(crow, v) : -INFINITY;
-      const double m = v < V ? ldexp((double)fast_exp2(fmaf(x, c, p.k == -INFINITY ? 0.f : -p.k)),
-                                     shift_amount(p.k - km))
-                             : 0.0;
-      const double inc = wave_incl_scan(m);
-      const bool past = base < 0.0;  // no crossing: the last token with mass
-      const uint64_t hit = __ballot(!past && m > 0.0 && base + inc > target);
-      const int lastm = wave_max_i(m > 0.0 ? l : -1);
-      const int pick = hit ? __builtin_ctzll(hit) : (lastm >= 0 ? lastm : 0);
-      const float xp = __shfl(x, pick);
-      y = tile * kMarkovRows + pick;
-      qy = row_prob(xp, c, km, S);
-      if (l == 0) sh.found = y;
-    }
-    __syncthreads();
-    y = sh.found;
-    qy = 0.0;
-    if (w == 0) {
-      // (recomputed in wave 0 for the stored probability)
-      const float xp = load_elem<DT>(crow, min(y, V - 1));
-      qy = row_prob(xp, c, km, S);
-    }
+    const Partial p = pr[tile];
+    const int v = tile * kMarkovRows + l;
+    const float x = v < V ? load_elem<DT>(crow, v) : -INFINITY;
+    const double m = v < V ? ldexp((double)fast_exp2(fmaf(x, c, p.k == -INFINITY ? 0.f : -p.k)),
+                                   shift_amount(p.k - km))
+                           : 0.0;
+    const double inc = wave_incl_scan(m);
+    const bool past = base < 0.0;  // no crossing: the last token with mass
+    const uint64_t hit = __ballot(!past && m > 0.0 && base + inc > target);
+    const int lastm = wave_max_i(m > 0.0 ? l : -1);
+    const int pick = hit ? __builtin_ctzll(hit) : (lastm >= 0 ? lastm : 0);
+    const float xp = __shfl(x, pick);
+    y = tile * kMarkovRows + pick;
+    qy = row_prob(xp, c, km, S);
   }
   if (tid == 0) {
     a.drafted[(size_t)b * K + (k - 1)] = y;

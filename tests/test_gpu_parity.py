@@ -695,7 +695,9 @@ def _markov_case(B, K, V, r, dtype, seed, temps, fixed=True, requests=None, scal
 
 
 @pytest.mark.parametrize("B,K,V,r,dtype", [(4, 3, 1000, 64, "bf16"), (70, 2, 5000, 128, "bf16"),
-                                           (6, 4, 151936, 256, "bf16"), (3, 3, 4100, 32, "f32")])
+                                           (6, 4, 151936, 256, "bf16"), (3, 3, 4100, 32, "f32"),
+                                           (5, 2, 3000, 48, "bf16"), (3, 2, 777, 16, "f32"),
+                                           (2, 2, 1001, 80, "bf16"), (3, 2, 300000, 16, "bf16")])
 def test_markov_draft_parity(B, K, V, r, dtype):
     reqs = list(range(B)) if B <= 8 else [0, 1, 33, 63, 64, 69]
     gc, gy, gq, st, rc, ry, rq, dist, T = _markov_case(B, K, V, r, dtype, seed=B + V, temps=[1.0, 0.0, 0.7],
