@@ -74,6 +74,8 @@ __device__ __forceinline__ float store_elem(void* row, int v, float x) {
 
 }  // namespace
 
+static_assert(kMarkovBatch * 4 == 256, "four staging threads per request");
+
 template <int DT>
 __global__ void __launch_bounds__(256) k_markov_bias(MarkovArgs a) {
   constexpr int kLds = kMarkovMaxRank + 8;  // padded row of a staged Vm row (bf16)
@@ -163,18 +165,28 @@ __global__ void __launch_bounds__(256) k_markov_bias(MarkovArgs a) {
     load_a(blockIdx.x, areg);
     load_base(blockIdx.x, xraw);
   }
-  // the previous tokens' rows of Vm, 16 bytes at a time (zero rows past B),
-  // staged once for all the tiles this workgroup takes
-  const int pieces = r / 8;
-  for (int e = threadIdx.x; e < kMarkovBatch * pieces; e += 256) {
-    const int i = e / pieces, piece = e - i * pieces;
+  // the previous tokens' rows of Vm (zero rows past B), staged once for all
+  // the tiles this workgroup takes: four threads per request, each with one
+  // token load and then all its 16-byte pieces in flight at once (the four
+  // threads cover 64 contiguous bytes per step)
+  {
+    const int i = threadIdx.x >> 2, sub = threadIdx.x & 3;
     const int b = b0 + i;
-    uint4 v = {0u, 0u, 0u, 0u};
-    if (b < a.B) {
-      const int prev = prev_token(a, b, bad);
-      v = *reinterpret_cast<const uint4*>(a.Vm + (size_t)prev * r + piece * 8);
+    const int pieces = r / 8;
+    const uint16_t* vrow = nullptr;
+    if (b < a.B) vrow = a.Vm + (size_t)prev_token(a, b, bad) * r;
+    uint4 v[kMarkovMaxRank / 32];
+#pragma unroll
+    for (int j = 0; j < kMarkovMaxRank / 32; ++j) {
+      const int piece = 4 * j + sub;
+      v[j] = uint4{0u, 0u, 0u, 0u};
+      if (vrow && piece < pieces) v[j] = *reinterpret_cast<const uint4*>(vrow + piece * 8);
     }
-    *reinterpret_cast<uint4*>(&s_w[i][piece * 8]) = v;
+#pragma unroll
+    for (int j = 0; j < kMarkovMaxRank / 32; ++j) {
+      const int piece = 4 * j + sub;
+      if (piece < pieces) *reinterpret_cast<uint4*>(&s_w[i][piece * 8]) = v[j];
+    }
   }
   __syncthreads();
   for (int tile = blockIdx.x; tile < a.tiles; tile += gridDim.x) {
@@ -341,33 +353,52 @@ __global__ void __launch_bounds__(256) k_markov_draw(MarkovArgs a) {
   const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
   const int K = a.K, V = a.V, k = a.step, nt = a.tiles;
   const Partial* pr = a.part + (size_t)b * nt;
-  const float T = a.temperature[b];
   const size_t roff = ((size_t)b * K + (k - 1)) * (size_t)V;
   const void* crow = static_cast<const char*>(a.corrected) + roff * Elem<DT>::kBytes;
+  // each thread owns a contiguous run of tiles; the first kRun summaries are
+  // read into registers at once, together with the temperature and the
+  // uniform (runs are longer only past 2^18 tokens: the rest is re-read)
+  const int per = (nt + 255) / 256;
+  const int t0 = min(tid * per, nt), t1 = min(t0 + per, nt);
+  float rk[kRun];
+  int rx[kRun];
+  double rs[kRun];
+#pragma unroll
+  for (int j = 0; j < kRun; ++j) {
+    rk[j] = -INFINITY;
+    rx[j] = 0x7fffffff;
+    rs[j] = 0.0;
+    if (t0 + j < t1) {
+      const Partial p = pr[t0 + j];
+      rk[j] = p.k;
+      rx[j] = p.idx;
+      rs[j] = p.s;
+    }
+  }
+  const float T = a.temperature[b];
+  const double u = (double)a.uniforms[(size_t)b * K + (k - 1)];
   int y = 0;
   double qy = 1.0;
   if (!(T >= 0.f)) {
     if (tid == 0) flag(a.dev_status, DSPARK_DEV_BAD_TEMP);
   } else if (T == 0.f) {
-    // the lowest-index maximum over the tiles (tiles in index order)
+    // the lowest-index maximum over the tiles
     float m = -INFINITY;
     int mi = 0x7fffffff;
-    for (int t = tid; t < nt; t += 256) {
-      const Partial p = pr[t];
-      if (p.k > m || (p.k == m && p.idx < mi)) {
-        m = p.k;
-        mi = p.idx;
+    auto take = [&](float pk, int pi) {
+      if (pk > m || (pk == m && pi < mi)) {
+        m = pk;
+        mi = pi;
       }
+    };
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) take(rk[j], rx[j]);
+    for (int t = t0 + kRun; t < t1; ++t) {
+      const Partial p = pr[t];
+      take(p.k, p.idx);
     }
     // wave, then block
-    for (int o = 32; o > 0; o >>= 1) {
-      const float om = __shfl_xor(m, o);
-      const int oi = __shfl_xor(mi, o);
-      if (om > m || (om == m && oi < mi)) {
-        m = om;
-        mi = oi;
-      }
-    }
+    for (int o = 32; o > 0; o >>= 1) take(__shfl_xor(m, o), __shfl_xor(mi, o));
     if (l == 0) {
       sh.f[w] = m;
       sh.i[w] = mi;
@@ -375,33 +406,13 @@ __global__ void __launch_bounds__(256) k_markov_draw(MarkovArgs a) {
     __syncthreads();
     m = sh.f[0];
     mi = sh.i[0];
-    for (int ww = 1; ww < 4; ++ww)
-      if (sh.f[ww] > m || (sh.f[ww] == m && sh.i[ww] < mi)) {
-        m = sh.f[ww];
-        mi = sh.i[ww];
-      }
+    for (int ww = 1; ww < 4; ++ww) take(sh.f[ww], sh.i[ww]);
     y = mi < V ? mi : 0;
   } else {
     const float c = temp_c(T);
-    const double u = (double)a.uniforms[(size_t)b * K + (k - 1)];
-    // each thread owns a contiguous run of tiles, read once: the first kRun
-    // summaries stay in registers (runs are longer only past 2^18 tokens)
-    const int per = (nt + 255) / 256;
-    const int t0 = min(tid * per, nt), t1 = min(t0 + per, nt);
-    float rk[kRun];
-    double rs[kRun];
     float km = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kRun; ++j) {
-      rk[j] = -INFINITY;
-      rs[j] = 0.0;
-      if (t0 + j < t1) {
-        const Partial p = pr[t0 + j];
-        rk[j] = p.k;
-        rs[j] = p.s;
-        km = fmaxf(km, p.k);
-      }
-    }
+    for (int j = 0; j < kRun; ++j) km = fmaxf(km, rk[j]);
     for (int t = t0 + kRun; t < t1; ++t) km = fmaxf(km, pr[t].k);
     // shift of the row: the largest tile shift
     km = wave_max(km);
