@@ -254,16 +254,20 @@ __global__ void __launch_bounds__(256) k_markov_bias(MarkovArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float x = xb[i] + a.scale * s_c[w * 16 + ri][row_of(i)];
-      // rounded to the storage dtype (bf16: nearest even)
-      float st;
+      // rounded to the storage dtype (bf16: nearest even; a NaN here is
+      // flagged below, and the request's outputs are then unspecified)
       if constexpr (DT == DSPARK_BF16) {
         const uint32_t u = __float_as_uint(x);
-        const uint32_t h = x != x ? 0x7fc0u : ((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-        st = __uint_as_float(h << 16);
+        xs[i] = __uint_as_float((u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u);
       } else {
-        st = x;
+        xs[i] = x;
       }
-      xs[i] = bok && vt + row_of(i) < V ? st : -INFINITY;
+    }
+    // rows past V (ragged last tile) and lanes past B take no part
+    if (!full || !bok) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (!bok || vt + row_of(i) >= V) xs[i] = -INFINITY;
     }
     if (bok) {
       if (full) {
@@ -291,10 +295,12 @@ __global__ void __launch_bounds__(256) k_markov_bias(MarkovArgs a) {
     float m = xs[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) m = fmaxf(m, xs[i]);
-    bool nonfinite = false;
+    // NaN or +inf among the values: a scaled sum (no overflow from finite
+    // values) is NaN or +inf exactly then; -inf alone leaves it -inf
+    float fin = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) nonfinite |= xs[i] != xs[i] || xs[i] == INFINITY;
-    if (nonfinite) bad |= DSPARK_DEV_NONFINITE;
+    for (int i = 0; i < 16; ++i) fin = fmaf(xs[i], 0x1p-8f, fin);
+    if (fin != fin || fin == INFINITY) bad |= DSPARK_DEV_NONFINITE;
     m = fmaxf(m, dpp<kQuadXor1>(m));
     m = fmaxf(m, dpp<kQuadXor2>(m));
     Partial pt;

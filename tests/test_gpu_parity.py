@@ -853,3 +853,26 @@ def test_graph_capture_replay_next_rows():
         assert torch.equal(th_g, th_e) and torch.equal(s_g, s_e), rep
         moved += int(not torch.equal(th_g, th0))
     assert moved >= 2                                # window ends fell inside the replays
+
+
+def test_markov_draft_nonfinite_flag():
+    # -inf logits (masked tokens) are valid; NaN or +inf in the corrected
+    # logits raise the non-finite flag
+    B, K, V, r = 3, 2, 3000, 32
+    rng = np.random.default_rng(6)
+    base = oracle.bf16_round(rng.normal(size=(B, K, V)).astype(np.float32))
+    base[:, :, ::7] = 0xff80                          # -inf (bf16 bits)
+    U = _to_bf16_tensor(_fixed_bf16(rng, (V, r)))
+    y0 = torch.tensor([1, 2, 3], dtype=torch.int32, device=DEV)
+    T = torch.tensor([1.0, 0.0, 0.5], device=DEV)
+    u = torch.full((B, K), 0.5, device=DEV)
+    _, y, _, st = ds.markov_draft(_to_bf16_tensor(base), U, U, 1.0, y0, T, u)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.all(host(y) % 7 != 0)                  # masked tokens are never drawn
+    for bad_bits, at in ((0x7fc0, (1, 0, 77)), (0x7f80, (2, 1, 2999)), (0xffc1, (0, 1, 64))):
+        b2 = base.copy()
+        b2[at] = bad_bits                            # NaN, +inf, negative NaN
+        _, _, _, st = ds.markov_draft(_to_bf16_tensor(b2), U, U, 1.0, y0, T, u)
+        torch.cuda.synchronize()
+        assert int(st.item()) & oracle.DEV_NONFINITE, (hex(bad_bits), at)
