@@ -22,7 +22,9 @@ peak: its algorithmic bytes per launch, s*V*sum_b rows_b with rows_b = 2 L_b + 1
 that the library records on its own stream around that launch.  ``traffic`` is
 the HBM bytes per launch that rocprofv3 counters measured for the same kernel
 (profiles/k_stream_rows_b64_k16_v151936_pmc.md), used only while the kernel
-sources still hash to the recorded value.  ``cpu_baseline`` times the CPU
+sources still hash to the recorded value.  ``contiguous_read_reference`` times
+dspark_read_probe, a plain read of the same byte count in the same launch
+shape, as the yardstick of what a read-only kernel reaches at this size.  ``cpu_baseline`` times the CPU
 oracle on a bounded sample of the same workload.
 
 ``rows`` times, apart from the step, the hot-path rows the step does not
@@ -31,7 +33,9 @@ schedule with a binding budget, the load-aware schedule (threshold and budget
 from an engine load and a throughput curve), online calibration (temperature
 scaling and one round into the calibration window), Markov logit-bias drafting
 of the workload's block and a mixed-temperature batch of 1024 requests
-(``--no-rows`` skips them).
+(``--no-rows`` skips them).  ``V_length_sweep`` times the streaming pass at
+uniform lengths 0..16 beside the plain read of the same bytes and fits each
+with a line: bandwidth (slope) and fixed cost per launch (intercept).
 
 --calibrate-copy N runs, after the timed steps, a plain elementwise copy of
 N MiB (read N MiB, write N MiB) five times: the reference kernel of known size
@@ -127,7 +131,51 @@ def time_calls(fn, reps, stream, torch):
     return ms[len(ms) // 2], sum(ms) / len(ms)
 
 
-def row_measurements(ds, workloads, sets, outs, ws_v, dev, stream, torch, np, log):
+class ReadProbe:
+    """Plain contiguous reads (dspark_read_probe) of a given byte count, each
+    call at an offset at least 300 MB past the previous one in a 2.2 GB
+    buffer, so that, like the rotating input sets, no call reads bytes left
+    in the 256 MB last-level cache by the calls before it."""
+
+    SPAN = 2_200_000_000
+    STRIDE = 300_000_000
+
+    def __init__(self, ds, torch, dev):
+        self.ds, self.torch = ds, torch
+        self.buf = torch.empty(self.SPAN, dtype=torch.uint8, device=dev)  # contents irrelevant
+        self.sink = torch.zeros(4, dtype=torch.int32, device=dev)
+        self.k = 0
+
+    def call(self, nbytes, stream):
+        nbytes = nbytes // 16 * 16
+        step = max(self.STRIDE, nbytes) // 256 * 256 + 256
+        room = self.SPAN - nbytes
+        off = (self.k * step) % room // 256 * 256
+        self.k += 1
+        self.ds.read_probe(self.buf[off:], nbytes, self.sink, stream)
+
+    def timed(self, nbytes, reps, stream, np):
+        """Mean event-timed duration (ms) of `reps` calls, the host queued ahead."""
+        torch = self.torch
+        for _ in range(4):
+            self.call(nbytes, stream)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for e in evs:
+            for x in e:
+                x.record(stream)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(SPIN_CYCLES)
+        for e0, e1 in evs:
+            e0.record(stream)
+            self.call(nbytes, stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def row_measurements(ds, workloads, sets, outs, ws_v, dev, stream, torch, np, log, probe):
     """The hot-path rows the headline step does not exercise, each timed
     apart (not part of `value`): the greedy rule, full-length blocks, a
     binding budget, the load-aware schedule, online calibration, Markov
@@ -196,6 +244,36 @@ def row_measurements(ds, workloads, sets, outs, ws_v, dev, stream, torch, np, lo
                              "stream_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
                              "stream_us_mean": round(t_s * 1e3, 2), "call_us_median": round(t_c * 1e3, 2),
                              "positions_per_s": round(B * K / (t_c / 1e3), 1)}
+
+    # The streaming pass against its byte count: every length = L for several
+    # L, a least-squares line through (bytes, time), and the plain contiguous
+    # read of the same byte counts beside it.  The slope is the pass's
+    # bandwidth once it runs; the intercept its fixed cost per launch.
+    sweep = []
+    for Lx in (0, 2, 4, 8, 16):
+        lx = torch.full((B,), Lx, dtype=torch.int32, device=dev)
+
+        def vl(i, lx=lx):
+            w = sets[i % n]
+            ds.verify(w.target, w.draft, w.drafted, lx, w.temperature, w.uniforms, accepted=accf,
+                      tokens=tokf, p_tok=ptf, q_tok=qtf, dev_status=st_, ws=ws_v, stream=stream)
+        for i in range(n):
+            vl(i)
+        by = s * V * B * (2 * Lx + 1)
+        t_s, _ = stream_timed(vl, 18)
+        t_p = probe.timed(by, 18, stream, np)
+        sweep.append((by, t_s * 1e3, t_p * 1e3))
+    xb = np.array([x[0] for x in sweep], dtype=np.float64)
+    fit_s = np.polyfit(xb, [x[1] for x in sweep], 1)
+    fit_p = np.polyfit(xb, [x[2] for x in sweep], 1)
+    rows["V_length_sweep"] = {
+        "workload": "b64-k16-v151936 logits, every length = L for L in 0, 2, 4, 8, 16",
+        "points": [{"L": Lx, "bytes": int(by), "stream_us": round(ts, 2), "read_us": round(tp, 2)}
+                   for Lx, (by, ts, tp) in zip((0, 2, 4, 8, 16), sweep)],
+        "stream_slope_gbs": round(1e-3 / fit_s[0], 1), "stream_intercept_us": round(fit_s[1], 2),
+        "read_slope_gbs": round(1e-3 / fit_p[0], 1), "read_intercept_us": round(fit_p[1], 2),
+        "note": "read = dspark_read_probe, a plain contiguous read of the same bytes in the same "
+                "launch shape"}
 
     # S3 and the mixed batch: workload b1024-k8-v151936 (temperatures 0 / 0.6 / 1)
     w5 = workloads.make(5, device=dev)
@@ -493,6 +571,12 @@ def main():
     mean_acc = float(np.mean([a.mean() for a, _ in accs]))
     waste = float(np.mean([1 - a.sum() / max(1, L.sum()) for a, L in accs]))
     traffic, traffic_note = measured_traffic()
+    # the plain contiguous read of the same byte count in the same launch
+    # shape: what a kernel that only reads achieves at this size
+    probe = ReadProbe(ds, torch, dev)
+    ref_bytes = round(s_bytes / args.steps) // 16 * 16
+    ref_ms = probe.timed(ref_bytes, 30, stream, np)
+    ref_gbs = ref_bytes / (ref_ms / 1e3) / 1e9
     # every input set scheduled once (short runs leave some unscheduled), so
     # that the rows read valid lengths
     for i in range(len(sets)):
@@ -539,11 +623,16 @@ def main():
             "schedule_us_median": round(float(np.median(sched_ms)) * 1e3, 2),
             "kernel_timing": "separate pass over the same steps, events around each call and "
                              "(library-recorded, same stream) around each streaming launch",
+            "contiguous_read_reference": {
+                "bytes": ref_bytes, "us_mean": round(ref_ms * 1e3, 2), "gbs": round(ref_gbs, 1),
+                "frac": round(ref_gbs / HBM_PEAK_GBS, 4),
+                "note": "dspark_read_probe: the same bytes read contiguously, same launch shape, "
+                        "events around the call"},
         },
         "accepted_mean": round(mean_acc, 3),
         "waste_ratio": round(waste, 4),
         "rows": None if args.no_rows else row_measurements(ds, workloads, sets, outs, ws_v, dev,
-                                                             stream, torch, np, log),
+                                                             stream, torch, np, log, probe),
     }
 
     if args.calibrate_copy > 0:
@@ -573,7 +662,7 @@ def main():
             runs += 1
             cpu_pos += int(L.sum())
             el = time.perf_counter() - t0
-            if el >= args.cpu_seconds or runs >= 50:
+            if el >= args.cpu_seconds or runs >= 400:
                 break
         result["cpu_baseline"] = {
             "value": round(cpu_pos / el, 2),

@@ -38,7 +38,7 @@ ERR_PARAM = 7
 EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_schedule",
            "dspark_schedule_load_aware", "dspark_calibrate", "dspark_calib_state_bytes",
            "dspark_calib_observe", "dspark_markov_draft", "dspark_verify", "dspark_verify_greedy",
-           "dspark_set_stream_events")
+           "dspark_set_stream_events", "dspark_read_probe")
 
 
 class DsparkError(RuntimeError):
@@ -85,6 +85,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dspark_verify_greedy.restype = i32
     lib.dspark_set_stream_events.argtypes = [vp, vp]
     lib.dspark_set_stream_events.restype = i32
+    lib.dspark_read_probe.argtypes = [vp, sz, vp, vp]
+    lib.dspark_read_probe.restype = i32
     _lib = lib
     return lib
 
@@ -109,6 +111,16 @@ def dspark_set_stream_events(before, after) -> None:
             raise ValueError("event has no HIP handle yet: record it once first")
         return h
     _check(load_library().dspark_set_stream_events(handle(before), handle(after)))
+
+
+def read_probe(x, nbytes: int, sink, stream=None) -> None:
+    """Plain contiguous read of the first ``nbytes`` bytes of device tensor
+    ``x`` (the bandwidth reference for the streaming pass); ``sink`` is a
+    device tensor of at least 4 bytes."""
+    if nbytes > x.numel() * x.element_size():
+        raise ValueError("nbytes past the end of x")
+    _check(load_library().dspark_read_probe(_ptr(x), int(nbytes), _ptr(sink),
+                                            _stream(stream, x.device)))
 
 
 def _check(status: int):

@@ -10,7 +10,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["api.hip", "schedule.hip", "verify.hip", "calib.hip", "markov.hip"]
+SOURCES = ["api.hip", "schedule.hip", "verify.hip", "calib.hip", "markov.hip", "probe.hip"]
 LIB = os.path.join(HERE, "libdspark.so")
 
 FLAGS = [

@@ -53,6 +53,9 @@ hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
 
 }  // namespace
 
+// the plain-read reference kernel (probe.hip)
+int launch_read_probe(const void* x, size_t bytes, uint32_t* sink, hipStream_t st);
+
 // Compute units of the current device (cached per device; 256 if the query
 // fails).
 int compute_units() {
@@ -341,6 +344,12 @@ int dspark_set_stream_events(void* before, void* after) {
     g_ev_before = g_ev_after = nullptr;
   }
   return DSPARK_OK;
+}
+
+int dspark_read_probe(const void* x, size_t bytes, uint32_t* sink, void* stream) {
+  if (!x || !sink) return DSPARK_ERR_NULL;
+  if (bytes == 0 || bytes % 16 != 0 || !aligned(x, 16)) return DSPARK_ERR_PARAM;
+  return launch_read_probe(x, bytes, sink, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

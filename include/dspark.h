@@ -84,7 +84,7 @@ typedef enum {
   DSPARK_ERR_BUDGET = 4,    /* budget >= 0 but < B*min_len, or min_len not in [0,K] */
   DSPARK_ERR_WORKSPACE = 5, /* ws_bytes too small or workspace misaligned         */
   DSPARK_ERR_LAUNCH = 6,    /* the HIP runtime rejected a launch                  */
-  DSPARK_ERR_PARAM = 7      /* a load-aware parameter out of range (see dspark_schedule_load_aware) */
+  DSPARK_ERR_PARAM = 7      /* a parameter out of range or misaligned (per call)  */
 } dspark_status;
 
 typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
@@ -363,6 +363,22 @@ DSPARK_API int dspark_verify_greedy(const void* target_logits, int dtype, int B,
  * calls, and keep the events alive while it is set. Returns DSPARK_OK.
  */
 DSPARK_API int dspark_set_stream_events(void* before, void* after);
+
+/*
+ * dspark_read_probe — plain contiguous read of a device buffer (measurement
+ * support; the pages define no such call).
+ *
+ * Reads `bytes` bytes at `x` once, in the launch shape of the streaming pass
+ * (one 768-thread workgroup per compute unit, 8 KB tiles of coalesced
+ * 16-byte loads per wave), and computes nothing from them that reaches
+ * memory: `sink` (one uint32_t of device memory) is written only if a
+ * checksum of the data equals a fixed constant. It is the reference with
+ * which the streaming pass's bandwidth at the same byte count is compared.
+ * Work goes onto `stream`; nothing is allocated.
+ * Errors: NULL x or sink (DSPARK_ERR_NULL); bytes zero or not a multiple of
+ * 16, or x not 16-byte aligned (DSPARK_ERR_PARAM).
+ */
+DSPARK_API int dspark_read_probe(const void* x, size_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -176,3 +176,13 @@ def test_stream_events_hook_off_without_gpu():
     assert lib.dspark_set_stream_events(None, None) == 0
     assert lib.dspark_set_stream_events(P, None) == 0
     ds.dspark_set_stream_events(None, None)
+
+
+def test_read_probe_argument_errors():
+    # checks come before any launch: NULL pointers, sizes, alignment
+    lib = ds.load_library()
+    assert lib.dspark_read_probe(None, 16, P, None) == 1
+    assert lib.dspark_read_probe(P, 16, None, None) == 1
+    assert lib.dspark_read_probe(P, 0, P, None) == ds.ERR_PARAM
+    assert lib.dspark_read_probe(P, 24, P, None) == ds.ERR_PARAM
+    assert lib.dspark_read_probe(P + 8, 32, P, None) == ds.ERR_PARAM

@@ -519,6 +519,18 @@ def test_graph_capture_replay():
 
 # ---------------------------------------------------------------- timing hook
 
+@pytest.mark.parametrize("nbytes", [16, 8192 * 3 + 48, 82_450_608])
+def test_read_probe_reads_and_writes_nothing(nbytes):
+    # the plain-read reference: whole tiles and a ragged tail; the sink keeps
+    # its value (the checksum of random data is not the magic constant)
+    x = torch.randint(0, 256, (nbytes + 64,), dtype=torch.uint8, device=DEV)
+    sink = torch.full((4,), 7, dtype=torch.int32, device=DEV)
+    print(f"read probe {nbytes} bytes", flush=True)
+    ds.read_probe(x, nbytes, sink)
+    torch.cuda.synchronize()
+    assert sink.tolist() == [7, 7, 7, 7]
+
+
 def test_stream_events_bracket_the_streaming_pass():
     w = workloads.make(3, device=DEV)
     lengths, _, _, _ = _sched(w)
