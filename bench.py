@@ -1,15 +1,18 @@
 """Benchmark: verified draft positions per second and achieved HBM bandwidth of
 confidence-scheduled block verification on one MI355X.
 
-One step = dspark_schedule + dspark_verify over one batch of the
+One step = the schedule and the verification of one batch of the
 V=151936, B=64, K=16 workload (bf16 logits, T=1, threshold 0.2, budget 512;
-seeded synthetic inputs resident in HBM).  Six input sets (seed offsets
+seeded synthetic inputs resident in HBM), as one dspark_schedule_verify call,
+which works the schedule out inside the streaming launch; the same steps as
+two calls (dspark_schedule, then dspark_verify) are timed beside it
+(``config.two_call_us_per_step``).  Six input sets (seed offsets
 0, 100, ..., 500; 641 MB each) rotate so that no step reads logits left in the
 256 MB last-level cache by the step before.
 
 The timed region launches the K steps directly on one stream with nothing
 in between (``--graphs`` replays each step from its own HIP graph instead,
-which is slower on this stack).  Kernel times (schedule, verify, streaming
+which is slower on this stack).  Kernel times (the call, the streaming
 pass) come from a separate pass over the same steps with events around each
 call and, recorded by the library on the same stream, around each streaming
 launch.
@@ -58,7 +61,8 @@ HBM_PEAK_GBS = 8000.0
 SPIN_CYCLES = 20_000_000  # GPU clock cycles the pre-queued spin kernel runs for
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_stream_rows_b64_k16_v151936_pmc.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "draft_verification_dspark_amd", "csrc", f)
-                  for f in ("verify.hip", "device.hpp", "args.hpp")]
+                  for f in ("verify.hip", "device.hpp", "args.hpp", "schedule_core.hpp",
+                            "schedule_args.hpp")]
 METRIC = "verified draft positions/sec and achieved HBM GB/s vs peak (V=151936, B=64, K=16)"
 
 
@@ -471,26 +475,34 @@ def main():
             st=torch.zeros(1, dtype=torch.int32, device=dev)))
     ws_s = ds.workspace(ds.OP_SCHEDULE, B, K, 1, dev)
     ws_v = ds.workspace(ds.OP_VERIFY, B, K, V, dev)
+    ws_sv = ds.workspace(ds.OP_SCHEDULE_VERIFY, B, K, V, dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(i, cur, ev=None):
-        """One step on stream `cur`; with `ev` = five events: around schedule,
-        around verify, and (recorded by the library) around the streaming
+        """One step on stream `cur`: dspark_schedule_verify (the schedule
+        worked out inside the streaming pass); with `ev` = three events:
+        around the call, and (recorded by the library) around the streaming
         launch."""
         w, o = sets[i % len(sets)], outs[i % len(sets)]
         if ev is not None:
             ev[0].record(cur)
+            ds.dspark_set_stream_events(ev[1], ev[2])
+        ds.schedule_verify(w.conf, w.threshold, w.budget, w.min_len, w.target, w.draft, w.drafted,
+                           w.temperature, w.uniforms, lengths=o["lengths"], mask=o["mask"],
+                           survival=o["surv"], accepted=o["acc"], tokens=o["tok"], p_tok=o["pt"],
+                           q_tok=o["qt"], dev_status=o["st"], ws=ws_sv, stream=cur)
+        if ev is not None:
+            ds.dspark_set_stream_events(None, None)
+            ev[3].record(cur)
+
+    def step_two_calls(i, cur):
+        """The same step as two calls: dspark_schedule, then dspark_verify."""
+        w, o = sets[i % len(sets)], outs[i % len(sets)]
         ds.schedule(w.conf, w.threshold, w.budget, w.min_len, lengths=o["lengths"], mask=o["mask"],
                     survival=o["surv"], dev_status=o["st"], ws=ws_s, stream=cur)
-        if ev is not None:
-            ev[1].record(cur)
-            ds.dspark_set_stream_events(ev[3], ev[4])
         ds.verify(w.target, w.draft, w.drafted, o["lengths"], w.temperature, w.uniforms,
                   accepted=o["acc"], tokens=o["tok"], p_tok=o["pt"], q_tok=o["qt"],
                   dev_status=o["st"], ws=ws_v, stream=cur)
-        if ev is not None:
-            ds.dspark_set_stream_events(None, None)
-            ev[2].record(cur)
 
     for i in range(args.warmup):
         step(i, stream)
@@ -510,10 +522,10 @@ def main():
         sbytes.append(stream_bytes(w, L, T))
         accs.append((a, L))
 
-    # Kernel timing pass: direct launches with events around schedule, around
-    # verify and, recorded by the library on the same stream, around the
-    # streaming launch.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # Kernel timing pass: direct launches with events around the call and,
+    # recorded by the library on the same stream, around the streaming
+    # launch.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for e in ev:
         for x in e:
             x.record(stream)           # creates the HIP events
@@ -523,10 +535,9 @@ def main():
     for i in range(args.steps):
         step(i, stream, ev[i])
     torch.cuda.synchronize()
-    sched_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    ver_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    str_ms = [e[3].elapsed_time(e[4]) for e in ev]
-    assert all(0 < t <= v for t, v in zip(str_ms, ver_ms)), "stream events outside verify"
+    ver_ms = [e[0].elapsed_time(e[3]) for e in ev]
+    str_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    assert all(0 < t <= v for t, v in zip(str_ms, ver_ms)), "stream events outside the call"
 
     # Timed region: K steps launched directly on one stream with nothing
     # between the calls (an event between kernels delays the next one); with
@@ -565,9 +576,43 @@ def main():
     verify_gbs = n_bytes / (sum(ver_ms) / 1e3) / 1e9
     stream_gbs = s_bytes / (sum(str_ms) / 1e3) / 1e9
     log(f"timed {args.steps} steps ({'graphs' if graphs is not None else 'direct'}): {total_ms:.3f} ms, "
-        f"{total_ms / args.steps * 1e3:.1f} us/step; kernel pass: schedule median {np.median(sched_ms)*1e3:.1f} us, "
-        f"verify median {np.median(ver_ms)*1e3:.1f} us ({verify_gbs:.0f} GB/s); streaming pass median "
+        f"{total_ms / args.steps * 1e3:.1f} us/step; kernel pass: schedule + verify call median "
+        f"{np.median(ver_ms)*1e3:.1f} us ({verify_gbs:.0f} GB/s); streaming pass median "
         f"{np.median(str_ms)*1e3:.1f} us ({stream_gbs:.0f} GB/s)")
+    # the same steps as two calls (schedule, then verify), timed the same way
+    for i in range(args.warmup):
+        step_two_calls(i, stream)
+    torch.cuda.synchronize()
+    t2a = torch.cuda.Event(enable_timing=True)
+    t2b = torch.cuda.Event(enable_timing=True)
+    t2a.record(stream)
+    for i in range(args.steps):
+        step_two_calls(i, stream)
+    t2b.record(stream)
+    torch.cuda.synchronize()
+    two_ms = t2a.elapsed_time(t2b)
+    log(f"the same {args.steps} steps as two calls: {two_ms / args.steps * 1e3:.1f} us/step")
+    # the streaming pass alone (dspark_verify after dspark_schedule), its
+    # launch timed by library-recorded events as above
+    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in ev2:
+        for x in e:
+            x.record(stream)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(SPIN_CYCLES)
+    for i in range(args.steps):
+        w, o = sets[i % len(sets)], outs[i % len(sets)]
+        ds.schedule(w.conf, w.threshold, w.budget, w.min_len, lengths=o["lengths"], mask=o["mask"],
+                    survival=o["surv"], dev_status=o["st"], ws=ws_s, stream=stream)
+        ds.dspark_set_stream_events(ev2[i][0], ev2[i][1])
+        ds.verify(w.target, w.draft, w.drafted, o["lengths"], w.temperature, w.uniforms,
+                  accepted=o["acc"], tokens=o["tok"], p_tok=o["pt"], q_tok=o["qt"],
+                  dev_status=o["st"], ws=ws_v, stream=stream)
+        ds.dspark_set_stream_events(None, None)
+    torch.cuda.synchronize()
+    alone_ms = [a.elapsed_time(b) for a, b in ev2]
+    alone_gbs = s_bytes / (sum(alone_ms) / 1e3) / 1e9
     mean_acc = float(np.mean([a.mean() for a, _ in accs]))
     waste = float(np.mean([1 - a.sum() / max(1, L.sum()) for a, L in accs]))
     traffic, traffic_note = measured_traffic()
@@ -603,13 +648,16 @@ def main():
             "logits": w0.dtype,
             "input_sets": len(sets),
             "launch": "hip graph per step" if graphs is not None else "direct",
+            "step": "dspark_schedule_verify (schedule inside the streaming launch)",
+            "two_call_us_per_step": round(two_ms / args.steps * 1e3, 2),
             "positions_per_step": pos,
             "verify_bytes_per_call": nbytes,
             "stream_bytes_per_call": sbytes,
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_stream_rows (streaming pass of dspark_verify)",
+            "kernel": "k_stream_rows<FUSED> (streaming pass of dspark_schedule_verify, schedule "
+                      "worked out inside)",
             "achieved": round(stream_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -618,11 +666,16 @@ def main():
             "traffic_note": traffic_note,
             "algorithmic_bytes_per_launch": round(s_bytes / args.steps),
             "launch_us_mean": round(float(np.mean(str_ms)) * 1e3, 2),
-            "verify_call_gbs": round(verify_gbs, 1),
-            "verify_us_median": round(float(np.median(ver_ms)) * 1e3, 2),
-            "schedule_us_median": round(float(np.median(sched_ms)) * 1e3, 2),
+            "call_gbs": round(verify_gbs, 1),
+            "call_us_median": round(float(np.median(ver_ms)) * 1e3, 2),
             "kernel_timing": "separate pass over the same steps, events around each call and "
-                             "(library-recorded, same stream) around each streaming launch",
+                             "(library-recorded, same stream) around each streaming launch; the "
+                             "streaming launch works out the schedule as well",
+            "streaming_pass_alone": {
+                "us_mean": round(float(np.mean(alone_ms)) * 1e3, 2), "gbs": round(alone_gbs, 1),
+                "frac": round(alone_gbs / HBM_PEAK_GBS, 4),
+                "note": "the streaming launch of dspark_verify after a separate dspark_schedule "
+                        "(no schedule inside), same steps, same event timing"},
             "contiguous_read_reference": {
                 "bytes": ref_bytes, "us_mean": round(ref_ms * 1e3, 2), "gbs": round(ref_gbs, 1),
                 "frac": round(ref_gbs / HBM_PEAK_GBS, 4),

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(HERE, "libdspark.so")
 DSPARK_OK = 0
 DSPARK_F32 = 0
 DSPARK_BF16 = 1
-OP_SCHEDULE, OP_VERIFY, OP_VERIFY_GREEDY, OP_MARKOV_DRAFT = 0, 1, 2, 3
+OP_SCHEDULE, OP_VERIFY, OP_VERIFY_GREEDY, OP_MARKOV_DRAFT, OP_SCHEDULE_VERIFY = 0, 1, 2, 3, 4
 
 DEV_BAD_TOKEN = 1
 DEV_NONFINITE = 2
@@ -38,7 +38,7 @@ ERR_PARAM = 7
 EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_schedule",
            "dspark_schedule_load_aware", "dspark_calibrate", "dspark_calib_state_bytes",
            "dspark_calib_observe", "dspark_markov_draft", "dspark_verify", "dspark_verify_greedy",
-           "dspark_set_stream_events", "dspark_read_probe")
+           "dspark_set_stream_events", "dspark_read_probe", "dspark_schedule_verify")
 
 
 class DsparkError(RuntimeError):
@@ -87,6 +87,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dspark_set_stream_events.restype = i32
     lib.dspark_read_probe.argtypes = [vp, sz, vp, vp]
     lib.dspark_read_probe.restype = i32
+    lib.dspark_schedule_verify.argtypes = [vp, f32, i32, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                           vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dspark_schedule_verify.restype = i32
     _lib = lib
     return lib
 
@@ -371,6 +374,49 @@ def verify(target, draft, drafted, lengths, temperature, uniforms, *, accepted=N
                            _stream(stream, dev))
     _check(st)
     return dict(accepted=accepted, tokens=tokens, p_tok=p_tok, q_tok=q_tok, dev_status=dev_status)
+
+
+def schedule_verify(conf, threshold: float, budget: int, min_len: int, target, draft, drafted,
+                    temperature, uniforms, *, lengths=None, mask=None, survival=None,
+                    accepted=None, tokens=None, p_tok=None, q_tok=None, dev_status=None,
+                    ws: Optional[Workspace] = None, stream=None):
+    """dspark_schedule_verify on torch tensors: the schedule and the verification
+    of one step in one call.  Returns dict(lengths, mask, survival, accepted,
+    tokens, p_tok, q_tok, dev_status)."""
+    torch = _torch()
+    lib = load_library()
+    dev = target.device
+    B, K1, V = target.shape
+    K = K1 - 1
+    code = _dtype_code(target)
+    _req(conf, "conf", torch.float32, (B, K), dev)
+    _req(target, "target", target.dtype, (B, K + 1, V), dev)
+    _req(draft, "draft", target.dtype, (B, K, V), dev)
+    _req(drafted, "drafted", torch.int32, (B, K), dev)
+    _req(temperature, "temperature", torch.float32, (B,), dev)
+    _req(uniforms, "uniforms", torch.float32, (B, K + 1), dev)
+    lengths = torch.empty(B, dtype=torch.int32, device=dev) if lengths is None else \
+        _req(lengths, "lengths", torch.int32, (B,), dev)
+    mask = torch.empty((B, K), dtype=torch.uint8, device=dev) if mask is None else \
+        _req(mask, "mask", torch.uint8, (B, K), dev)
+    survival = torch.empty((B, K), dtype=torch.float32, device=dev) if survival is None else \
+        _req(survival, "survival", torch.float32, (B, K), dev)
+    accepted = torch.empty(B, dtype=torch.int32, device=dev) if accepted is None else accepted
+    tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev) if tokens is None else tokens
+    p_tok = torch.empty((B, K), dtype=torch.float32, device=dev) if p_tok is None else p_tok
+    q_tok = torch.empty((B, K), dtype=torch.float32, device=dev) if q_tok is None else q_tok
+    if dev_status is None:
+        dev_status = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = ws or workspace(OP_SCHEDULE_VERIFY, B, K, V, dev)
+    st = lib.dspark_schedule_verify(_ptr(conf), float(threshold), int(budget), int(min_len),
+                                    _ptr(lengths), _ptr(mask), _ptr(survival), _ptr(target),
+                                    _ptr(draft), code, B, K, V, _ptr(drafted), _ptr(temperature),
+                                    _ptr(uniforms), _ptr(accepted), _ptr(tokens), _ptr(p_tok),
+                                    _ptr(q_tok), _ptr(dev_status), ws.ptr, ws.nbytes,
+                                    _stream(stream, dev))
+    _check(st)
+    return dict(lengths=lengths, mask=mask, survival=survival, accepted=accepted, tokens=tokens,
+                p_tok=p_tok, q_tok=q_tok, dev_status=dev_status)
 
 
 def verify_greedy(target, drafted, lengths, *, accepted=None, tokens=None, dev_status=None,

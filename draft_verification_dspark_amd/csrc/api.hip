@@ -89,6 +89,10 @@ size_t dspark_workspace_bytes(int op, int B, int K, int V) {
     if (V < 1 || K > kMaxK) return 0;
     return verify_layout(B, K, V).total;
   }
+  if (op == DSPARK_OP_SCHEDULE_VERIFY) {
+    if (V < 1 || K > kMaxK) return 0;
+    return up(verify_layout(B, K, V).total) + schedule_layout(B, K).total;
+  }
   return 0;
 }
 
@@ -101,7 +105,7 @@ const char* dspark_status_string(int status) {
     case DSPARK_ERR_BUDGET: return "budget below B*min_len or min_len outside [0,K]";
     case DSPARK_ERR_WORKSPACE: return "workspace too small or misaligned";
     case DSPARK_ERR_LAUNCH: return "kernel launch failed";
-    case DSPARK_ERR_PARAM: return "load-aware parameter out of range";
+    case DSPARK_ERR_PARAM: return "parameter out of range or misaligned";
     default: return "unknown status";
   }
 }
@@ -178,7 +182,8 @@ static int verify_common(const void* target, const void* draft, int dtype, int B
                          const int32_t* drafted, const int32_t* lengths, const float* temperature,
                          const float* uniforms, int32_t* accepted, int32_t* tokens, float* p_tok,
                          float* q_tok, int32_t* dev_status, void* workspace, size_t ws_bytes,
-                         void* stream, int greedy_only) {
+                         void* stream, int greedy_only, bool dry = false,
+                         const ScheduleArgs* fused = nullptr) {
   if (!target || !drafted || !accepted || !tokens || !dev_status || !workspace)
     return DSPARK_ERR_NULL;
   if (!greedy_only && (!draft || !temperature || !uniforms)) return DSPARK_ERR_NULL;
@@ -208,6 +213,7 @@ static int verify_common(const void* target, const void* draft, int dtype, int B
   a.G = dtype == DSPARK_BF16 ? chunks_per_row<DSPARK_BF16>(V) : chunks_per_row<DSPARK_F32>(V);
   a.greedy_only = greedy_only;
   a.vec_ok = (V % per_vec == 0) && aligned(target, 16) && (greedy_only || aligned(draft, 16));
+  if (dry) return DSPARK_OK;  // arguments checked, nothing launched
   // consecutive sub-batches of at most kLaunchBatch requests on one stream
   const size_t s = dtype == DSPARK_BF16 ? 2 : 4;
   for (int b0 = 0; b0 < B; b0 += kLaunchBatch) {
@@ -226,7 +232,8 @@ static int verify_common(const void* target, const void* draft, int dtype, int B
     sub.q_tok = a.q_tok ? a.q_tok + (size_t)b0 * K : nullptr;
     const bool first = b0 == 0;
     const int st = launch_verify(sub, dtype, static_cast<hipStream_t>(stream),
-                                 first ? g_ev_before : nullptr, first ? g_ev_after : nullptr);
+                                 first ? g_ev_before : nullptr, first ? g_ev_after : nullptr,
+                                 first ? fused : nullptr);
     if (st != DSPARK_OK) return st;
   }
   return DSPARK_OK;
@@ -334,6 +341,36 @@ int dspark_markov_draft(const void* base, int dtype, int B, int K, int V, const 
   a.V = V;
   a.tiles = (V + kMarkovRows - 1) / kMarkovRows;
   return launch_markov(a, dtype, static_cast<hipStream_t>(stream));
+}
+
+int dspark_schedule_verify(const float* conf, float threshold, int budget, int min_len,
+                           int32_t* lengths, uint8_t* mask, float* survival,
+                           const void* target_logits, const void* draft_logits, int dtype, int B,
+                           int K, int V, const int32_t* drafted, const float* temperature,
+                           const float* uniforms, int32_t* accepted, int32_t* tokens,
+                           float* p_tok, float* q_tok, int32_t* dev_status, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  if (!workspace) return DSPARK_ERR_NULL;
+  if (B < 1 || K < 1 || V < 1 || K > kMaxK || B > kMaxB || V > (1 << 30)) return DSPARK_ERR_SHAPE;
+  // workspace: the verify layout, then the schedule layout
+  const size_t vbytes = up(verify_layout(B, K, V).total);
+  if (ws_bytes < vbytes || !aligned(workspace, kAlign)) return DSPARK_ERR_WORKSPACE;
+  ScheduleArgs sa;
+  int st = schedule_common(sa, conf, B, K, threshold, budget, min_len, lengths, mask, survival,
+                           dev_status, static_cast<char*>(workspace) + vbytes, ws_bytes - vbytes);
+  if (st != DSPARK_OK) return st;
+  st = verify_common(target_logits, draft_logits, dtype, B, K, V, drafted, lengths, temperature,
+                     uniforms, accepted, tokens, p_tok, q_tok, dev_status, workspace, vbytes,
+                     stream, 0, true);
+  if (st != DSPARK_OK) return st;
+  const bool fuse = B <= kFusedMaxB && K <= kFusedMaxK && (long long)B * K <= kFusedMaxPositions;
+  if (!fuse) {
+    st = launch_schedule(sa, static_cast<hipStream_t>(stream));
+    if (st != DSPARK_OK) return st;
+  }
+  return verify_common(target_logits, draft_logits, dtype, B, K, V, drafted, lengths, temperature,
+                       uniforms, accepted, tokens, p_tok, q_tok, dev_status, workspace, vbytes,
+                       stream, 0, false, fuse ? &sa : nullptr);
 }
 
 int dspark_set_stream_events(void* before, void* after) {

@@ -29,14 +29,26 @@ struct VerifyArgs {
   int vec_ok;
 };
 
-// ev_before / ev_after: optional events recorded around the streaming pass
+struct ScheduleArgs;
+
+// ev_before / ev_after: optional events recorded around the streaming pass.
+// fused: the schedule to work out inside the streaming pass (at most
+// kFusedMaxB requests and kFusedMaxPositions positions), else NULL.
 int launch_verify(VerifyArgs& a, int dtype, hipStream_t st, hipEvent_t ev_before,
-                  hipEvent_t ev_after);
+                  hipEvent_t ev_after, const ScheduleArgs* fused = nullptr);
 int compute_units();  // of the current device
 
 // Requests per launch sequence of dspark_verify (the streaming kernel keeps
 // a per-request plan of this many entries in LDS); larger batches run as
 // consecutive sub-batches on the same stream.
 constexpr int kLaunchBatch = 2048;
+
+// Largest batch whose schedule the fused schedule + verify call works out
+// inside the streaming pass (one request per thread of a streaming
+// workgroup, at most 16 positions per request, every position's key in
+// LDS); larger batches launch the schedule on its own first.
+constexpr int kFusedMaxB = 768;
+constexpr int kFusedMaxK = 16;  // a thread's confidences are loaded in one round trip
+constexpr int kFusedMaxPositions = 12288;
 
 }  // namespace dspark

@@ -41,6 +41,7 @@
 #include <hip/hip_runtime.h>
 
 #include "args.hpp"
+#include "schedule_core.hpp"
 
 namespace dspark {
 
@@ -62,11 +63,12 @@ struct ReqInfo {
   float c;
 };
 
-__device__ __forceinline__ ReqInfo req_info(const VerifyArgs& a, int b) {
+// L: the request's length as given (checked and clamped here); T: its
+// temperature (unused on a greedy-only call)
+__device__ __forceinline__ ReqInfo req_info_lt(const VerifyArgs& a, int L, float T) {
   ReqInfo r;
   r.bad = 0;
   r.c = 0.f;
-  int L = a.lengths ? a.lengths[b] : a.K;
   if (L < 0 || L > a.K) {
     r.bad |= DSPARK_DEV_BAD_LENGTH;
     L = L < 0 ? 0 : a.K;
@@ -75,7 +77,6 @@ __device__ __forceinline__ ReqInfo req_info(const VerifyArgs& a, int b) {
   if (a.greedy_only) {
     r.kind = kKindGreedy;
   } else {
-    const float T = a.temperature[b];
     if (!(T >= 0.f)) {
       r.bad |= DSPARK_DEV_BAD_TEMP;
       r.kind = kKindSkip;
@@ -87,6 +88,10 @@ __device__ __forceinline__ ReqInfo req_info(const VerifyArgs& a, int b) {
     }
   }
   return r;
+}
+
+__device__ __forceinline__ ReqInfo req_info(const VerifyArgs& a, int b) {
+  return req_info_lt(a, a.lengths ? a.lengths[b] : a.K, a.greedy_only ? 0.f : a.temperature[b]);
 }
 
 // ------------------------------------------------------------------ pass 1
@@ -181,6 +186,8 @@ struct TileRef {
 #endif
 constexpr int kStreamBlock = DSPARK_STREAM_BLOCK;
 constexpr int kStreamWaves = kStreamBlock / kWave;
+static_assert(kFusedMaxB == kStreamBlock && kFusedMaxPositions == kSchedLds,
+              "fused schedule limits: one request per streaming thread, keys in LDS");
 
 // The tile list.  Tiles [0, B*G) are target row 0 of every request (chunk c of
 // request b is tile b*G + c): that row is read whatever the length, so these
@@ -302,8 +309,15 @@ __device__ __forceinline__ void summarise_tile(const Tile<DT>& t, const TileRef&
 // through an LDS counter, so that waves which the compute unit's arbitration
 // serves more slowly simply take fewer tiles.  A wave's first tile, when it
 // is a row-0 tile, is requested before the plan is built.
-template <int DT, bool VEC>
-__global__ void __launch_bounds__(kStreamBlock) k_stream_rows(VerifyArgs a) {
+//
+// FUSED (the schedule + verify call, at most kStreamBlock requests and
+// kSchedLds positions): every workgroup first works out the whole schedule
+// from the confidences `s` itself, while its row-0 loads are in flight, and
+// takes the lengths from it; the schedule is deterministic, so all agree.
+// Workgroup 0 alone writes the schedule's outputs (lengths, mask, survival,
+// status), which the later launches read.
+template <int DT, bool VEC, bool FUSED>
+__global__ void __launch_bounds__(kStreamBlock) k_stream_rows(VerifyArgs a, ScheduleArgs s) {
   extern __shared__ int plan[];
   __shared__ int s_next;
   int* start = plan;                                        // [B + 1]
@@ -320,17 +334,44 @@ __global__ void __launch_bounds__(kStreamBlock) k_stream_rows(VerifyArgs a) {
   Tile<DT> A, Bt;
   TileRef ra, rb;
   int t0 = w;
-  // On the vector path a wave whose first tile is a row-0 tile requests it
-  // at once; with one request per thread the request data follows, so the
-  // two round trips overlap.
+  // With one request per thread, the thread's request data (length and
+  // temperature, or for FUSED its confidences, at most 16) is requested
+  // first and, on the vector path, a wave whose first tile is a row-0 tile
+  // requests it right after: the plan then waits for the request data only,
+  // with the tile still in flight.
   const bool one_each = a.B <= kStreamBlock;
-  const bool early = VEC && one_each && tile_of(t0) < a.B * a.G;
-  if (early) {
-    ra = decode_tile<DT>(a, start, info, tile_of(t0));
+  const bool mine_req = one_each && (int)threadIdx.x < a.B;
+  int l_raw = a.K;
+  float t_raw = 0.f;
+  float cpre[16];
+  if (mine_req) {
+    if (!a.greedy_only) t_raw = a.temperature[threadIdx.x];
+    if constexpr (FUSED) {
+      // one path of plain loads (two would meet in a copy that waits)
+      const float* cr = s.conf + (size_t)threadIdx.x * s.K;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) cpre[i] = cr[min(i, s.K - 1)];
+    } else {
+      if (a.lengths) l_raw = a.lengths[threadIdx.x];
+    }
+  }
+  // Every wave issues the same eight loads here, so that waiting for the
+  // request data above never waits for them: its first tile when that is a
+  // row-0 tile (needs no plan), else another wave's row-0 tile (a tile of a
+  // workgroup on the same XCD, usually served from L2), dropped.
+  const int P0 = a.B * a.G;
+  const bool early = VEC && tile_of(t0) < P0;
+  if constexpr (VEC) {
+    ra = decode_tile<DT>(a, start, info, early ? tile_of(t0) : tile_of(t0) % P0);
     A.template load<VEC>(ra.base, ra.n);
   }
   ReqInfo mine{0, kKindSkip, 0, 0.f};
-  if (one_each && (int)threadIdx.x < a.B) mine = req_info(a, threadIdx.x);
+  if constexpr (FUSED) {
+    const int len = schedule_body<kStreamBlock, 16, true>(s, s.tau, s.budget, g == 0, cpre);
+    if (mine_req) mine = req_info_lt(a, len, t_raw);
+  } else {
+    if (mine_req) mine = req_info_lt(a, l_raw, t_raw);
+  }
   build_plan(a, start, info, cval, one_each, mine);
   const int total = uniform(start[a.B]);
   const int end = uniform((total - g + n - 1) / n);  // tiles of this workgroup
@@ -1120,12 +1161,17 @@ __global__ void __launch_bounds__(kBlock) k_draw(VerifyArgs a) {
 // ------------------------------------------------------------------ launch
 
 template <int DT, bool VEC>
-static int launch_verify_t(VerifyArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+static int launch_verify_t(VerifyArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1,
+                           const ScheduleArgs* fused) {
   const size_t lds = sizeof(int) * (3 * (size_t)a.B + 1);
   const int grid = compute_units();
   if (ev0 && ev1 && hipEventRecord(ev0, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
-  hipLaunchKernelGGL((k_stream_rows<DT, VEC>), dim3((unsigned)grid), dim3(kStreamBlock), lds, st,
-                     a);
+  if (fused)
+    hipLaunchKernelGGL((k_stream_rows<DT, VEC, true>), dim3((unsigned)grid), dim3(kStreamBlock),
+                       lds, st, a, *fused);
+  else
+    hipLaunchKernelGGL((k_stream_rows<DT, VEC, false>), dim3((unsigned)grid), dim3(kStreamBlock),
+                       lds, st, a, ScheduleArgs{});
   if (ev0 && ev1 && hipEventRecord(ev1, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
   a.groups = (a.G + kChunksPerGroup - 1) / kChunksPerGroup;
   hipLaunchKernelGGL((k_decide<DT, VEC>), dim3((unsigned)((long)a.B * a.groups)),
@@ -1135,12 +1181,15 @@ static int launch_verify_t(VerifyArgs& a, hipStream_t st, hipEvent_t ev0, hipEve
   return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_ERR_LAUNCH;
 }
 
-int launch_verify(VerifyArgs& a, int dtype, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+int launch_verify(VerifyArgs& a, int dtype, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1,
+                  const ScheduleArgs* fused) {
+  if (fused && (a.B > kStreamBlock || a.K > kFusedMaxK || a.B * a.K > kSchedLds))
+    return DSPARK_ERR_SHAPE;
   if (dtype == DSPARK_BF16)
-    return a.vec_ok ? launch_verify_t<DSPARK_BF16, true>(a, st, ev0, ev1)
-                    : launch_verify_t<DSPARK_BF16, false>(a, st, ev0, ev1);
-  return a.vec_ok ? launch_verify_t<DSPARK_F32, true>(a, st, ev0, ev1)
-                  : launch_verify_t<DSPARK_F32, false>(a, st, ev0, ev1);
+    return a.vec_ok ? launch_verify_t<DSPARK_BF16, true>(a, st, ev0, ev1, fused)
+                    : launch_verify_t<DSPARK_BF16, false>(a, st, ev0, ev1, fused);
+  return a.vec_ok ? launch_verify_t<DSPARK_F32, true>(a, st, ev0, ev1, fused)
+                  : launch_verify_t<DSPARK_F32, false>(a, st, ev0, ev1, fused);
 }
 
 }  // namespace dspark

@@ -103,6 +103,7 @@ typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
 #define DSPARK_OP_VERIFY 1
 #define DSPARK_OP_VERIFY_GREEDY 2
 #define DSPARK_OP_MARKOV_DRAFT 3
+#define DSPARK_OP_SCHEDULE_VERIFY 4
 
 /* Bytes of workspace `op` needs for these sizes (0 for bad sizes). */
 DSPARK_API size_t dspark_workspace_bytes(int op, int B, int K, int V);
@@ -346,6 +347,38 @@ DSPARK_API int dspark_verify_greedy(const void* target_logits, int dtype, int B,
                          const int32_t* drafted, const int32_t* lengths, int32_t* accepted,
                          int32_t* tokens, int32_t* dev_status, void* workspace, size_t ws_bytes,
                          void* stream);
+
+/*
+ * dspark_schedule_verify — one verification step: dspark_schedule, then
+ * dspark_verify on the lengths it produced, as one call (DSpark Deep Dive,
+ * "GPU-Resident Scheduling": the schedule runs on the device and hands the
+ * lengths to verification without a host round trip; the scheduling and
+ * verification passages cited at those two calls define what is computed).
+ *
+ * Results are exactly those of
+ *   dspark_schedule(conf, B, K, threshold, budget, min_len, lengths, mask,
+ *                   survival, ...) followed by
+ *   dspark_verify(target_logits, draft_logits, dtype, B, K, V, drafted,
+ *                 lengths, temperature, uniforms, accepted, tokens, p_tok,
+ *                 q_tok, ...)
+ * on the same stream; the arguments mean what they mean there, and lengths
+ * is required (it is the schedule's output and the verification's input).
+ * With B <= 768, K <= 16 and B*K <= 12288 the schedule is worked out inside the
+ * streaming pass (every workgroup computes it from the confidences while its
+ * first loads are in flight; one writes lengths, mask and survival), which
+ * saves a launch; larger batches launch the schedule first.
+ *   workspace  dspark_workspace_bytes(DSPARK_OP_SCHEDULE_VERIFY, B, K, V)
+ * Errors: those of the two calls (argument checks of both come before any
+ * launch).
+ */
+DSPARK_API int dspark_schedule_verify(const float* conf, float threshold, int budget,
+                                      int min_len, int32_t* lengths, uint8_t* mask,
+                                      float* survival, const void* target_logits,
+                                      const void* draft_logits, int dtype, int B, int K, int V,
+                                      const int32_t* drafted, const float* temperature,
+                                      const float* uniforms, int32_t* accepted, int32_t* tokens,
+                                      float* p_tok, float* q_tok, int32_t* dev_status,
+                                      void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * dspark_set_stream_events — timing hook for the streaming pass (measurement

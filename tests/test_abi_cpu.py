@@ -186,3 +186,38 @@ def test_read_probe_argument_errors():
     assert lib.dspark_read_probe(P, 0, P, None) == ds.ERR_PARAM
     assert lib.dspark_read_probe(P, 24, P, None) == ds.ERR_PARAM
     assert lib.dspark_read_probe(P + 8, 32, P, None) == ds.ERR_PARAM
+
+
+def _sv(conf=P, thr=0.1, budget=-1, ml=1, L=P, t=P, d=P, dtype=1, B=2, K=4, V=100, y=P, T=P,
+        u=P, acc=P, tok=P, st=P, ws=P, nb=10 ** 9):
+    lib = ds.load_library()
+    return lib.dspark_schedule_verify(conf, thr, budget, ml, L, None, None, t, d, dtype, B, K, V,
+                                      y, T, u, acc, tok, None, None, st, ws, nb, None)
+
+
+def test_schedule_verify_argument_errors():
+    # the checks of both halves come before any launch
+    assert _sv(ws=None) == 1
+    assert _sv(conf=None) == 1
+    assert _sv(L=None) == 1
+    assert _sv(t=None) == 1
+    assert _sv(d=None) == 1
+    assert _sv(u=None) == 1
+    assert _sv(B=0) == 2
+    assert _sv(K=65) == 2
+    assert _sv(V=0) == 2
+    assert _sv(dtype=2) == 3
+    assert _sv(budget=1, ml=1) == 4          # budget below B * min_len
+    assert _sv(ml=5) == 4
+    need = ds.dspark_workspace_bytes(ds.OP_SCHEDULE_VERIFY, 2, 4, 100)
+    assert _sv(nb=need - 1) == 5
+    assert _sv(ws=P + 64) == 5
+
+
+def test_schedule_verify_workspace_is_both_layouts():
+    w = ds.dspark_workspace_bytes
+    for B, K, V in ((64, 16, 151936), (1, 4, 1024), (1024, 8, 151936)):
+        v = w(ds.OP_VERIFY, B, K, V)
+        s = w(ds.OP_SCHEDULE, B, K, 1)
+        assert w(ds.OP_SCHEDULE_VERIFY, B, K, V) == (v + 255) // 256 * 256 + s
+    assert w(ds.OP_SCHEDULE_VERIFY, 1, 65, 10) == 0

@@ -517,6 +517,75 @@ def test_graph_capture_replay():
         assert int(st.item()) == 0
 
 
+# ---------------------------------------------------------------- fused schedule + verify
+
+def _fused_vs_separate(w, budget=None, conf=None):
+    """dspark_schedule_verify against dspark_schedule then dspark_verify on
+    the same inputs: every output equal bit for bit."""
+    conf = w.conf if conf is None else conf
+    budget = w.budget if budget is None else budget
+    Ls, ms, ss, st_s = ds.schedule(conf, w.threshold, budget, w.min_len)
+    sep = ds.verify(w.target, w.draft, w.drafted, Ls, w.temperature, w.uniforms, dev_status=st_s)
+    fu = ds.schedule_verify(conf, w.threshold, budget, w.min_len, w.target, w.draft, w.drafted,
+                            w.temperature, w.uniforms)
+    torch.cuda.synchronize()
+    ref = {"lengths": Ls, "mask": ms, "survival": ss, "accepted": sep["accepted"],
+           "tokens": sep["tokens"], "p_tok": sep["p_tok"], "q_tok": sep["q_tok"],
+           "dev_status": st_s}
+    for k, v in ref.items():
+        a, b = fu[k], v
+        if a.dtype == torch.float32:  # bit patterns: NaN survival values compare equal
+            a, b = a.view(torch.int32), b.view(torch.int32)
+        assert torch.equal(a, b), k
+    return fu, ref
+
+
+@pytest.mark.parametrize("wid,kw,budget", [
+    (1, {}, None),
+    (2, {}, None),
+    (3, {}, None),
+    (4, {}, None),                        # 256 requests, budget 2048 binds: radix select inside
+    (5, dict(B=512), None),               # temperatures 0 / 0.6 / 1 (greedy requests fused)
+    (5, dict(B=512), 700),                # the same with a binding budget
+    (5, dict(B=64, V=9001), None),        # unaligned rows: the scalar streaming path
+    (3, dict(B=768, V=4096), 1000),       # the largest fused batch: 768 requests, 12288 keys
+    (3, dict(B=769, V=4096), 1000),       # one more: the schedule launches on its own
+    (5, {}, None),                        # 1024 requests: launched separately
+])
+def test_schedule_verify_matches_separate_calls(wid, kw, budget):
+    w = workloads.make(wid, device=DEV, **kw)
+    print(f"fused vs separate: workload {wid} {kw} budget={budget}", flush=True)
+    fu, _ = _fused_vs_separate(w, budget=budget)
+    if budget is not None:
+        assert int(fu["lengths"].sum().item()) == budget  # the budget bound
+    assert int(fu["dev_status"].item()) == 0
+
+
+def test_schedule_verify_against_oracle():
+    w = workloads.make(3, seed_offset=300, device=DEV)
+    fu = ds.schedule_verify(w.conf, w.threshold, w.budget, w.min_len, w.target, w.draft,
+                            w.drafted, w.temperature, w.uniforms)
+    torch.cuda.synchronize()
+    ref_s = oracle.schedule(host(w.conf), w.threshold, w.budget, w.min_len)
+    compare_schedule((host(fu["lengths"]), host(fu["mask"]), host(fu["survival"])), ref_s)
+    L = host(fu["lengths"])
+    g = {k: host(fu[k]) for k in ("accepted", "tokens", "p_tok", "q_tok", "dev_status")}
+    ref = oracle.verify(host(w.target), host(w.draft), host(w.drafted), L, host(w.temperature),
+                        host(w.uniforms))
+    rep = compare_verify(g, ref, L, host(w.temperature))
+    print(f"fused vs oracle: mismatches={rep.n_mismatch} boundary={rep.n_boundary}", flush=True)
+    rep.assert_ok()
+
+
+def test_schedule_verify_flags_bad_confidence():
+    w = workloads.make(2, device=DEV)
+    conf = w.conf.clone()
+    conf[3, 2] = float("nan")
+    conf[7, 0] = 1.5
+    fu, ref = _fused_vs_separate(w, conf=conf)
+    assert int(fu["dev_status"].item()) & ds.DEV_BAD_CONF
+
+
 # ---------------------------------------------------------------- timing hook
 
 @pytest.mark.parametrize("nbytes", [16, 8192 * 3 + 48, 82_450_608])
