@@ -577,6 +577,82 @@ def test_schedule_verify_against_oracle():
     rep.assert_ok()
 
 
+def test_schedule_verify_null_mask_and_survival():
+    # mask and survival are optional outputs of the C call: with NULL the
+    # survival products go to the workspace and the results are unchanged
+    w = workloads.make(3, seed_offset=100, device=DEV)
+    B, K, V = w.B, w.K, w.V
+    ref = ds.schedule_verify(w.conf, w.threshold, w.budget, w.min_len, w.target, w.draft,
+                             w.drafted, w.temperature, w.uniforms)
+    lib = ds.load_library()
+    i32, f32 = torch.int32, torch.float32
+    L = torch.empty(B, dtype=i32, device=DEV)
+    acc = torch.empty(B, dtype=i32, device=DEV)
+    tok = torch.empty((B, K + 1), dtype=i32, device=DEV)
+    pt = torch.empty((B, K), dtype=f32, device=DEV)
+    qt = torch.empty((B, K), dtype=f32, device=DEV)
+    st = torch.zeros(1, dtype=i32, device=DEV)
+    ws = ds.workspace(ds.OP_SCHEDULE_VERIFY, B, K, V, DEV)
+    p = lambda t: t.data_ptr()
+    code = lib.dspark_schedule_verify(p(w.conf), w.threshold, w.budget, w.min_len, p(L), None, None,
+                                      p(w.target), p(w.draft), ds.DSPARK_BF16, B, K, V,
+                                      p(w.drafted), p(w.temperature), p(w.uniforms), p(acc),
+                                      p(tok), p(pt), p(qt), p(st), ws.ptr, ws.nbytes,
+                                      torch.cuda.current_stream().cuda_stream)
+    assert code == 0
+    torch.cuda.synchronize()
+    for k, v in (("lengths", L), ("accepted", acc), ("tokens", tok), ("p_tok", pt),
+                 ("q_tok", qt), ("dev_status", st)):
+        assert torch.equal(ref[k], v), k
+
+
+def test_schedule_verify_graph_replay():
+    # the one-call step captured in a HIP graph and replayed on fresh
+    # confidences and uniforms: every replay equals the eager call
+    w = workloads.make(3, seed_offset=200, device=DEV)
+    B, K = w.B, w.K
+    conf = w.conf.clone()
+    u = w.uniforms.clone()
+    outs = dict(lengths=torch.empty(B, dtype=torch.int32, device=DEV),
+                mask=torch.empty((B, K), dtype=torch.uint8, device=DEV),
+                survival=torch.empty((B, K), dtype=torch.float32, device=DEV),
+                accepted=torch.empty(B, dtype=torch.int32, device=DEV),
+                tokens=torch.empty((B, K + 1), dtype=torch.int32, device=DEV),
+                p_tok=torch.empty((B, K), dtype=torch.float32, device=DEV),
+                q_tok=torch.empty((B, K), dtype=torch.float32, device=DEV),
+                dev_status=torch.zeros(1, dtype=torch.int32, device=DEV))
+    ws = ds.workspace(ds.OP_SCHEDULE_VERIFY, B, K, w.V, DEV)
+
+    def step():
+        outs["dev_status"].zero_()
+        ds.schedule_verify(conf, w.threshold, w.budget, w.min_len, w.target, w.draft, w.drafted,
+                           w.temperature, u, ws=ws, **outs)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(9)
+    for rep in range(4):
+        print(f"graph replay {rep}", flush=True)
+        u.copy_(torch.rand(u.shape, generator=gen, device=DEV))
+        conf.copy_(torch.rand(conf.shape, generator=gen, device=DEV) * 0.5 + 0.5)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {k: v.clone() for k, v in outs.items()}
+        step()                                   # eager on the same inputs
+        torch.cuda.synchronize()
+        for k, v in outs.items():
+            assert torch.equal(got[k], v), (rep, k)
+        assert int(outs["dev_status"].item()) == 0
+
+
 def test_schedule_verify_flags_bad_confidence():
     w = workloads.make(2, device=DEV)
     conf = w.conf.clone()
