@@ -320,37 +320,42 @@ template <int DT, int U> struct TileN {
   // is one, and otherwise the smallest (most negative) pattern is.  bf16
   // pairs use packed 16-bit max / min.  NaN patterns can win; a NaN shift
   // makes the exponent sum NaN, which is reported there.
+  // The largest key is the largest element unless every element is
+  // negative (sign bit set); only then, wave-uniformly, a second pass takes
+  // the smallest key, which is the largest negative element.
   __device__ __forceinline__ float shift_max() const {
     if constexpr (DT == DSPARK_BF16) {
       typedef short s16x2 __attribute__((ext_vector_type(2)));
-      s16x2 mx = {(short)-32768, (short)-32768}, mn = {(short)32767, (short)32767};
+      s16x2 mx = {(short)-32768, (short)-32768};
 #pragma unroll
       for (int v = 0; v < U; ++v)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const s16x2 x = __builtin_bit_cast(s16x2, w[v][i]);
-          mx = __builtin_elementwise_max(mx, x);
-          mn = __builtin_elementwise_min(mn, x);
-        }
-      int hi = mx.x > mx.y ? mx.x : mx.y;
-      int lo = mn.x < mn.y ? mn.x : mn.y;
-      hi = wave_max_i(hi);
-      lo = wave_min_i(lo);
-      const int bits = hi >= 0 ? hi : lo;
-      return __uint_as_float((uint32_t)(bits & 0xffff) << 16);
+        for (int i = 0; i < 4; ++i)
+          mx = __builtin_elementwise_max(mx, __builtin_bit_cast(s16x2, w[v][i]));
+      const int hi = wave_max_i(mx.x > mx.y ? mx.x : mx.y);
+      if (hi >= 0) return __uint_as_float((uint32_t)hi << 16);
+      s16x2 mn = {(short)32767, (short)32767};
+#pragma unroll
+      for (int v = 0; v < U; ++v)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          mn = __builtin_elementwise_min(mn, __builtin_bit_cast(s16x2, w[v][i]));
+      const int lo = wave_min_i(mn.x < mn.y ? mn.x : mn.y);
+      return __uint_as_float((uint32_t)(lo & 0xffff) << 16);
     } else {
-      int mx = INT_MIN, mn = INT_MAX;
+      int mx = INT_MIN;
 #pragma unroll
       for (int v = 0; v < U; ++v)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int x = (int)w[v][i];
-          mx = max(mx, x);
-          mn = min(mn, x);
-        }
+        for (int i = 0; i < 4; ++i) mx = max(mx, (int)w[v][i]);
       mx = wave_max_i(mx);
-      mn = wave_min_i(mn);
-      return __int_as_float(mx >= 0 ? mx : mn);
+      if (mx >= 0) return __int_as_float(mx);
+      int mn = INT_MAX;
+#pragma unroll
+      for (int v = 0; v < U; ++v)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mn = min(mn, (int)w[v][i]);
+      return __int_as_float(wave_min_i(mn));
     }
   }
 

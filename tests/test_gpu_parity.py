@@ -517,6 +517,22 @@ def test_graph_capture_replay():
         assert int(st.item()) == 0
 
 
+def test_all_negative_logits():
+    # every logit negative: each tile's maximum comes from the second (smallest
+    # key) pass; sampled and greedy rules against the oracle
+    w = workloads.make(2, seed_offset=7, device=DEV, B=8, V=20000)
+    w.target = -(w.target.abs() + 1.0)
+    w.draft = -(w.draft.abs() + 1.0)
+    _check_workload(w)
+    lengths = torch.full((w.B,), w.K, dtype=torch.int32, device=DEV)
+    og = ds.verify_greedy(w.target, w.greedy_drafted, lengths)
+    torch.cuda.synchronize()
+    rg = oracle.verify_greedy(host(w.target), host(w.greedy_drafted), host(lengths))
+    assert np.array_equal(host(og["accepted"]), rg["accepted"])
+    assert np.array_equal(host(og["tokens"]), rg["tokens"])
+    assert int(og["dev_status"].item()) == 0
+
+
 # ---------------------------------------------------------------- fused schedule + verify
 
 def _fused_vs_separate(w, budget=None, conf=None):
