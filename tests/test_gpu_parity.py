@@ -577,6 +577,18 @@ def test_schedule_verify_matches_separate_calls(wid, kw, budget):
     assert int(fu["dev_status"].item()) == 0
 
 
+@pytest.mark.parametrize("K,min_len,budget", [(5, 0, 9), (5, 2, 40), (16, 0, 1)])
+def test_schedule_verify_min_len_and_odd_k(K, min_len, budget):
+    # min_len 0 or 2 with a binding budget (radix select inside the streaming
+    # launch), and K not a multiple of 4 (confidences loaded one by one)
+    w = workloads.make(2, seed_offset=11, device=DEV, B=20, K=K, V=7000)
+    w.min_len = min_len
+    fu, _ = _fused_vs_separate(w, budget=budget)
+    assert int(fu["lengths"].sum().item()) <= max(budget, w.B * min_len)
+    ref_s = oracle.schedule(host(w.conf), w.threshold, budget, min_len)
+    compare_schedule((host(fu["lengths"]), host(fu["mask"]), host(fu["survival"])), ref_s)
+
+
 def test_schedule_verify_against_oracle():
     w = workloads.make(3, seed_offset=300, device=DEV)
     fu = ds.schedule_verify(w.conf, w.threshold, w.budget, w.min_len, w.target, w.draft,
