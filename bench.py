@@ -11,8 +11,9 @@ two calls (dspark_schedule, then dspark_verify) are timed beside it
 256 MB last-level cache by the step before.
 
 The timed region launches the K steps directly on one stream with nothing
-in between (``--graphs`` replays each step from its own HIP graph instead,
-which is slower on this stack).  Kernel times (the call, the streaming
+in between, behind a spin kernel that lets the host queue them all first
+(``--graphs`` replays each step from its own HIP graph instead, which is
+slower on this stack).  Kernel times (the call, the streaming
 pass) come from a separate pass over the same steps with events around each
 call and, recorded by the library on the same stream, around each streaming
 launch.
@@ -560,6 +561,10 @@ def main():
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    # a spin kernel queued first: the host queues all K steps while it runs,
+    # so the region times the GPU's work, not the host's launch rate
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(SPIN_CYCLES)
     t_start.record(stream)
     for i in range(args.steps):
         if graphs is not None:
@@ -585,6 +590,8 @@ def main():
     torch.cuda.synchronize()
     t2a = torch.cuda.Event(enable_timing=True)
     t2b = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(SPIN_CYCLES)
     t2a.record(stream)
     for i in range(args.steps):
         step_two_calls(i, stream)
