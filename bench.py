@@ -82,6 +82,19 @@ def algorithmic_bytes(w, lengths, accepted, temperature) -> int:
     return int(s * w.V * rows.sum())
 
 
+def early_exit_bytes(w, lengths, accepted, temperature) -> int:
+    """The early-exit lower bound: the rows a verifier that could stop at the
+    first rejection would still read, s*V*sum[2(a+1) + 2*rejected] for T > 0
+    and s*V*sum(a+1) for T = 0; beside the streaming pass's bytes it shows
+    the over-read of rows past the first rejection."""
+    s = 2 if w.dtype == "bf16" else 4
+    L = lengths.astype("int64")
+    a = accepted.astype("int64")
+    soft = temperature > 0
+    rows = (2 * (a + 1) + 2 * (a < L)) * soft + (a + 1) * (~soft)
+    return int(s * w.V * rows.sum())
+
+
 def stream_bytes(w, lengths, temperature) -> int:
     """Bytes the streaming pass must read: every scheduled row once."""
     s = 2 if w.dtype == "bf16" else 4
@@ -511,7 +524,7 @@ def main():
     log(f"warmup {args.warmup} steps done")
 
     # per-set positions and algorithmic bytes (outputs are deterministic per set)
-    pos, nbytes, sbytes, accs = [], [], [], []
+    pos, nbytes, sbytes, mbytes, accs = [], [], [], [], []
     for i in range(len(sets)):
         o, w = outs[i], sets[i]
         L = o["lengths"].cpu().numpy()
@@ -521,6 +534,7 @@ def main():
         pos.append(int(L.sum()))
         nbytes.append(algorithmic_bytes(w, L, a, T))
         sbytes.append(stream_bytes(w, L, T))
+        mbytes.append(early_exit_bytes(w, L, a, T))
         accs.append((a, L))
 
     # Kernel timing pass: direct launches with events around the call and,
@@ -601,7 +615,7 @@ def main():
     log(f"the same {args.steps} steps as two calls: {two_ms / args.steps * 1e3:.1f} us/step")
     # the streaming pass alone (dspark_verify after dspark_schedule), its
     # launch timed by library-recorded events as above
-    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for e in ev2:
         for x in e:
             x.record(stream)
@@ -612,13 +626,16 @@ def main():
         w, o = sets[i % len(sets)], outs[i % len(sets)]
         ds.schedule(w.conf, w.threshold, w.budget, w.min_len, lengths=o["lengths"], mask=o["mask"],
                     survival=o["surv"], dev_status=o["st"], ws=ws_s, stream=stream)
+        ev2[i][2].record(stream)
         ds.dspark_set_stream_events(ev2[i][0], ev2[i][1])
         ds.verify(w.target, w.draft, w.drafted, o["lengths"], w.temperature, w.uniforms,
                   accepted=o["acc"], tokens=o["tok"], p_tok=o["pt"], q_tok=o["qt"],
                   dev_status=o["st"], ws=ws_v, stream=stream)
         ds.dspark_set_stream_events(None, None)
+        ev2[i][3].record(stream)
     torch.cuda.synchronize()
-    alone_ms = [a.elapsed_time(b) for a, b in ev2]
+    alone_ms = [e[0].elapsed_time(e[1]) for e in ev2]
+    vonly_ms = [e[2].elapsed_time(e[3]) for e in ev2]
     alone_gbs = s_bytes / (sum(alone_ms) / 1e3) / 1e9
     mean_acc = float(np.mean([a.mean() for a, _ in accs]))
     waste = float(np.mean([1 - a.sum() / max(1, L.sum()) for a, L in accs]))
@@ -629,6 +646,13 @@ def main():
     ref_bytes = round(s_bytes / args.steps) // 16 * 16
     ref_ms = probe.timed(ref_bytes, 30, stream, np)
     ref_gbs = ref_bytes / (ref_ms / 1e3) / 1e9
+    # and of 2 GB: the read bandwidth this GPU reaches at all
+    big_bytes = 2_000_000_000
+    big_ms = probe.timed(big_bytes, 8, stream, np)
+    big_gbs = big_bytes / (big_ms / 1e3) / 1e9
+
+    def pct(x, q):
+        return round(float(np.percentile(np.asarray(x) * 1e3, q)), 2)
     # every input set scheduled once (short runs leave some unscheduled), so
     # that the rows read valid lengths
     for i in range(len(sets)):
@@ -678,11 +702,23 @@ def main():
             "kernel_timing": "separate pass over the same steps, events around each call and "
                              "(library-recorded, same stream) around each streaming launch; the "
                              "streaming launch works out the schedule as well",
+            "launch_us_p10_p50_p90": [pct(str_ms, 10), pct(str_ms, 50), pct(str_ms, 90)],
+            "call_us_p10_p90": [pct(ver_ms, 10), pct(ver_ms, 90)],
+            "early_exit": {
+                "bytes_per_call": round(sum(mbytes[i % len(sets)] for i in range(args.steps))
+                                        / args.steps),
+                "verify_bytes_per_call": round(n_bytes / args.steps),
+                "note": "the rows a verifier stopping at the first rejection would read, beside "
+                        "the whole call's algorithmic bytes (streaming pass + residual rows)"},
             "streaming_pass_alone": {
                 "us_mean": round(float(np.mean(alone_ms)) * 1e3, 2), "gbs": round(alone_gbs, 1),
                 "frac": round(alone_gbs / HBM_PEAK_GBS, 4),
+                "verify_call_us_p10_p50_p90": [pct(vonly_ms, 10), pct(vonly_ms, 50),
+                                               pct(vonly_ms, 90)],
                 "note": "the streaming launch of dspark_verify after a separate dspark_schedule "
                         "(no schedule inside), same steps, same event timing"},
+            "read_ceiling_2gb": {"gbs": round(big_gbs, 1), "frac": round(big_gbs / HBM_PEAK_GBS, 4),
+                                 "note": "dspark_read_probe over 2 GB, events around the call"},
             "contiguous_read_reference": {
                 "bytes": ref_bytes, "us_mean": round(ref_ms * 1e3, 2), "gbs": round(ref_gbs, 1),
                 "frac": round(ref_gbs / HBM_PEAK_GBS, 4),
