@@ -435,7 +435,9 @@ def row_measurements(ds, workloads, sets, outs, ws_v, dev, stream, torch, np, lo
                                 "positions_per_s": round(int(L.sum()) / (t_c / 1e3), 1)}
     flags = {"G1/full": int(st_.item()), "b1024": int(st5.item()), "markov": int(stm.item())}
     assert not any(flags.values()), f"device status flags set: {flags}"
-    log("rows: " + "; ".join(f"{k} {v.get('stream_gbs', v.get('call_us_median'))}" for k, v in rows.items()))
+    log("rows: " + "; ".join(
+        f"{k} {v.get('stream_gbs', v.get('call_us_median', v.get('stream_slope_gbs')))}"
+        for k, v in rows.items()))
     return rows
 
 
