@@ -97,7 +97,7 @@ __global__ void __launch_bounds__(kSchedThreads) k_schedule(ScheduleArgs a) {
       if (a.budget_out) *a.budget_out = budget;
     }
   }
-  schedule_body<kSchedThreads>(a, tau, budget, true);
+  schedule_body<kSchedThreads>(a, tau, budget, 0, 1);
 }
 
 int launch_schedule(ScheduleArgs& a, hipStream_t st) {

@@ -221,17 +221,19 @@ __device__ void budget_cut(int n, const Src& src, long long m, long long ncand, 
 }
 
 // The schedule of the whole batch by one workgroup of kSchedThreads threads
-// (every thread calls it; thread t owns requests t, t + T, ...).  With
-// `write`, the survival products, threshold lengths (where kept in memory),
-// lengths, mask and status bits go to memory; without it nothing is written
-// and the caller guarantees that nothing has to be read back either
-// (B * K <= kSchedLds and B <= kSchedThreads * kSchedRegs).  Returns the
-// length of request threadIdx.x (0 for threads without a request).
+// (every thread calls it; thread t owns requests t, t + T, ...).  The
+// outputs of request b (survival products, length, mask, status bits) go to
+// memory when b % nwg == wg: with nwg = 1 this workgroup writes them all
+// (and the threshold lengths that the budget cut may read back); with
+// several workgroups working out the same schedule, each writes its share,
+// and the caller guarantees that nothing has to be read back (B * K <=
+// kSchedLds and B <= kSchedThreads * kSchedRegs).  Returns the length of
+// request threadIdx.x (0 for threads without a request).
 // kStage: confidences per thread loaded at once (one round trip per kStage
 // positions).  kPre: the caller has loaded them already, into `pre`, for its
 // own request (one request per thread, K <= kStage).
 template <int kSchedThreads, int kStage = kConfStage, bool kPre = false>
-__device__ int schedule_body(const ScheduleArgs& a, float tau, int budget, bool write,
+__device__ int schedule_body(const ScheduleArgs& a, float tau, int budget, int wg, int nwg,
                              const float* pre = nullptr) {
   constexpr int kSchedWaves = kSchedThreads / kWave;
   __shared__ long long red[kSchedWaves];
@@ -251,6 +253,7 @@ __device__ int schedule_body(const ScheduleArgs& a, float tau, int budget, bool 
   long long local = 0;
   int bad = 0;
   for (int j = 0, b = tid; b < B; ++j, b += kSchedThreads) {
+    const bool write = nwg == 1 || b % nwg == wg;  // this request's outputs
     const float* __restrict__ cr = a.conf + (size_t)b * K;
     float* __restrict__ sr = a.surv + (size_t)b * K;
     float C = 1.f;
@@ -307,10 +310,11 @@ __device__ int schedule_body(const ScheduleArgs& a, float tau, int budget, bool 
     if (j < kSchedRegs) lt_reg[j] = lt;
     // in memory: rows past the registers, and every row when the keys are
     // recomputed from memory below
-    if (write && (j >= kSchedRegs || !keys_in_lds)) a.lthr[b] = lt;
+    if (nwg == 1 && (j >= kSchedRegs || !keys_in_lds)) a.lthr[b] = lt;
     local += lt;
+    if (write && bad) flag(a.dev_status, bad);
+    bad = 0;
   }
-  if (write && bad) flag(a.dev_status, bad);
   auto lthr_of = [&](int j, int b) -> int {
     int v = 0;
 #pragma unroll
@@ -355,7 +359,7 @@ __device__ int schedule_body(const ScheduleArgs& a, float tau, int budget, bool 
       len = ml + take;
     }
     if (b == tid) my_len = len;
-    if (!write) continue;
+    if (!(nwg == 1 || b % nwg == wg)) continue;
     a.lengths[b] = len;
     if (a.mask) {
       uint8_t* mr = a.mask + (size_t)b * K;

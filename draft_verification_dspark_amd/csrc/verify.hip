@@ -314,8 +314,9 @@ __device__ __forceinline__ void summarise_tile(const Tile<DT>& t, const TileRef&
 // kSchedLds positions): every workgroup first works out the whole schedule
 // from the confidences `s` itself, while its row-0 loads are in flight, and
 // takes the lengths from it; the schedule is deterministic, so all agree.
-// Workgroup 0 alone writes the schedule's outputs (lengths, mask, survival,
-// status), which the later launches read.
+// Workgroup g writes the schedule's outputs (lengths, mask, survival,
+// status) of the requests b with b % n == g, which the later launches read;
+// one workgroup writing them all would start streaming last.
 template <int DT, bool VEC, bool FUSED>
 __global__ void __launch_bounds__(kStreamBlock) k_stream_rows(VerifyArgs a, ScheduleArgs s) {
   extern __shared__ int plan[];
@@ -367,7 +368,7 @@ __global__ void __launch_bounds__(kStreamBlock) k_stream_rows(VerifyArgs a, Sche
   }
   ReqInfo mine{0, kKindSkip, 0, 0.f};
   if constexpr (FUSED) {
-    const int len = schedule_body<kStreamBlock, 16, true>(s, s.tau, s.budget, g == 0, cpre);
+    const int len = schedule_body<kStreamBlock, 16, true>(s, s.tau, s.budget, g, n, cpre);
     if (mine_req) mine = req_info_lt(a, len, t_raw);
   } else {
     if (mine_req) mine = req_info_lt(a, l_raw, t_raw);
