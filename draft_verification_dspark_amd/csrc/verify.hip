@@ -23,7 +23,10 @@
 //                  double-buffering the 16-byte loads of the next tile while
 //                  summarising the current one: an integer exponent shift
 //                  k = ceil(max * c) and the sum of 2^(x*c - k) (fp32 terms,
-//                  fp64 accumulation), or (max, lowest index).
+//                  fp64 accumulation), or (max, lowest index).  For the
+//                  schedule + verify call it first works out the schedule
+//                  itself (every workgroup, from the confidences, while its
+//                  first tile loads are in flight).
 //   k_decide       `groups` workgroups per request: each merges the request's
 //                  row summaries (shifts align by exact powers of two), and
 //                  wave 0 forms p(y), q(y), alpha, the accept ballot and the
