@@ -363,10 +363,12 @@ DSPARK_API int dspark_verify_greedy(const void* target_logits, int dtype, int B,
  *                 q_tok, ...)
  * on the same stream; the arguments mean what they mean there, and lengths
  * is required (it is the schedule's output and the verification's input).
- * With B <= 768, K <= 16 and B*K <= 12288 the schedule is worked out inside the
- * streaming pass (every workgroup computes it from the confidences while its
- * first loads are in flight; one writes lengths, mask and survival), which
- * saves a launch; larger batches launch the schedule first.
+ * With B <= 768, K <= 16 and B*K <= 12288 the schedule is worked out inside
+ * the streaming pass (every workgroup computes it from the confidences while
+ * its first loads are in flight, and each writes the lengths, mask rows and
+ * survival rows of its share of the requests), which saves a launch; larger
+ * batches launch the schedule first. Overlapping calls need distinct
+ * workspaces, as for the other calls.
  *   workspace  dspark_workspace_bytes(DSPARK_OP_SCHEDULE_VERIFY, B, K, V)
  * Errors: those of the two calls (argument checks of both come before any
  * launch).
