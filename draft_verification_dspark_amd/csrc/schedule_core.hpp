@@ -252,6 +252,41 @@ __device__ int schedule_body(const ScheduleArgs& a, float tau, int budget, int w
   int lt_reg[kSchedRegs];
   long long local = 0;
   int bad = 0;
+  if constexpr (kPre) {
+    // One request per thread, its K <= kStage confidences in registers: the
+    // same steps straight-line, with no branch per position.  A position
+    // past K leaves the product and the run as they are and stores again
+    // the last position's survival value and key into that position's slot.
+    const int b = tid;
+    if (b < B) {
+      const bool write = nwg == 1 || b % nwg == wg;
+      float* __restrict__ sr = a.surv + (size_t)b * K;
+      float C = 1.f;
+      int run = 0;
+      bool go = true;
+      uint32_t key = 0u;
+#pragma unroll
+      for (int k = 0; k < kStage; ++k) {
+        const bool in = k < K;  // the same in every thread
+        const float c = pre[k];
+        if (in && !(c >= 0.f && c <= 1.f)) bad |= DSPARK_DEV_BAD_CONF;
+        const float Cn = k == 0 ? c : C * c;
+        C = in ? Cn : C;
+        const bool gn = go && C >= tau;
+        go = in ? gn : go;
+        run += (in && go) ? 1 : 0;
+        key = in ? ((go && k + 1 > ml) ? surv_key(C) + 1u : 0u) : key;
+        const int slot = k < K ? k : K - 1;
+        if (keys_in_lds) s_key[(size_t)b * K + slot] = key;
+        if (write) sr[slot] = C;
+      }
+      const int lt = max(ml, run);
+      lt_reg[0] = lt;
+      if (nwg == 1 && !keys_in_lds) a.lthr[b] = lt;  // read back by the budget cut
+      local = lt;
+      if (write && bad) flag(a.dev_status, bad);
+    }
+  } else {
   for (int j = 0, b = tid; b < B; ++j, b += kSchedThreads) {
     const bool write = nwg == 1 || b % nwg == wg;  // this request's outputs
     const float* __restrict__ cr = a.conf + (size_t)b * K;
@@ -264,10 +299,7 @@ __device__ int schedule_body(const ScheduleArgs& a, float tau, int budget, int w
     // survival values overwrite them and are stored the same way
     for (int k0 = 0; k0 < K; k0 += kStage) {
       float ck[kStage];
-      if constexpr (kPre) {
-#pragma unroll
-        for (int i = 0; i < kStage; ++i) ck[i] = pre[i];
-      } else if (a.vec4) {
+      if (a.vec4) {
 #pragma unroll
         for (int q = 0; q < kStage / 4; ++q) {
           const float4 v = *reinterpret_cast<const float4*>(cr + min(k0 + 4 * q, K - 4));
@@ -314,6 +346,7 @@ __device__ int schedule_body(const ScheduleArgs& a, float tau, int budget, int w
     local += lt;
     if (write && bad) flag(a.dev_status, bad);
     bad = 0;
+  }
   }
   auto lthr_of = [&](int j, int b) -> int {
     int v = 0;
