@@ -7,8 +7,10 @@ has not been built (``python -m draft_verification_dspark_amd.build`` or
 ``__graft_entry__.build()``), loading raises.
 
 Names follow the C ABI: ``dspark_schedule``, ``dspark_schedule_load_aware``,
-``dspark_verify``, ``dspark_verify_greedy``, ``dspark_calibrate``,
-``dspark_calib_observe``, ``dspark_calib_state_bytes``, ``dspark_markov_draft``,
+``dspark_verify``, ``dspark_verify_greedy``, ``dspark_schedule_verify`` (each
+with a ``*_phase`` twin that enqueues the streaming pass or the rest on its
+own), ``dspark_calibrate``, ``dspark_calib_observe``,
+``dspark_calib_state_bytes``, ``dspark_markov_draft``,
 ``dspark_workspace_bytes``, ``dspark_status_string``.
 """
 from __future__ import annotations
@@ -35,10 +37,15 @@ DEV_BAD_LOAD = 64
 DEV_BAD_CURVE = 128
 ERR_PARAM = 7
 
+PHASE_STREAM = 1
+PHASE_FINISH = 2
+PHASE_ALL = PHASE_STREAM | PHASE_FINISH
+
 EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_schedule",
            "dspark_schedule_load_aware", "dspark_calibrate", "dspark_calib_state_bytes",
            "dspark_calib_observe", "dspark_markov_draft", "dspark_verify", "dspark_verify_greedy",
-           "dspark_set_stream_events", "dspark_read_probe", "dspark_schedule_verify")
+           "dspark_schedule_verify", "dspark_verify_phase", "dspark_verify_greedy_phase",
+           "dspark_schedule_verify_phase")
 
 
 class DsparkError(RuntimeError):
@@ -83,13 +90,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dspark_verify.restype = i32
     lib.dspark_verify_greedy.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.dspark_verify_greedy.restype = i32
-    lib.dspark_set_stream_events.argtypes = [vp, vp]
-    lib.dspark_set_stream_events.restype = i32
-    lib.dspark_read_probe.argtypes = [vp, sz, vp, vp]
-    lib.dspark_read_probe.restype = i32
     lib.dspark_schedule_verify.argtypes = [vp, f32, i32, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                            vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.dspark_schedule_verify.restype = i32
+    lib.dspark_verify_phase.argtypes = [i32] + lib.dspark_verify.argtypes
+    lib.dspark_verify_phase.restype = i32
+    lib.dspark_verify_greedy_phase.argtypes = [i32] + lib.dspark_verify_greedy.argtypes
+    lib.dspark_verify_greedy_phase.restype = i32
+    lib.dspark_schedule_verify_phase.argtypes = [i32] + lib.dspark_schedule_verify.argtypes
+    lib.dspark_schedule_verify_phase.restype = i32
     _lib = lib
     return lib
 
@@ -100,30 +109,6 @@ def dspark_status_string(status: int) -> str:
 
 def dspark_workspace_bytes(op: int, B: int, K: int, V: int) -> int:
     return int(load_library().dspark_workspace_bytes(int(op), int(B), int(K), int(V)))
-
-
-def dspark_set_stream_events(before, after) -> None:
-    """Record ``before`` / ``after`` (``torch.cuda.Event`` objects that have
-    been recorded once, so that they exist, or raw hipEvent_t handles) around
-    the streaming pass of every following verify call; ``None`` turns it off."""
-    def handle(e):
-        if e is None:
-            return None
-        h = getattr(e, "cuda_event", e)
-        if not h:
-            raise ValueError("event has no HIP handle yet: record it once first")
-        return h
-    _check(load_library().dspark_set_stream_events(handle(before), handle(after)))
-
-
-def read_probe(x, nbytes: int, sink, stream=None) -> None:
-    """Plain contiguous read of the first ``nbytes`` bytes of device tensor
-    ``x`` (the bandwidth reference for the streaming pass); ``sink`` is a
-    device tensor of at least 4 bytes."""
-    if nbytes > x.numel() * x.element_size():
-        raise ValueError("nbytes past the end of x")
-    _check(load_library().dspark_read_probe(_ptr(x), int(nbytes), _ptr(sink),
-                                            _stream(stream, x.device)))
 
 
 def _check(status: int):
@@ -163,11 +148,15 @@ class Workspace:
         self.nbytes = nbytes
 
 
-def workspace(op: int, B: int, K: int, V: int, device) -> Workspace:
-    """Cached workspace for (device, op, B, K, V)."""
+def workspace(op: int, B: int, K: int, V: int, device, stream=None) -> Workspace:
+    """Cached workspace for (device, op, B, K, V) and one stream (``None``: the
+    device's current stream).  Calls that may run at the same time need
+    distinct workspaces, so calls on different streams never share one."""
     torch = _torch()
     device = torch.device(device)
-    key = (device.index, op, B, K, V)
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    key = (device.index, op, B, K, V, int(stream.cuda_stream))
     ws = _ws_cache.get(key)
     if ws is None:
         nbytes = dspark_workspace_bytes(op, B, K, V)
@@ -183,6 +172,35 @@ def _stream(stream, device):
     if stream is None:
         stream = torch.cuda.current_stream(device)
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _status(dev_status, dev):
+    """The caller's device-status word (int32[1] on the device) or a new
+    zeroed one."""
+    torch = _torch()
+    if dev_status is None:
+        return torch.zeros(1, dtype=torch.int32, device=dev)
+    return _req(dev_status, "dev_status", torch.int32, (1,), dev)
+
+
+def _out(t, name, dtype, shape, dev):
+    """A caller-supplied output checked against what the kernels write, or a
+    new one."""
+    torch = _torch()
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=dev)
+    return _req(t, name, dtype, shape, dev)
+
+
+def _ws(ws, op, B, K, V, dev, stream):
+    """The caller's workspace, checked against the size the call needs, or the
+    cached one of this stream."""
+    if ws is None:
+        return workspace(op, B, K, V, dev, stream)
+    need = dspark_workspace_bytes(op, B, K, V)
+    if ws.nbytes < need:
+        raise ValueError(f"workspace of {ws.nbytes} bytes, the call needs {need}")
+    return ws
 
 
 def _dtype_code(t):
@@ -202,15 +220,11 @@ def schedule(conf, threshold: float, budget: int, min_len: int = 1, *, lengths=N
     dev = conf.device
     B, K = conf.shape
     _req(conf, "conf", torch.float32, (B, K), dev)
-    lengths = torch.empty(B, dtype=torch.int32, device=dev) if lengths is None else \
-        _req(lengths, "lengths", torch.int32, (B,), dev)
-    mask = torch.empty((B, K), dtype=torch.uint8, device=dev) if mask is None else \
-        _req(mask, "mask", torch.uint8, (B, K), dev)
-    survival = torch.empty((B, K), dtype=torch.float32, device=dev) if survival is None else \
-        _req(survival, "survival", torch.float32, (B, K), dev)
-    if dev_status is None:
-        dev_status = torch.zeros(1, dtype=torch.int32, device=dev)
-    ws = ws or workspace(OP_SCHEDULE, B, K, 1, dev)
+    lengths = _out(lengths, "lengths", torch.int32, (B,), dev)
+    mask = _out(mask, "mask", torch.uint8, (B, K), dev)
+    survival = _out(survival, "survival", torch.float32, (B, K), dev)
+    dev_status = _status(dev_status, dev)
+    ws = _ws(ws, OP_SCHEDULE, B, K, 1, dev, stream)
     st = lib.dspark_schedule(_ptr(conf), B, K, float(threshold), int(budget), int(min_len),
                              _ptr(lengths), _ptr(mask), _ptr(survival), _ptr(dev_status),
                              ws.ptr, ws.nbytes, _stream(stream, dev))
@@ -235,19 +249,13 @@ def schedule_load_aware(conf, load, q_max: float, m_max: float, tau_min: float, 
     if curve is not None:
         n_curve = curve.shape[0]
         _req(curve, "curve", torch.float32, (n_curve, 2), dev)
-    lengths = torch.empty(B, dtype=torch.int32, device=dev) if lengths is None else \
-        _req(lengths, "lengths", torch.int32, (B,), dev)
-    mask = torch.empty((B, K), dtype=torch.uint8, device=dev) if mask is None else \
-        _req(mask, "mask", torch.uint8, (B, K), dev)
-    survival = torch.empty((B, K), dtype=torch.float32, device=dev) if survival is None else \
-        _req(survival, "survival", torch.float32, (B, K), dev)
-    tau_out = torch.empty(1, dtype=torch.float32, device=dev) if tau_out is None else \
-        _req(tau_out, "tau_out", torch.float32, (1,), dev)
-    budget_out = torch.empty(1, dtype=torch.int32, device=dev) if budget_out is None else \
-        _req(budget_out, "budget_out", torch.int32, (1,), dev)
-    if dev_status is None:
-        dev_status = torch.zeros(1, dtype=torch.int32, device=dev)
-    ws = ws or workspace(OP_SCHEDULE, B, K, 1, dev)
+    lengths = _out(lengths, "lengths", torch.int32, (B,), dev)
+    mask = _out(mask, "mask", torch.uint8, (B, K), dev)
+    survival = _out(survival, "survival", torch.float32, (B, K), dev)
+    tau_out = _out(tau_out, "tau_out", torch.float32, (1,), dev)
+    budget_out = _out(budget_out, "budget_out", torch.int32, (1,), dev)
+    dev_status = _status(dev_status, dev)
+    ws = _ws(ws, OP_SCHEDULE, B, K, 1, dev, stream)
     st = lib.dspark_schedule_load_aware(
         _ptr(conf), B, K, _ptr(load), float(q_max), float(m_max), float(tau_min), float(tau_max),
         _ptr(curve) if curve is not None else None, n_curve, float(slot_cost), int(min_len),
@@ -265,10 +273,8 @@ def calibrate(raw, theta, *, out=None, dev_status=None, stream=None):
     B, K = raw.shape
     _req(raw, "raw", torch.float32, (B, K), dev)
     _req(theta, "theta", torch.float32, (K,), dev)
-    out = torch.empty((B, K), dtype=torch.float32, device=dev) if out is None else \
-        _req(out, "out", torch.float32, (B, K), dev)
-    if dev_status is None:
-        dev_status = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = _out(out, "out", torch.float32, (B, K), dev)
+    dev_status = _status(dev_status, dev)
     _check(lib.dspark_calibrate(_ptr(raw), _ptr(theta), B, K, _ptr(out), _ptr(dev_status),
                                 _stream(stream, dev)))
     return out, dev_status
@@ -300,8 +306,7 @@ def calib_observe(calibrated, lengths, accepted, theta, lr: float, theta_min: fl
         raise ValueError("state: expected a contiguous tensor on the same device")
     ece_out = torch.zeros(1, dtype=torch.float32, device=dev) if ece_out is None else \
         _req(ece_out, "ece_out", torch.float32, (1,), dev)
-    if dev_status is None:
-        dev_status = torch.zeros(1, dtype=torch.int32, device=dev)
+    dev_status = _status(dev_status, dev)
     _check(lib.dspark_calib_observe(_ptr(calibrated), _ptr(lengths), _ptr(accepted), B, K,
                                     _ptr(theta), float(lr), float(theta_min), int(window),
                                     int(n_bins), _ptr(state), state.numel() * state.element_size(),
@@ -326,15 +331,11 @@ def markov_draft(base, U, Vm, scale: float, y0, temperature, uniforms, *, correc
     _req(y0, "y0", torch.int32, (B,), dev)
     _req(temperature, "temperature", torch.float32, (B,), dev)
     _req(uniforms, "uniforms", torch.float32, (B, K), dev)
-    corrected = torch.empty_like(base) if corrected is None else \
-        _req(corrected, "corrected", base.dtype, (B, K, V), dev)
-    drafted = torch.empty((B, K), dtype=torch.int32, device=dev) if drafted is None else \
-        _req(drafted, "drafted", torch.int32, (B, K), dev)
-    q_tok = torch.empty((B, K), dtype=torch.float32, device=dev) if q_tok is None else \
-        _req(q_tok, "q_tok", torch.float32, (B, K), dev)
-    if dev_status is None:
-        dev_status = torch.zeros(1, dtype=torch.int32, device=dev)
-    ws = ws or workspace(OP_MARKOV_DRAFT, B, K, V, dev)
+    corrected = _out(corrected, "corrected", base.dtype, (B, K, V), dev)
+    drafted = _out(drafted, "drafted", torch.int32, (B, K), dev)
+    q_tok = _out(q_tok, "q_tok", torch.float32, (B, K), dev)
+    dev_status = _status(dev_status, dev)
+    ws = _ws(ws, OP_MARKOV_DRAFT, B, K, V, dev, stream)
     _check(lib.dspark_markov_draft(_ptr(base), code, B, K, V, _ptr(U), _ptr(Vm), r, float(scale),
                                    _ptr(y0), _ptr(temperature), _ptr(uniforms), _ptr(corrected),
                                    _ptr(drafted), _ptr(q_tok), _ptr(dev_status), ws.ptr, ws.nbytes,
@@ -344,8 +345,9 @@ def markov_draft(base, U, Vm, scale: float, y0, temperature, uniforms, *, correc
 
 def verify(target, draft, drafted, lengths, temperature, uniforms, *, accepted=None, tokens=None,
            p_tok=None, q_tok=None, dev_status=None, ws: Optional[Workspace] = None, stream=None,
-           want_probs: bool = True):
-    """dspark_verify on torch tensors.  ``lengths=None`` verifies all K.
+           want_probs: bool = True, phases: int = PHASE_ALL):
+    """dspark_verify on torch tensors (``phases`` other than PHASE_ALL:
+    dspark_verify_phase).  ``lengths=None`` verifies all K.
     Returns dict(accepted, tokens, p_tok, q_tok, dev_status)."""
     torch = _torch()
     lib = load_library()
@@ -360,29 +362,34 @@ def verify(target, draft, drafted, lengths, temperature, uniforms, *, accepted=N
         _req(lengths, "lengths", torch.int32, (B,), dev)
     _req(temperature, "temperature", torch.float32, (B,), dev)
     _req(uniforms, "uniforms", torch.float32, (B, K + 1), dev)
-    accepted = torch.empty(B, dtype=torch.int32, device=dev) if accepted is None else accepted
-    tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev) if tokens is None else tokens
+    accepted = _out(accepted, "accepted", torch.int32, (B,), dev)
+    tokens = _out(tokens, "tokens", torch.int32, (B, K + 1), dev)
     if want_probs:
-        p_tok = torch.empty((B, K), dtype=torch.float32, device=dev) if p_tok is None else p_tok
-        q_tok = torch.empty((B, K), dtype=torch.float32, device=dev) if q_tok is None else q_tok
-    if dev_status is None:
-        dev_status = torch.zeros(1, dtype=torch.int32, device=dev)
-    ws = ws or workspace(OP_VERIFY, B, K, V, dev)
-    st = lib.dspark_verify(_ptr(target), _ptr(draft), code, B, K, V, _ptr(drafted), _ptr(lengths),
-                           _ptr(temperature), _ptr(uniforms), _ptr(accepted), _ptr(tokens),
-                           _ptr(p_tok), _ptr(q_tok), _ptr(dev_status), ws.ptr, ws.nbytes,
-                           _stream(stream, dev))
-    _check(st)
+        p_tok = _out(p_tok, "p_tok", torch.float32, (B, K), dev)
+        q_tok = _out(q_tok, "q_tok", torch.float32, (B, K), dev)
+    else:
+        p_tok = None if p_tok is None else _req(p_tok, "p_tok", torch.float32, (B, K), dev)
+        q_tok = None if q_tok is None else _req(q_tok, "q_tok", torch.float32, (B, K), dev)
+    dev_status = _status(dev_status, dev)
+    ws = _ws(ws, OP_VERIFY, B, K, V, dev, stream)
+    args = (_ptr(target), _ptr(draft), code, B, K, V, _ptr(drafted), _ptr(lengths),
+            _ptr(temperature), _ptr(uniforms), _ptr(accepted), _ptr(tokens), _ptr(p_tok),
+            _ptr(q_tok), _ptr(dev_status), ws.ptr, ws.nbytes, _stream(stream, dev))
+    if phases == PHASE_ALL:
+        _check(lib.dspark_verify(*args))
+    else:
+        _check(lib.dspark_verify_phase(int(phases), *args))
     return dict(accepted=accepted, tokens=tokens, p_tok=p_tok, q_tok=q_tok, dev_status=dev_status)
 
 
 def schedule_verify(conf, threshold: float, budget: int, min_len: int, target, draft, drafted,
                     temperature, uniforms, *, lengths=None, mask=None, survival=None,
                     accepted=None, tokens=None, p_tok=None, q_tok=None, dev_status=None,
-                    ws: Optional[Workspace] = None, stream=None):
-    """dspark_schedule_verify on torch tensors: the schedule and the verification
-    of one step in one call.  Returns dict(lengths, mask, survival, accepted,
-    tokens, p_tok, q_tok, dev_status)."""
+                    ws: Optional[Workspace] = None, stream=None, phases: int = PHASE_ALL):
+    """dspark_schedule_verify on torch tensors (``phases`` other than
+    PHASE_ALL: dspark_schedule_verify_phase): the schedule and the
+    verification of one step in one call.  Returns dict(lengths, mask,
+    survival, accepted, tokens, p_tok, q_tok, dev_status)."""
     torch = _torch()
     lib = load_library()
     dev = target.device
@@ -395,33 +402,31 @@ def schedule_verify(conf, threshold: float, budget: int, min_len: int, target, d
     _req(drafted, "drafted", torch.int32, (B, K), dev)
     _req(temperature, "temperature", torch.float32, (B,), dev)
     _req(uniforms, "uniforms", torch.float32, (B, K + 1), dev)
-    lengths = torch.empty(B, dtype=torch.int32, device=dev) if lengths is None else \
-        _req(lengths, "lengths", torch.int32, (B,), dev)
-    mask = torch.empty((B, K), dtype=torch.uint8, device=dev) if mask is None else \
-        _req(mask, "mask", torch.uint8, (B, K), dev)
-    survival = torch.empty((B, K), dtype=torch.float32, device=dev) if survival is None else \
-        _req(survival, "survival", torch.float32, (B, K), dev)
-    accepted = torch.empty(B, dtype=torch.int32, device=dev) if accepted is None else accepted
-    tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev) if tokens is None else tokens
-    p_tok = torch.empty((B, K), dtype=torch.float32, device=dev) if p_tok is None else p_tok
-    q_tok = torch.empty((B, K), dtype=torch.float32, device=dev) if q_tok is None else q_tok
-    if dev_status is None:
-        dev_status = torch.zeros(1, dtype=torch.int32, device=dev)
-    ws = ws or workspace(OP_SCHEDULE_VERIFY, B, K, V, dev)
-    st = lib.dspark_schedule_verify(_ptr(conf), float(threshold), int(budget), int(min_len),
-                                    _ptr(lengths), _ptr(mask), _ptr(survival), _ptr(target),
-                                    _ptr(draft), code, B, K, V, _ptr(drafted), _ptr(temperature),
-                                    _ptr(uniforms), _ptr(accepted), _ptr(tokens), _ptr(p_tok),
-                                    _ptr(q_tok), _ptr(dev_status), ws.ptr, ws.nbytes,
-                                    _stream(stream, dev))
-    _check(st)
+    lengths = _out(lengths, "lengths", torch.int32, (B,), dev)
+    mask = _out(mask, "mask", torch.uint8, (B, K), dev)
+    survival = _out(survival, "survival", torch.float32, (B, K), dev)
+    accepted = _out(accepted, "accepted", torch.int32, (B,), dev)
+    tokens = _out(tokens, "tokens", torch.int32, (B, K + 1), dev)
+    p_tok = _out(p_tok, "p_tok", torch.float32, (B, K), dev)
+    q_tok = _out(q_tok, "q_tok", torch.float32, (B, K), dev)
+    dev_status = _status(dev_status, dev)
+    ws = _ws(ws, OP_SCHEDULE_VERIFY, B, K, V, dev, stream)
+    args = (_ptr(conf), float(threshold), int(budget), int(min_len), _ptr(lengths), _ptr(mask),
+            _ptr(survival), _ptr(target), _ptr(draft), code, B, K, V, _ptr(drafted),
+            _ptr(temperature), _ptr(uniforms), _ptr(accepted), _ptr(tokens), _ptr(p_tok),
+            _ptr(q_tok), _ptr(dev_status), ws.ptr, ws.nbytes, _stream(stream, dev))
+    if phases == PHASE_ALL:
+        _check(lib.dspark_schedule_verify(*args))
+    else:
+        _check(lib.dspark_schedule_verify_phase(int(phases), *args))
     return dict(lengths=lengths, mask=mask, survival=survival, accepted=accepted, tokens=tokens,
                 p_tok=p_tok, q_tok=q_tok, dev_status=dev_status)
 
 
 def verify_greedy(target, drafted, lengths, *, accepted=None, tokens=None, dev_status=None,
-                  ws: Optional[Workspace] = None, stream=None):
-    """dspark_verify_greedy on torch tensors.  Returns dict(accepted, tokens, dev_status)."""
+                  ws: Optional[Workspace] = None, stream=None, phases: int = PHASE_ALL):
+    """dspark_verify_greedy on torch tensors (``phases`` other than PHASE_ALL:
+    dspark_verify_greedy_phase).  Returns dict(accepted, tokens, dev_status)."""
     torch = _torch()
     lib = load_library()
     dev = target.device
@@ -432,13 +437,14 @@ def verify_greedy(target, drafted, lengths, *, accepted=None, tokens=None, dev_s
     _req(drafted, "drafted", torch.int32, (B, K), dev)
     if lengths is not None:
         _req(lengths, "lengths", torch.int32, (B,), dev)
-    accepted = torch.empty(B, dtype=torch.int32, device=dev) if accepted is None else accepted
-    tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev) if tokens is None else tokens
-    if dev_status is None:
-        dev_status = torch.zeros(1, dtype=torch.int32, device=dev)
-    ws = ws or workspace(OP_VERIFY_GREEDY, B, K, V, dev)
-    st = lib.dspark_verify_greedy(_ptr(target), code, B, K, V, _ptr(drafted), _ptr(lengths),
-                                  _ptr(accepted), _ptr(tokens), _ptr(dev_status), ws.ptr,
-                                  ws.nbytes, _stream(stream, dev))
-    _check(st)
+    accepted = _out(accepted, "accepted", torch.int32, (B,), dev)
+    tokens = _out(tokens, "tokens", torch.int32, (B, K + 1), dev)
+    dev_status = _status(dev_status, dev)
+    ws = _ws(ws, OP_VERIFY_GREEDY, B, K, V, dev, stream)
+    args = (_ptr(target), code, B, K, V, _ptr(drafted), _ptr(lengths), _ptr(accepted),
+            _ptr(tokens), _ptr(dev_status), ws.ptr, ws.nbytes, _stream(stream, dev))
+    if phases == PHASE_ALL:
+        _check(lib.dspark_verify_greedy(*args))
+    else:
+        _check(lib.dspark_verify_greedy_phase(int(phases), *args))
     return dict(accepted=accepted, tokens=tokens, dev_status=dev_status)

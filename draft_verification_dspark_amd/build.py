@@ -1,7 +1,10 @@
-"""Build the gfx950 shared library ``libdspark.so`` in-tree with hipcc.
+"""Build the gfx950 shared libraries in-tree with hipcc.
 
-Every HIP source under ``csrc/`` is compiled in one hipcc invocation; the
-C ABI is declared in ``include/dspark.h`` at the repository root."""
+``libdspark.so`` is the verification library: every HIP source of the path
+under ``csrc/`` in one hipcc invocation, its C ABI declared in
+``include/dspark.h`` at the repository root.  ``libdspark_bench.so`` is the
+benchmark's measurement library (``csrc/probe.hip``, C ABI in
+``include/dspark_bench.h``); the verification library does not contain it."""
 from __future__ import annotations
 
 import os
@@ -10,8 +13,10 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["api.hip", "schedule.hip", "verify.hip", "calib.hip", "markov.hip", "probe.hip"]
+SOURCES = ["api.hip", "schedule.hip", "verify.hip", "calib.hip", "markov.hip"]
 LIB = os.path.join(HERE, "libdspark.so")
+BENCH_SOURCES = ["probe.hip"]
+BENCH_LIB = os.path.join(HERE, "libdspark_bench.so")
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
@@ -25,10 +30,11 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
-    """Compile the library to ``out``; ``defines`` are extra -D tuning knobs."""
+def build(verbose: bool = False, out: str = LIB, defines=(), sources=SOURCES) -> str:
+    """Compile ``sources`` (under csrc/) to ``out``; ``defines`` are extra -D
+    tuning knobs."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    srcs = [os.path.join(HERE, "csrc", s) for s in SOURCES]
+    srcs = [os.path.join(HERE, "csrc", s) for s in sources]
     tmp = out + ".tmp"
     cmd = [hipcc, *FLAGS, *[f"-D{d}" for d in defines], "-I", os.path.join(ROOT, "include"),
            "-I", os.path.join(HERE, "csrc"), *srcs, "-o", tmp]
@@ -44,5 +50,12 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     return out
 
 
+def build_all(verbose: bool = False) -> list:
+    """Both libraries: the verification library and the benchmark's."""
+    return [build(verbose=verbose),
+            build(verbose=verbose, out=BENCH_LIB, sources=BENCH_SOURCES)]
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    for p in build_all(verbose=True):
+        print(p)

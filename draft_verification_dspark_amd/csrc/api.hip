@@ -48,13 +48,9 @@ ScheduleLayout schedule_layout(int B, int K) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// events of dspark_set_stream_events (both NULL = off)
-hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
+constexpr int kPhaseAll = kPhaseStream | kPhaseFinish;
 
 }  // namespace
-
-// the plain-read reference kernel (probe.hip)
-int launch_read_probe(const void* x, size_t bytes, uint32_t* sink, hipStream_t st);
 
 // Compute units of the current device (cached per device; 256 if the query
 // fails).
@@ -182,13 +178,16 @@ static int verify_common(const void* target, const void* draft, int dtype, int B
                          const int32_t* drafted, const int32_t* lengths, const float* temperature,
                          const float* uniforms, int32_t* accepted, int32_t* tokens, float* p_tok,
                          float* q_tok, int32_t* dev_status, void* workspace, size_t ws_bytes,
-                         void* stream, int greedy_only, bool dry = false,
+                         void* stream, int greedy_only, int phases, bool dry = false,
                          const ScheduleArgs* fused = nullptr) {
   if (!target || !drafted || !accepted || !tokens || !dev_status || !workspace)
     return DSPARK_ERR_NULL;
   if (!greedy_only && (!draft || !temperature || !uniforms)) return DSPARK_ERR_NULL;
   if (B < 1 || K < 1 || V < 1 || K > kMaxK || B > kMaxB || V > (1 << 30)) return DSPARK_ERR_SHAPE;
   if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return DSPARK_ERR_DTYPE;
+  // a call split into its phases keeps one launch batch's state in the workspace
+  if (phases != kPhaseAll && (phases < 1 || phases > kPhaseAll)) return DSPARK_ERR_PARAM;
+  if (phases != kPhaseAll && B > kLaunchBatch) return DSPARK_ERR_SHAPE;
   const VerifyLayout L = verify_layout(B, K, V);
   if (ws_bytes < L.total || !aligned(workspace, kAlign)) return DSPARK_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
@@ -230,13 +229,21 @@ static int verify_common(const void* target, const void* draft, int dtype, int B
     sub.tokens = tokens + (size_t)b0 * (K + 1);
     sub.p_tok = a.p_tok ? a.p_tok + (size_t)b0 * K : nullptr;
     sub.q_tok = a.q_tok ? a.q_tok + (size_t)b0 * K : nullptr;
-    const bool first = b0 == 0;
-    const int st = launch_verify(sub, dtype, static_cast<hipStream_t>(stream),
-                                 first ? g_ev_before : nullptr, first ? g_ev_after : nullptr,
-                                 first ? fused : nullptr);
+    const int st = launch_verify(sub, dtype, static_cast<hipStream_t>(stream), phases,
+                                 b0 == 0 ? fused : nullptr);
     if (st != DSPARK_OK) return st;
   }
   return DSPARK_OK;
+}
+
+int dspark_verify_phase(int phases, const void* target_logits, const void* draft_logits,
+                        int dtype, int B, int K, int V, const int32_t* drafted,
+                        const int32_t* lengths, const float* temperature, const float* uniforms,
+                        int32_t* accepted, int32_t* tokens, float* p_tok, float* q_tok,
+                        int32_t* dev_status, void* workspace, size_t ws_bytes, void* stream) {
+  return verify_common(target_logits, draft_logits, dtype, B, K, V, drafted, lengths, temperature,
+                       uniforms, accepted, tokens, p_tok, q_tok, dev_status, workspace, ws_bytes,
+                       stream, 0, phases);
 }
 
 int dspark_verify(const void* target_logits, const void* draft_logits, int dtype, int B, int K,
@@ -244,18 +251,26 @@ int dspark_verify(const void* target_logits, const void* draft_logits, int dtype
                   const float* temperature, const float* uniforms, int32_t* accepted,
                   int32_t* tokens, float* p_tok, float* q_tok, int32_t* dev_status,
                   void* workspace, size_t ws_bytes, void* stream) {
-  return verify_common(target_logits, draft_logits, dtype, B, K, V, drafted, lengths, temperature,
-                       uniforms, accepted, tokens, p_tok, q_tok, dev_status, workspace, ws_bytes,
-                       stream, 0);
+  return dspark_verify_phase(kPhaseAll, target_logits, draft_logits, dtype, B, K, V, drafted,
+                             lengths, temperature, uniforms, accepted, tokens, p_tok, q_tok,
+                             dev_status, workspace, ws_bytes, stream);
+}
+
+int dspark_verify_greedy_phase(int phases, const void* target_logits, int dtype, int B, int K,
+                               int V, const int32_t* drafted, const int32_t* lengths,
+                               int32_t* accepted, int32_t* tokens, int32_t* dev_status,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  return verify_common(target_logits, nullptr, dtype, B, K, V, drafted, lengths, nullptr, nullptr,
+                       accepted, tokens, nullptr, nullptr, dev_status, workspace, ws_bytes, stream,
+                       1, phases);
 }
 
 int dspark_verify_greedy(const void* target_logits, int dtype, int B, int K, int V,
                          const int32_t* drafted, const int32_t* lengths, int32_t* accepted,
                          int32_t* tokens, int32_t* dev_status, void* workspace, size_t ws_bytes,
                          void* stream) {
-  return verify_common(target_logits, nullptr, dtype, B, K, V, drafted, lengths, nullptr, nullptr,
-                       accepted, tokens, nullptr, nullptr, dev_status, workspace, ws_bytes, stream,
-                       1);
+  return dspark_verify_greedy_phase(kPhaseAll, target_logits, dtype, B, K, V, drafted, lengths,
+                                    accepted, tokens, dev_status, workspace, ws_bytes, stream);
 }
 
 int dspark_calibrate(const float* raw, const float* theta, int B, int K, float* calibrated,
@@ -343,13 +358,14 @@ int dspark_markov_draft(const void* base, int dtype, int B, int K, int V, const 
   return launch_markov(a, dtype, static_cast<hipStream_t>(stream));
 }
 
-int dspark_schedule_verify(const float* conf, float threshold, int budget, int min_len,
-                           int32_t* lengths, uint8_t* mask, float* survival,
-                           const void* target_logits, const void* draft_logits, int dtype, int B,
-                           int K, int V, const int32_t* drafted, const float* temperature,
-                           const float* uniforms, int32_t* accepted, int32_t* tokens,
-                           float* p_tok, float* q_tok, int32_t* dev_status, void* workspace,
-                           size_t ws_bytes, void* stream) {
+int dspark_schedule_verify_phase(int phases, const float* conf, float threshold, int budget,
+                                 int min_len, int32_t* lengths, uint8_t* mask, float* survival,
+                                 const void* target_logits, const void* draft_logits, int dtype,
+                                 int B, int K, int V, const int32_t* drafted,
+                                 const float* temperature, const float* uniforms,
+                                 int32_t* accepted, int32_t* tokens, float* p_tok, float* q_tok,
+                                 int32_t* dev_status, void* workspace, size_t ws_bytes,
+                                 void* stream) {
   if (!workspace) return DSPARK_ERR_NULL;
   if (B < 1 || K < 1 || V < 1 || K > kMaxK || B > kMaxB || V > (1 << 30)) return DSPARK_ERR_SHAPE;
   // workspace: the verify layout, then the schedule layout
@@ -361,32 +377,29 @@ int dspark_schedule_verify(const float* conf, float threshold, int budget, int m
   if (st != DSPARK_OK) return st;
   st = verify_common(target_logits, draft_logits, dtype, B, K, V, drafted, lengths, temperature,
                      uniforms, accepted, tokens, p_tok, q_tok, dev_status, workspace, vbytes,
-                     stream, 0, true);
+                     stream, 0, phases, true);
   if (st != DSPARK_OK) return st;
   const bool fuse = B <= kFusedMaxB && K <= kFusedMaxK && (long long)B * K <= kFusedMaxPositions;
-  if (!fuse) {
+  if (!fuse && (phases & kPhaseStream)) {
     st = launch_schedule(sa, static_cast<hipStream_t>(stream));
     if (st != DSPARK_OK) return st;
   }
   return verify_common(target_logits, draft_logits, dtype, B, K, V, drafted, lengths, temperature,
                        uniforms, accepted, tokens, p_tok, q_tok, dev_status, workspace, vbytes,
-                       stream, 0, false, fuse ? &sa : nullptr);
+                       stream, 0, phases, false, fuse ? &sa : nullptr);
 }
 
-int dspark_set_stream_events(void* before, void* after) {
-  if (before && after) {
-    g_ev_before = static_cast<hipEvent_t>(before);
-    g_ev_after = static_cast<hipEvent_t>(after);
-  } else {
-    g_ev_before = g_ev_after = nullptr;
-  }
-  return DSPARK_OK;
-}
-
-int dspark_read_probe(const void* x, size_t bytes, uint32_t* sink, void* stream) {
-  if (!x || !sink) return DSPARK_ERR_NULL;
-  if (bytes == 0 || bytes % 16 != 0 || !aligned(x, 16)) return DSPARK_ERR_PARAM;
-  return launch_read_probe(x, bytes, sink, static_cast<hipStream_t>(stream));
+int dspark_schedule_verify(const float* conf, float threshold, int budget, int min_len,
+                           int32_t* lengths, uint8_t* mask, float* survival,
+                           const void* target_logits, const void* draft_logits, int dtype, int B,
+                           int K, int V, const int32_t* drafted, const float* temperature,
+                           const float* uniforms, int32_t* accepted, int32_t* tokens,
+                           float* p_tok, float* q_tok, int32_t* dev_status, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  return dspark_schedule_verify_phase(kPhaseAll, conf, threshold, budget, min_len, lengths, mask,
+                                      survival, target_logits, draft_logits, dtype, B, K, V,
+                                      drafted, temperature, uniforms, accepted, tokens, p_tok,
+                                      q_tok, dev_status, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -31,11 +31,14 @@ struct VerifyArgs {
 
 struct ScheduleArgs;
 
-// ev_before / ev_after: optional events recorded around the streaming pass.
+// phases: kPhaseStream enqueues the streaming pass, kPhaseFinish the launches
+// after it (decide, draw), both the whole call.
 // fused: the schedule to work out inside the streaming pass (at most
 // kFusedMaxB requests and kFusedMaxPositions positions), else NULL.
-int launch_verify(VerifyArgs& a, int dtype, hipStream_t st, hipEvent_t ev_before,
-                  hipEvent_t ev_after, const ScheduleArgs* fused = nullptr);
+constexpr int kPhaseStream = DSPARK_PHASE_STREAM;
+constexpr int kPhaseFinish = DSPARK_PHASE_FINISH;
+int launch_verify(VerifyArgs& a, int dtype, hipStream_t st, int phases,
+                  const ScheduleArgs* fused = nullptr);
 int compute_units();  // of the current device
 
 // Requests per launch sequence of dspark_verify (the streaming kernel keeps

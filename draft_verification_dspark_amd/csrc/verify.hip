@@ -1165,35 +1165,36 @@ __global__ void __launch_bounds__(kBlock) k_draw(VerifyArgs a) {
 // ------------------------------------------------------------------ launch
 
 template <int DT, bool VEC>
-static int launch_verify_t(VerifyArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1,
-                           const ScheduleArgs* fused) {
+static int launch_verify_t(VerifyArgs& a, hipStream_t st, int phases, const ScheduleArgs* fused) {
   const size_t lds = sizeof(int) * (3 * (size_t)a.B + 1);
   const int grid = compute_units();
-  if (ev0 && ev1 && hipEventRecord(ev0, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
-  if (fused)
-    hipLaunchKernelGGL((k_stream_rows<DT, VEC, true>), dim3((unsigned)grid), dim3(kStreamBlock),
-                       lds, st, a, *fused);
-  else
-    hipLaunchKernelGGL((k_stream_rows<DT, VEC, false>), dim3((unsigned)grid), dim3(kStreamBlock),
-                       lds, st, a, ScheduleArgs{});
-  if (ev0 && ev1 && hipEventRecord(ev1, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
-  a.groups = (a.G + kChunksPerGroup - 1) / kChunksPerGroup;
-  hipLaunchKernelGGL((k_decide<DT, VEC>), dim3((unsigned)((long)a.B * a.groups)),
-                     dim3(kDecideBlock), 0, st, a);
-  if (!a.greedy_only)
-    hipLaunchKernelGGL((k_draw<DT, VEC>), dim3((unsigned)a.B), dim3(kBlock), 0, st, a);
+  if (phases & kPhaseStream) {
+    if (fused)
+      hipLaunchKernelGGL((k_stream_rows<DT, VEC, true>), dim3((unsigned)grid), dim3(kStreamBlock),
+                         lds, st, a, *fused);
+    else
+      hipLaunchKernelGGL((k_stream_rows<DT, VEC, false>), dim3((unsigned)grid),
+                         dim3(kStreamBlock), lds, st, a, ScheduleArgs{});
+  }
+  if (phases & kPhaseFinish) {
+    a.groups = (a.G + kChunksPerGroup - 1) / kChunksPerGroup;
+    hipLaunchKernelGGL((k_decide<DT, VEC>), dim3((unsigned)((long)a.B * a.groups)),
+                       dim3(kDecideBlock), 0, st, a);
+    if (!a.greedy_only)
+      hipLaunchKernelGGL((k_draw<DT, VEC>), dim3((unsigned)a.B), dim3(kBlock), 0, st, a);
+  }
   return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_ERR_LAUNCH;
 }
 
-int launch_verify(VerifyArgs& a, int dtype, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1,
+int launch_verify(VerifyArgs& a, int dtype, hipStream_t st, int phases,
                   const ScheduleArgs* fused) {
   if (fused && (a.B > kStreamBlock || a.K > kFusedMaxK || a.B * a.K > kSchedLds))
     return DSPARK_ERR_SHAPE;
   if (dtype == DSPARK_BF16)
-    return a.vec_ok ? launch_verify_t<DSPARK_BF16, true>(a, st, ev0, ev1, fused)
-                    : launch_verify_t<DSPARK_BF16, false>(a, st, ev0, ev1, fused);
-  return a.vec_ok ? launch_verify_t<DSPARK_F32, true>(a, st, ev0, ev1, fused)
-                  : launch_verify_t<DSPARK_F32, false>(a, st, ev0, ev1, fused);
+    return a.vec_ok ? launch_verify_t<DSPARK_BF16, true>(a, st, phases, fused)
+                    : launch_verify_t<DSPARK_BF16, false>(a, st, phases, fused);
+  return a.vec_ok ? launch_verify_t<DSPARK_F32, true>(a, st, phases, fused)
+                  : launch_verify_t<DSPARK_F32, false>(a, st, phases, fused);
 }
 
 }  // namespace dspark

@@ -383,37 +383,52 @@ DSPARK_API int dspark_schedule_verify(const float* conf, float threshold, int bu
                                       void* workspace, size_t ws_bytes, void* stream);
 
 /*
- * dspark_set_stream_events — timing hook for the streaming pass (measurement
- * support; the pages define no such call).
+ * The calls above in two halves, for callers that want to place or time the
+ * streaming pass on its own (for instance to run the streaming pass of the
+ * next batch on another stream while this one finishes, or to bracket it
+ * with events).  The pages define no such split; what is computed is exactly
+ * what the call without the suffix computes.
  *
- * When `before` and `after` (hipEvent_t handles passed as void*, created by
- * the caller) are both non-NULL, every following dspark_verify and
- * dspark_verify_greedy call records `before` on its stream immediately before
- * it launches its streaming pass (the kernel that reads each scheduled logits
- * row once) and `after` immediately after that launch, so that
- * hipEventElapsedTime(before, after) is the streaming pass alone. With
- * several sub-batches (B > 2048) the events bracket the first sub-batch's
- * pass. Passing NULL for either turns the hook off. The setting is
- * process-wide and unsynchronised: set it from the thread that issues the
- * calls, and keep the events alive while it is set. Returns DSPARK_OK.
+ *   phases  DSPARK_PHASE_STREAM: enqueue everything up to and including the
+ *           streaming pass (the launch that reads every scheduled logits row
+ *           once; for dspark_schedule_verify_phase with more than 768
+ *           requests, the schedule's own launch first);
+ *           DSPARK_PHASE_FINISH: enqueue the rest (the decision, the residual
+ *           and the draw), which reads what the streaming pass left in the
+ *           workspace;
+ *           both bits: the whole call.
+ *   other arguments: as for the call without the suffix.
+ * The FINISH half must follow the STREAM half on the same stream, with the
+ * same arguments and workspace, and nothing that writes the workspace in
+ * between. A split call (phases other than both bits) needs
+ * B <= 2048 (the workspace holds one launch batch); larger batches return
+ * DSPARK_ERR_SHAPE. phases outside 1..3 returns DSPARK_ERR_PARAM.
  */
-DSPARK_API int dspark_set_stream_events(void* before, void* after);
+#define DSPARK_PHASE_STREAM 1
+#define DSPARK_PHASE_FINISH 2
 
-/*
- * dspark_read_probe — plain contiguous read of a device buffer (measurement
- * support; the pages define no such call).
- *
- * Reads `bytes` bytes at `x` once, in the launch shape of the streaming pass
- * (one 768-thread workgroup per compute unit, 8 KB tiles of coalesced
- * 16-byte loads per wave), and computes nothing from them that reaches
- * memory: `sink` (one uint32_t of device memory) is written only if a
- * checksum of the data equals a fixed constant. It is the reference with
- * which the streaming pass's bandwidth at the same byte count is compared.
- * Work goes onto `stream`; nothing is allocated.
- * Errors: NULL x or sink (DSPARK_ERR_NULL); bytes zero or not a multiple of
- * 16, or x not 16-byte aligned (DSPARK_ERR_PARAM).
- */
-DSPARK_API int dspark_read_probe(const void* x, size_t bytes, uint32_t* sink, void* stream);
+DSPARK_API int dspark_verify_phase(int phases, const void* target_logits, const void* draft_logits,
+                                   int dtype, int B, int K, int V, const int32_t* drafted,
+                                   const int32_t* lengths, const float* temperature,
+                                   const float* uniforms, int32_t* accepted, int32_t* tokens,
+                                   float* p_tok, float* q_tok, int32_t* dev_status,
+                                   void* workspace, size_t ws_bytes, void* stream);
+
+DSPARK_API int dspark_verify_greedy_phase(int phases, const void* target_logits, int dtype, int B,
+                                          int K, int V, const int32_t* drafted,
+                                          const int32_t* lengths, int32_t* accepted,
+                                          int32_t* tokens, int32_t* dev_status, void* workspace,
+                                          size_t ws_bytes, void* stream);
+
+DSPARK_API int dspark_schedule_verify_phase(int phases, const float* conf, float threshold,
+                                            int budget, int min_len, int32_t* lengths,
+                                            uint8_t* mask, float* survival,
+                                            const void* target_logits, const void* draft_logits,
+                                            int dtype, int B, int K, int V, const int32_t* drafted,
+                                            const float* temperature, const float* uniforms,
+                                            int32_t* accepted, int32_t* tokens, float* p_tok,
+                                            float* q_tok, int32_t* dev_status, void* workspace,
+                                            size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -11,16 +11,30 @@ import draft_verification_dspark_amd as ds
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared():
-    with open(os.path.join(ROOT, "include", "dspark.h")) as f:
+def _declared(header="dspark.h", prefix="DSPARK_API"):
+    with open(os.path.join(ROOT, "include", header)) as f:
         src = f.read()
-    return re.findall(r"DSPARK_API\s+[\w\s\*]+?\b(dspark_\w+)\s*\(", src)
+    return re.findall(prefix + r"\s+[\w\s\*]+?\b(dspark_\w+)\s*\(", src)
 
 
 def test_exports_every_declared_symbol():
     lib = ds.load_library()
     names = _declared()
     assert set(names) == set(ds.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    # the measurement aids live in the benchmark's library only
+    for n in ("dspark_read_probe", "dspark_set_stream_events", "dspark_bench_read_probe"):
+        assert not hasattr(lib, n), n
+
+
+BENCH_LIB = os.path.join(ROOT, "draft_verification_dspark_amd", "libdspark_bench.so")
+
+
+def test_bench_library_exports_its_header():
+    lib = ctypes.CDLL(BENCH_LIB)
+    names = _declared("dspark_bench.h", r'__attribute__\(\(visibility\("default"\)\)\)')
+    assert names == ["dspark_bench_read_probe"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -170,22 +184,106 @@ def test_binding_refuses_without_library(tmp_path):
         mod._lib = saved
 
 
-def test_stream_events_hook_off_without_gpu():
-    # NULL handles switch the hook off; no HIP call is made
-    lib = ds.load_library()
-    assert lib.dspark_set_stream_events(None, None) == 0
-    assert lib.dspark_set_stream_events(P, None) == 0
-    ds.dspark_set_stream_events(None, None)
-
-
 def test_read_probe_argument_errors():
     # checks come before any launch: NULL pointers, sizes, alignment
+    lib = ctypes.CDLL(BENCH_LIB)
+    f = lib.dspark_bench_read_probe
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    assert f(None, 16, P, None) == 1
+    assert f(P, 16, None, None) == 1
+    assert f(P, 0, P, None) == ds.ERR_PARAM
+    assert f(P, 24, P, None) == ds.ERR_PARAM
+    assert f(P + 8, 32, P, None) == ds.ERR_PARAM
+
+
+def test_phase_argument_errors():
     lib = ds.load_library()
-    assert lib.dspark_read_probe(None, 16, P, None) == 1
-    assert lib.dspark_read_probe(P, 16, None, None) == 1
-    assert lib.dspark_read_probe(P, 0, P, None) == ds.ERR_PARAM
-    assert lib.dspark_read_probe(P, 24, P, None) == ds.ERR_PARAM
-    assert lib.dspark_read_probe(P + 8, 32, P, None) == ds.ERR_PARAM
+    args = (P, P, 1, 2, 4, 100, P, None, P, P, P, P, None, None, P, P, 10 ** 9, None)
+    assert lib.dspark_verify_phase(0, *args) == ds.ERR_PARAM
+    assert lib.dspark_verify_phase(4, *args) == ds.ERR_PARAM
+    assert lib.dspark_verify_phase(-1, *args) == ds.ERR_PARAM
+    # a split call keeps one launch batch (2048 requests) in the workspace
+    big = (P, P, 1, 2049, 4, 100, P, None, P, P, P, P, None, None, P, P, 10 ** 12, None)
+    assert lib.dspark_verify_phase(1, *big) == 2
+    assert lib.dspark_verify_phase(2, *big) == 2
+    g = (P, 1, 2, 4, 100, P, None, P, P, P, P, 16, None)
+    assert lib.dspark_verify_greedy_phase(1, *g) == 5
+    assert lib.dspark_verify_greedy_phase(5, *g[:-2], 10 ** 9, None) == ds.ERR_PARAM
+    sv = (P, 0.1, -1, 1, P, None, None, P, P, 1, 2, 4, 100, P, P, P, P, P, None, None, P, P,
+          10 ** 9, None)
+    assert lib.dspark_schedule_verify_phase(3, *sv[:-2], 8, None) == 5
+    assert lib.dspark_schedule_verify_phase(7, *sv) == ds.ERR_PARAM
+
+
+# ---------------------------------------------------------------- binding checks
+
+def _cpu_case(B=2, K=4, V=64):
+    import torch
+    t = torch.zeros((B, K + 1, V), dtype=torch.bfloat16)
+    d = torch.zeros((B, K, V), dtype=torch.bfloat16)
+    y = torch.zeros((B, K), dtype=torch.int32)
+    T = torch.ones(B, dtype=torch.float32)
+    u = torch.zeros((B, K + 1), dtype=torch.float32)
+    c = torch.ones((B, K), dtype=torch.float32)
+    return t, d, y, T, u, c
+
+
+def _bad_outputs(B=2, K=4):
+    import torch
+    return [
+        ("accepted", torch.zeros(B + 1, dtype=torch.int32)),
+        ("accepted", torch.zeros(B, dtype=torch.int64)),
+        ("tokens", torch.zeros((B, K), dtype=torch.int32)),
+        ("tokens", torch.zeros((K + 1, B), dtype=torch.int32).t()),   # not contiguous
+        ("p_tok", torch.zeros((B, K), dtype=torch.float64)),
+        ("q_tok", torch.zeros((B, K + 1), dtype=torch.float32)),
+        ("dev_status", torch.zeros(2, dtype=torch.int32)),
+        ("dev_status", torch.zeros(1, dtype=torch.float32)),
+    ]
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_verify_binding_refuses_bad_outputs(i):
+    t, d, y, T, u, _ = _cpu_case()
+    name, bad = _bad_outputs()[i]
+    with pytest.raises(ValueError, match=name):
+        ds.verify(t, d, y, None, T, u, **{name: bad})
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_schedule_verify_binding_refuses_bad_outputs(i):
+    t, d, y, T, u, c = _cpu_case()
+    name, bad = _bad_outputs()[i]
+    with pytest.raises(ValueError, match=name):
+        ds.schedule_verify(c, 0.1, -1, 1, t, d, y, T, u, **{name: bad})
+
+
+@pytest.mark.parametrize("i", [0, 1, 2, 3, 6, 7])
+def test_verify_greedy_binding_refuses_bad_outputs(i):
+    t, _, y, _, _, _ = _cpu_case()
+    name, bad = _bad_outputs()[i]
+    with pytest.raises(ValueError, match=name):
+        ds.verify_greedy(t, y, None, **{name: bad})
+
+
+def test_schedule_binding_refuses_bad_outputs():
+    import torch
+    c = torch.ones((3, 4), dtype=torch.float32)
+    for kw in (dict(lengths=torch.zeros(4, dtype=torch.int32)),
+               dict(mask=torch.zeros((3, 4), dtype=torch.bool)),
+               dict(survival=torch.zeros((4, 3), dtype=torch.float32)),
+               dict(dev_status=torch.zeros(1, dtype=torch.int64))):
+        with pytest.raises(ValueError, match=next(iter(kw))):
+            ds.schedule(c, 0.1, -1, 1, **kw)
+
+
+def test_binding_refuses_a_small_workspace():
+    t, d, y, T, u, _ = _cpu_case()
+
+    class Small:
+        nbytes, ptr = 16, P
+    with pytest.raises(ValueError, match="workspace"):
+        ds.verify(t, d, y, None, T, u, ws=Small())
 
 
 def _sv(conf=P, thr=0.1, budget=-1, ml=1, L=P, t=P, d=P, dtype=1, B=2, K=4, V=100, y=P, T=P,

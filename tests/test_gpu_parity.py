@@ -21,6 +21,11 @@ def _sched(w):
 
 
 def _check_workload(w, requests=None, check_sched=True):
+    """Both ways of running a step, against one oracle run on the same inputs:
+    dspark_schedule then dspark_verify, and dspark_schedule_verify (the
+    schedule worked out inside the streaming launch for B <= 768, its own
+    launch first above)."""
+    print(f"[{w.name} seed+{w.seed_offset}] B={w.B} K={w.K} V={w.V}", flush=True)
     lengths, mask, surv, st = _sched(w)
     torch.cuda.synchronize()
     ref_s = oracle.schedule(host(w.conf), w.threshold, w.budget, w.min_len)
@@ -28,18 +33,22 @@ def _check_workload(w, requests=None, check_sched=True):
         compare_schedule((host(lengths), host(mask), host(surv)), ref_s)
     assert int(st.item()) == 0
     out = ds.verify(w.target, w.draft, w.drafted, lengths, w.temperature, w.uniforms)
+    fu = ds.schedule_verify(w.conf, w.threshold, w.budget, w.min_len, w.target, w.draft,
+                            w.drafted, w.temperature, w.uniforms)
     torch.cuda.synchronize()
-    g = {k: host(v) for k, v in out.items()}
+    compare_schedule((host(fu["lengths"]), host(fu["mask"]), host(fu["survival"])), ref_s)
     L = host(lengths)
     ref = oracle.verify(host(w.target), host(w.draft), host(w.drafted), L, host(w.temperature),
                         host(w.uniforms), requests=requests)
-    rep = compare_verify(g, ref, L, host(w.temperature), requests=requests)
-    print(f"[{w.name} seed+{w.seed_offset}] requests={rep.n_requests} mismatches={rep.n_mismatch} "
-          f"boundary={rep.n_boundary} worst_prob_rel={rep.worst_prob_rel:.2e} sumL={int(L.sum())}",
-          flush=True)
-    rep.assert_ok()
-    assert int(g["dev_status"][0]) == ref["flags"] == 0
-    return g, ref, L
+    for name, o in (("two calls", out), ("one call", fu)):
+        g = {k: host(o[k]) for k in ("accepted", "tokens", "p_tok", "q_tok", "dev_status")}
+        rep = compare_verify(g, ref, L, host(w.temperature), requests=requests)
+        print(f"[{w.name} seed+{w.seed_offset}] {name}: requests={rep.n_requests} "
+              f"mismatches={rep.n_mismatch} boundary={rep.n_boundary} "
+              f"worst_prob_rel={rep.worst_prob_rel:.2e} sumL={int(L.sum())}", flush=True)
+        rep.assert_ok()
+        assert int(g["dev_status"][0]) == ref["flags"] == 0
+    return {k: host(v) for k, v in out.items()}, ref, L
 
 
 @pytest.mark.parametrize("seed", [0, 100, 200])
@@ -49,12 +58,14 @@ def test_workload_full_size(wid, seed):
     _check_workload(w)
 
 
+@pytest.mark.parametrize("seed", [0, 100, 200])
 @pytest.mark.parametrize("wid", [4, 5])
-def test_workload_full_size_large(wid):
-    w = workloads.make(wid, seed_offset=0, device=DEV)
-    # every request for workload 4; a deterministic quarter of workload 5
-    req = None if wid == 4 else list(range(0, w.B, 4))
-    _check_workload(w, requests=req)
+def test_workload_full_size_large(wid, seed):
+    # every request of the 256- and 1024-request workloads
+    w = workloads.make(wid, seed_offset=seed, device=DEV)
+    _check_workload(w)
+    del w
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("seed", [100, 200])
@@ -690,43 +701,99 @@ def test_schedule_verify_flags_bad_confidence():
     assert int(fu["dev_status"].item()) & ds.DEV_BAD_CONF
 
 
-# ---------------------------------------------------------------- timing hook
+# ---------------------------------------------------------------- split calls
+
+def _bench_probe():
+    import ctypes
+    import os
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "draft_verification_dspark_amd", "libdspark_bench.so")
+    lib = ctypes.CDLL(path)
+    f = lib.dspark_bench_read_probe
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    return f
+
 
 @pytest.mark.parametrize("nbytes", [16, 8192 * 3 + 48, 82_450_608])
 def test_read_probe_reads_and_writes_nothing(nbytes):
-    # the plain-read reference: whole tiles and a ragged tail; the sink keeps
-    # its value (the checksum of random data is not the magic constant)
+    # the benchmark's plain-read yardstick: whole tiles and a ragged tail; the
+    # sink keeps its value (the checksum of random data is not the magic constant)
     x = torch.randint(0, 256, (nbytes + 64,), dtype=torch.uint8, device=DEV)
     sink = torch.full((4,), 7, dtype=torch.int32, device=DEV)
     print(f"read probe {nbytes} bytes", flush=True)
-    ds.read_probe(x, nbytes, sink)
+    assert _bench_probe()(x.data_ptr(), nbytes, sink.data_ptr(),
+                          torch.cuda.current_stream().cuda_stream) == 0
     torch.cuda.synchronize()
     assert sink.tolist() == [7, 7, 7, 7]
 
 
-def test_stream_events_bracket_the_streaming_pass():
-    w = workloads.make(3, device=DEV)
-    lengths, _, _, _ = _sched(w)
+def _same(a, b, keys):
+    for k in keys:
+        assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("wid,kw", [(3, {}), (5, dict(B=900, V=20000)), (2, dict(B=5, V=4097))])
+def test_split_phases_equal_the_whole_call(wid, kw):
+    # the STREAM half then the FINISH half, with events around the first,
+    # give bit for bit what the whole call gives (fused schedule for B <= 768,
+    # the schedule's own launch first above it)
+    w = workloads.make(wid, device=DEV, **kw)
+    print(f"split phases {w.name} B={w.B} V={w.V}", flush=True)
+    args = (w.conf, w.threshold, w.budget, w.min_len, w.target, w.draft, w.drafted,
+            w.temperature, w.uniforms)
+    whole = ds.schedule_verify(*args)
     stream = torch.cuda.current_stream()
-    e0, e1, c0, c1 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
-    for e in (e0, e1):
-        e.record(stream)               # creates the HIP events
-    ds.dspark_set_stream_events(e0, e1)
-    try:
-        c0.record(stream)
-        out = ds.verify(w.target, w.draft, w.drafted, lengths, w.temperature, w.uniforms)
-        c1.record(stream)
-        torch.cuda.synchronize()
-    finally:
-        ds.dspark_set_stream_events(None, None)
-    t_pass, t_call = e0.elapsed_time(e1), c0.elapsed_time(c1)
-    print(f"streaming pass {t_pass * 1e3:.1f} us of verify {t_call * 1e3:.1f} us", flush=True)
-    assert 0.0 < t_pass < t_call
-    # the hook changes no result
-    ref = ds.verify(w.target, w.draft, w.drafted, lengths, w.temperature, w.uniforms)
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    e0.record(stream)
+    part = ds.schedule_verify(*args, phases=ds.PHASE_STREAM)
+    e1.record(stream)
+    part = ds.schedule_verify(*args, phases=ds.PHASE_FINISH, **{k: part[k] for k in part})
+    e2.record(stream)
     torch.cuda.synchronize()
-    for k in ("accepted", "tokens", "p_tok", "q_tok"):
-        assert torch.equal(out[k], ref[k]), k
+    t_s, t_c = e0.elapsed_time(e1), e0.elapsed_time(e2)
+    print(f"streaming half {t_s * 1e3:.1f} us of {t_c * 1e3:.1f} us", flush=True)
+    assert 0.0 < t_s < t_c
+    _same(whole, part, ("lengths", "mask", "survival", "accepted", "tokens", "p_tok", "q_tok",
+                        "dev_status"))
+    L = whole["lengths"]
+    v = ds.verify(w.target, w.draft, w.drafted, L, w.temperature, w.uniforms)
+    vs = ds.verify(w.target, w.draft, w.drafted, L, w.temperature, w.uniforms,
+                   phases=ds.PHASE_STREAM)
+    vs = ds.verify(w.target, w.draft, w.drafted, L, w.temperature, w.uniforms,
+                   phases=ds.PHASE_FINISH, accepted=vs["accepted"], tokens=vs["tokens"],
+                   p_tok=vs["p_tok"], q_tok=vs["q_tok"], dev_status=vs["dev_status"])
+    g = ds.verify_greedy(w.target, w.drafted, L)
+    gs = ds.verify_greedy(w.target, w.drafted, L, phases=ds.PHASE_STREAM)
+    gs = ds.verify_greedy(w.target, w.drafted, L, phases=ds.PHASE_FINISH, accepted=gs["accepted"],
+                          tokens=gs["tokens"], dev_status=gs["dev_status"])
+    torch.cuda.synchronize()
+    _same(v, vs, ("accepted", "tokens", "p_tok", "q_tok", "dev_status"))
+    _same(g, gs, ("accepted", "tokens", "dev_status"))
+
+
+def test_workspaces_are_per_stream():
+    # the binding's cached workspaces: one per stream, never shared between
+    # streams that may run at the same time
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    a = ds.workspace(ds.OP_VERIFY, 4, 4, 1000, DEV, stream=s1)
+    b = ds.workspace(ds.OP_VERIFY, 4, 4, 1000, DEV, stream=s2)
+    c = ds.workspace(ds.OP_VERIFY, 4, 4, 1000, DEV, stream=s1)
+    assert a is c and a is not b and a.ptr != b.ptr
+    # two streams verifying different batches at once give each its own result
+    w1 = workloads.make(3, device=DEV, B=8, V=30000)
+    w2 = workloads.make(3, device=DEV, B=8, V=30000, seed_offset=100)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s1):
+        o1 = ds.verify(w1.target, w1.draft, w1.drafted, None, w1.temperature, w1.uniforms, stream=s1)
+    with torch.cuda.stream(s2):
+        o2 = ds.verify(w2.target, w2.draft, w2.drafted, None, w2.temperature, w2.uniforms, stream=s2)
+    torch.cuda.synchronize()
+    r1 = ds.verify(w1.target, w1.draft, w1.drafted, None, w1.temperature, w1.uniforms)
+    r2 = ds.verify(w2.target, w2.draft, w2.drafted, None, w2.temperature, w2.uniforms)
+    torch.cuda.synchronize()
+    _same(o1, r1, ("accepted", "tokens", "p_tok", "q_tok"))
+    _same(o2, r2, ("accepted", "tokens", "p_tok", "q_tok"))
 
 
 # ---------------------------------------------------------------- calibration
