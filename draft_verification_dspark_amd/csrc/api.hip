@@ -28,7 +28,7 @@ VerifyLayout verify_layout(int B, int K, int V) {
   size_t off = 0;
   L.req = off;   off += up(sizeof(ReqState) * (size_t)B);
   L.part1 = off; off += up(sizeof(Partial) * (size_t)B * (K + 1) * 2 * G);
-  L.part2 = off; off += up(sizeof(double) * (size_t)B * G);
+  L.part2 = off; off += up(sizeof(ResidualChunk) * (size_t)B * G);
   L.total = off;
   return L;
 }
@@ -205,7 +205,7 @@ static int verify_common(const void* target, const void* draft, int dtype, int B
   a.dev_status = dev_status;
   a.req = reinterpret_cast<ReqState*>(ws + L.req);
   a.part1 = reinterpret_cast<Partial*>(ws + L.part1);
-  a.part2 = reinterpret_cast<double*>(ws + L.part2);
+  a.part2 = reinterpret_cast<ResidualChunk*>(ws + L.part2);
   a.K = K;
   a.V = V;
   const int per_vec = dtype == DSPARK_BF16 ? 8 : 4;

@@ -22,7 +22,7 @@ struct VerifyArgs {
   int32_t* dev_status;
   ReqState* req;       // [B]
   Partial* part1;      // [B*(K+1)*2*G] chunk summaries, (request, row j, side) major
-  double* part2;       // [B*G] residual mass per chunk of the rejected row pair
+  ResidualChunk* part2;  // [B*G] residual sums per chunk of the rejected row pair
   int B, K, V, G;
   int groups;          // k_decide workgroups per request
   int greedy_only;

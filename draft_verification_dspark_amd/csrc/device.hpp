@@ -18,9 +18,6 @@ constexpr int kUnroll = DSPARK_UNROLL;  // 16-byte vectors per lane per work ite
 constexpr int kBlock = 256;       // 4 waves per workgroup
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr float kLog2e = 1.4426950408889634f;
-// an element whose normalised p or q reaches 2^-12 is recomputed in fp64 in
-// the residual pass (p - q cancels there)
-constexpr float kHeavy = 1.0f / 4096.0f;
 
 // Elements per 16-byte vector and per work item for each storage type.
 template <int DT> struct Elem;
@@ -65,6 +62,14 @@ struct alignas(8) RowSum {
   int pad;
 };
 
+// Per-chunk sums of the rejected row pair (k_decide to k_draw): with d(v)
+// the difference of the target and the rescaled draft term of token v and
+// e2(v) that draft term, z = sum max(0, d), d = sum d, q = sum of e2 where
+// d > 0, e2 = sum e2.
+struct alignas(16) ResidualChunk {
+  double z, d, q, e2;
+};
+
 // Per-request state handed from k_decide to k_draw.
 enum : int { kModeNone = 0, kModeResidual = 1, kModeBonus = 2 };
 enum : int { kKindSoftmax = 0, kKindGreedy = 1, kKindSkip = 2 };
@@ -74,6 +79,7 @@ struct alignas(16) ReqState {
   int row;      // target row of the draw (rejected position, or L)
   int a;        // accepted count (column of the drawn token)
   float c;      // log2(e) / T as fp32
+  float clo;    // log2(e) / T - c
   float kt;     // shift of the target row
   float kd;     // shift of the draft row
   double st;    // sum of 2^(x*c - kt) over the target row

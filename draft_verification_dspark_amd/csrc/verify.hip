@@ -63,7 +63,8 @@ __device__ __forceinline__ Partial* row_parts(const VerifyArgs& a, int b, int j,
 // arrays: clamped length, greedy / softmax / skipped, c = log2(e) / T.
 struct ReqInfo {
   int L, kind, bad;
-  float c;
+  float c;    // log2(e) / T rounded to fp32 (the streaming pass's factor)
+  float clo;  // log2(e) / T - c, so that c + clo carries it to ~2^-48
 };
 
 // L: the request's length as given (checked and clamped here); T: its
@@ -72,6 +73,7 @@ __device__ __forceinline__ ReqInfo req_info_lt(const VerifyArgs& a, int L, float
   ReqInfo r;
   r.bad = 0;
   r.c = 0.f;
+  r.clo = 0.f;
   if (L < 0 || L > a.K) {
     r.bad |= DSPARK_DEV_BAD_LENGTH;
     L = L < 0 ? 0 : a.K;
@@ -87,7 +89,9 @@ __device__ __forceinline__ ReqInfo req_info_lt(const VerifyArgs& a, int L, float
       r.kind = kKindGreedy;
     } else {
       r.kind = kKindSoftmax;
-      r.c = (float)(1.4426950408889634 / (double)T);
+      const double c64 = 1.4426950408889634 / (double)T;
+      r.c = (float)c64;
+      r.clo = (float)(c64 - (double)r.c);
     }
   }
   return r;
@@ -505,33 +509,83 @@ __device__ RowSum merge_argmax16(const Partial* p, int G, int sub) {
   return r;
 }
 
-// probability of logit x under a merged row: 2^(x*c - K*) / S, in fp64
-
-// Residual p - q of one row pair at fp32 speed, with the elements whose
-// normalised p or q reaches 2^-12 redone in fp64 (their fp32 rounding would
-// show after dividing by a small residual mass).  The fp32 path takes
-// 2^(x*c - K*) with the row's integer shift K* (the argument rounds once, no
-// error common to the row) times fp32(1/S).
+// The residual of a rejected row pair, element by element, in a form whose
+// rounding error is relative to the difference itself rather than to p or
+// q.  With x1 = xt*c - kt, x2 = xd*c - kd + log2(St'/Sd') and g = x1 - x2,
+//   e1 = 2^x1,  e2 = 2^x2,  d = e1 - e2 = 2^x1 (1 - 2^-g)  (g >= 0; the
+//   mirror image for g < 0),
+// where St', Sd' are the merged rows' sums from the streaming pass.  In units
+// of the target row's sum, e1 is p(v) and e2 is q(v) rescaled by St'/Sd'.
+// g = (xt - xd)*c - D0, D0 = kt - kd + log2(St'/Sd'), is formed from the
+// exact difference of the two logits (bf16 values differ exactly in fp32;
+// fp32 values close enough to cancel differ exactly too), with c and D0 each
+// carried as an fp32 pair (hi + lo), so g keeps its relative precision
+// however small it is; 1 - 2^-|g| comes from its Taylor series below 1 and
+// from the exponentials above.  Elements whose p or q reaches 2^-12 are
+// redone in fp64 with the same formula.  c is log2(e)/T to fp64 precision.
+//
+// The streaming pass's St'/Sd' is accurate to about 1e-7, and its error
+// would move every d by a multiple of e2; divided by a small residual mass
+// that would show in the draw.  The pass over the rejected pair therefore
+// also sums, per chunk, D = sum d, E2 = sum e2 and Q = sum of e2 over the
+// elements with d > 0: the exact ratio of the two rows' sums is
+// rho * St'/Sd' with rho - 1 = (sum D)/(sum E2), formed from accurately
+// computed differences, and the residual at the exact ratio is
+// max(0, d - (rho - 1) e2), whose chunk mass is Z - (rho - 1) Q to first
+// order (elements that change sign contribute at second order).
 struct ResidualRows {
-  float c, kt, kd, rstf, rsdf;
-  double rst, rsd;  // 1 / S of the target and draft rows
-  __device__ ResidualRows(float c_, float kt_, double st, float kd_, double sd)
-      : c(c_), kt(kt_), kd(kd_) {
-    rst = 1.0 / st;
-    rsd = 1.0 / sd;
-    rstf = (float)rst;
-    rsdf = (float)rsd;
+  float chi, clo, nkt, nd0hi, nd0lo, theta;
+  double c64, kt64, d0;
+  __device__ ResidualRows(float c_, float clo_, float kt_, double st, float kd_, double sd)
+      : chi(c_), clo(clo_) {
+    c64 = (double)c_ + (double)clo_;
+    kt64 = (double)kt_;
+    d0 = (double)kt_ - (double)kd_ + (log2(st) - log2(sd));
+    nkt = -kt_;
+    nd0hi = (float)(-d0);
+    nd0lo = (float)(-d0 - (double)nd0hi);
+    theta = (float)(log2(st) - 12.0);  // p or q >= 2^-12  <=>  x1 or x2 >= theta
   }
-  __device__ __forceinline__ float fast(float xt, float xd, float& big) const {
-    const float p = fast_exp2(fmaf(xt, c, -kt)) * rstf;
-    const float q = fast_exp2(fmaf(xd, c, -kd)) * rsdf;
-    big = fmaxf(p, q);
-    return fmaxf(p - q, 0.f);
+  // fp32 path: d and e2 of one element; `heavy` reports an element to redo
+  // with exact()
+  __device__ __forceinline__ float fast(float xt, float xd, float& e2, bool& heavy) const {
+    const float dx = xt - xd;
+    const float g = fmaf(dx, chi, nd0hi) + fmaf(dx, clo, nd0lo);
+    const float x1 = fmaf(xt, clo, fmaf(xt, chi, nkt));
+    const float x2 = x1 - g;
+    heavy = fmaxf(x1, x2) >= theta;
+    const float e1 = fast_exp2(x1);
+    e2 = fast_exp2(x2);
+    // 1 - 2^-|g| = 1 - e^-z, z = |g| ln 2 < 0.7: Taylor series to z^10 (the
+    // truncation is below 2e-8 relative)
+    const float ag = fabsf(g);
+    const float z = ag * 0.69314718f;
+    float t = -1.f / 3628800.f;
+    t = fmaf(t, z, 1.f / 362880.f);
+    t = fmaf(t, z, -1.f / 40320.f);
+    t = fmaf(t, z, 1.f / 5040.f);
+    t = fmaf(t, z, -1.f / 720.f);
+    t = fmaf(t, z, 1.f / 120.f);
+    t = fmaf(t, z, -1.f / 24.f);
+    t = fmaf(t, z, 1.f / 6.f);
+    t = fmaf(t, z, -0.5f);
+    t = fmaf(t, z, 1.f);
+    const float big = g >= 0.f ? e1 : e2;
+    const float ad = ag >= 1.f ? fabsf(e1 - e2) : big * (t * z);
+    const float d = g >= 0.f ? ad : -ad;
+    return g == g ? d : 0.f;  // both logits -inf: nothing on either side
   }
-  __device__ __forceinline__ double exact(float xt, float xd) const {
-    const double p = exp2_f64((double)xt * (double)c - (double)kt) * rst;
-    const double q = exp2_f64((double)xd * (double)c - (double)kd) * rsd;
-    return fmax(p - q, 0.0);
+  // fp64 path, same formula (1 - 2^-|g| from expm1, so that a small |g|
+  // keeps its relative precision against the exponentials' own error)
+  __device__ __forceinline__ double exact(float xt, float xd, double& e2) const {
+    const double x1 = (double)xt * c64 - kt64;
+    const double g = ((double)xt - (double)xd) * c64 - d0;
+    const double e1 = exp2_f64(x1);
+    e2 = exp2_f64(x1 - g);
+    const double ag = fabs(g);
+    const double ad = ag >= 1.0 ? fabs(e1 - e2) : (g >= 0.0 ? e1 : e2) * -expm1(-ag * 0.69314718055994530942);
+    const double d = g >= 0.0 ? ad : -ad;
+    return g == g ? d : 0.0;
   }
 };
 
@@ -565,37 +619,42 @@ __device__ __forceinline__ float vec_elem(const uint32_t (&w)[4], int e) {
     return __uint_as_float(x);
 }
 
-// Residual mass of U of a chunk's kUnroll vectors per lane, starting at
-// vector v0, of the rejected row pair (wave total).  Vector by vector: the
+// The residual sums of U of a chunk's kUnroll vectors per lane, starting at
+// vector v0, of the rejected row pair (wave totals).  Vector by vector: the
 // fp32 terms, then, for a vector holding an element with p or q >= 2^-12,
 // those elements again in fp64 (a rolled loop).  The empty asm statements
 // keep each vector's work in place, so that the compiler does not spread all
 // vectors' conversions over the whole pass.
 template <int DT, bool VEC, int U>
-__device__ double residual_piece_mass(const ResidualRows& rr, const char* tchunk,
-                                      const char* dchunk, int n, int v0) {
+__device__ ResidualChunk residual_piece(const ResidualRows& rr, const char* tchunk,
+                                        const char* dchunk, int n, int v0) {
   constexpr int P = Elem<DT>::kPerVec;
   TileN<DT, U> tt, td;
   tt.template load<VEC>(tchunk, n, v0);
   td.template load<VEC>(dchunk, n, v0);
-  float light = 0.f;
-  double heavy = 0.0;
+  float lz = 0.f, ld = 0.f, lq = 0.f, le = 0.f;
+  double hz = 0.0, hd = 0.0, hq = 0.0, he = 0.0;
 #pragma unroll
   for (int v = 0; v < U; ++v) {
-    float r[P];
     uint32_t hm = 0;  // this lane's heavy elements of vector v
+    float sz = 0.f, sd = 0.f, sq = 0.f, se = 0.f;
 #pragma unroll
     for (int e = 0; e < P; ++e) {
-      float big;
-      const float x = rr.fast(tt.at(v, e), td.at(v, e), big);
-      const bool h = big >= kHeavy;
+      bool h;
+      float e2;
+      const float d = rr.fast(tt.at(v, e), td.at(v, e), e2, h);
       hm |= h ? 1u << e : 0u;
-      r[e] = h ? 0.f : x;
+      const float dl = h ? 0.f : d, el = h ? 0.f : e2;
+      sz += fmaxf(dl, 0.f);
+      sd += dl;
+      sq += dl > 0.f ? el : 0.f;
+      se += el;
     }
     const bool ok = tt.valid(v);
-    float s4 = (r[0] + r[1]) + (r[2] + r[3]);
-    if constexpr (P == 8) s4 += (r[4] + r[5]) + (r[6] + r[7]);
-    light += ok ? s4 : 0.f;
+    lz += ok ? sz : 0.f;
+    ld += ok ? sd : 0.f;
+    lq += ok ? sq : 0.f;
+    le += ok ? se : 0.f;
     if (!ok) hm = 0;
     if (hm) {
       // each lane walks its own heavy elements (usually one)
@@ -604,12 +663,22 @@ __device__ double residual_piece_mass(const ResidualRows& rr, const char* tchunk
       while (hm) {
         const int e = __builtin_ctz(hm);
         hm &= hm - 1;
-        heavy += rr.exact(vec_elem<DT>(wt, e), vec_elem<DT>(wd, e));
+        double e2;
+        const double d = rr.exact(vec_elem<DT>(wt, e), vec_elem<DT>(wd, e), e2);
+        hz += fmax(d, 0.0);
+        hd += d;
+        hq += d > 0.0 ? e2 : 0.0;
+        he += e2;
       }
     }
-    asm volatile("" : "+v"(light), "+v"(heavy));
+    asm volatile("" : "+v"(lz), "+v"(ld), "+v"(lq), "+v"(le));
   }
-  return wave_sum((double)light + heavy);
+  ResidualChunk c;
+  c.z = wave_sum((double)lz + hz);
+  c.d = wave_sum((double)ld + hd);
+  c.q = wave_sum((double)lq + hq);
+  c.e2 = wave_sum((double)le + he);
+  return c;
 }
 
 // Inverse CDF over at most 64 non-negative weights, one per lane (lanes past
@@ -676,7 +745,7 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
   __shared__ RowSum s_rows[kMaxRows + 2];  // merged rows, then the rejected pair
   __shared__ Partial s_part[kStage];       // chunk summaries of the rows being merged
   __shared__ int s_a, s_bad;
-  __shared__ double s_half[kDecideWaves];
+  __shared__ ResidualChunk s_half[kDecideWaves];
   const int b = blockIdx.x / a.groups;
   const int g = blockIdx.x - b * a.groups;
   const int w = uniform((int)(threadIdx.x / kWave));
@@ -859,6 +928,7 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
       st.row = an;
       st.a = an;
       st.c = r.c;
+      st.clo = r.clo;
       st.kt = dt.k;
       st.st = dt.s;
       st.kd = dd.k;
@@ -887,17 +957,17 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
   if (soft && !(bad_all & (DSPARK_DEV_BAD_TOKEN | DSPARK_DEV_NONFINITE)) && an_all < L) {
     const int an = an_all;
     const RowSum rt = s_rows[kMaxRows], rd = s_rows[kMaxRows + 1];
-    const ResidualRows rr(r.c, rt.k, rt.s, rd.k, rd.s);
+    const ResidualRows rr(r.c, r.clo, rt.k, rt.s, rd.k, rd.s);
     constexpr int kPart = kUnroll / kWavesPerChunk;  // vectors per wave
     const int cl = w % kChunksPerGroup, part = w / kChunksPerGroup;
     const int pi = g * kChunksPerGroup + cl;
-    double z = 0.0;
+    ResidualChunk z{0.0, 0.0, 0.0, 0.0};
     if (pi < a.G) {
       const int e0 = pi * E;
       const int n = min(E, a.V - e0);
-      z = residual_piece_mass<DT, VEC, kPart>(rr, target_row(a, b, an, S) + (size_t)e0 * S,
-                                              draft_row(a, b, an, S) + (size_t)e0 * S, n,
-                                              part * kPart);
+      z = residual_piece<DT, VEC, kPart>(rr, target_row(a, b, an, S) + (size_t)e0 * S,
+                                         draft_row(a, b, an, S) + (size_t)e0 * S, n,
+                                         part * kPart);
     }
     if (kWavesPerChunk == 1) {
       if (pi < a.G && l == 0) a.part2[(size_t)b * a.G + pi] = z;
@@ -905,8 +975,14 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
       if (l == 0) s_half[w] = z;
       __syncthreads();
       if (part == 0 && pi < a.G && l == 0) {
-        double t = 0.0;
-        for (int h = 0; h < kWavesPerChunk; ++h) t += s_half[w + h * kChunksPerGroup];
+        ResidualChunk t{0.0, 0.0, 0.0, 0.0};
+        for (int h = 0; h < kWavesPerChunk; ++h) {
+          const ResidualChunk& o = s_half[w + h * kChunksPerGroup];
+          t.z += o.z;
+          t.d += o.d;
+          t.q += o.q;
+          t.e2 += o.e2;
+        }
         a.part2[(size_t)b * a.G + pi] = t;
       }
     }
@@ -1106,41 +1182,79 @@ __global__ void __launch_bounds__(kBlock) k_draw(VerifyArgs a) {
   const int K = a.K;
   const int l = lane_id();
   // requested together: the draw state, the final uniform and this
-  // request's residual chunk masses (used only after a rejection)
+  // request's residual chunk sums (used only after a rejection)
   const ReqState st = a.req[b];
   const double u = (double)a.uniforms[(size_t)b * (K + 1) + K];
-  const double* z = a.part2 + (size_t)b * a.G;
-  double zl = l < a.G ? z[l] : 0.0;
-  asm volatile("" : "+v"(zl));
+  const ResidualChunk* zc = a.part2 + (size_t)b * a.G;
+  ResidualChunk zl = l < a.G ? zc[l] : ResidualChunk{0.0, 0.0, 0.0, 0.0};
+  asm volatile("" : "+v"(zl.z), "+v"(zl.d), "+v"(zl.q), "+v"(zl.e2));
   if (st.mode != kModeResidual && st.mode != kModeBonus) return;
   int t = 0;
   bool from_p = st.mode == kModeBonus;
   if (!from_p) {
-    const Located loc = a.G <= kWave ? wave_locate(zl, u)
-                                     : block_locate([&](int ci) -> double { return z[ci]; },
-                                                    a.G, u, sh);
+    // rho - 1: the correction of the streaming pass's ratio of the two rows'
+    // sums (see ResidualRows), from the signed differences of every chunk
+    double sd_ = 0.0, se_ = 0.0;
+    if (a.G <= kWave) {
+      sd_ = wave_sum(zl.d);
+      se_ = wave_sum(zl.e2);
+    } else {
+      double pd = 0.0, pe = 0.0;
+      for (int ci = threadIdx.x; ci < a.G; ci += kBlock) {
+        pd += zc[ci].d;
+        pe += zc[ci].e2;
+      }
+      pd = wave_sum(pd);
+      pe = wave_sum(pe);
+      if (l == 0) {
+        sh.w[threadIdx.x / kWave] = pd;
+        sh.i[threadIdx.x / kWave] = 0;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kWavesPerBlock; ++k) sd_ += sh.w[k];
+      __syncthreads();
+      if (l == 0) sh.w[threadIdx.x / kWave] = pe;
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kWavesPerBlock; ++k) se_ += sh.w[k];
+      __syncthreads();
+    }
+    const double rm1 = se_ > 0.0 ? sd_ / se_ : 0.0;
+    auto corrected = [&](const ResidualChunk& c) -> double {
+      return fmax(c.z - rm1 * c.q, 0.0);
+    };
+    const Located loc = a.G <= kWave ? wave_locate(l < a.G ? corrected(zl) : 0.0, u)
+                                     : block_locate([&](int ci) -> double {
+                                         return corrected(zc[ci]);
+                                       }, a.G, u, sh);
     if (!(loc.total > 0.0) || loc.idx < 0) {
       from_p = true;  // no residual mass: draw from p at the rejected position
     } else {
-      const ResidualRows rr(st.c, st.kt, st.st, st.kd, st.sd);
+      const ResidualRows rr(st.c, st.clo, st.kt, st.st, st.kd, st.sd);
       const int e0 = loc.idx * E;
       const int n = min(E, a.V - e0);
       LaneRun<DT, NV> rt, rd;
       rt.template load<VEC>(target_row(a, b, st.row, S) + (size_t)e0 * S, n, threadIdx.x);
       rd.template load<VEC>(draft_row(a, b, st.row, S) + (size_t)e0 * S, n, threadIdx.x);
-      // fp32 masses, then the heavy elements redone in fp64 by a rolled loop
+      // the residual at the corrected ratio, max(0, d - (rho - 1) e2): fp32
+      // terms, then the heavy elements redone in fp64 by a rolled loop
       double m[R];
       uint32_t heavy = 0;
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        float big;
-        m[i] = (double)rr.fast(rt.at(i), rd.at(i), big);
-        if (big >= kHeavy) heavy |= 1u << i;
+        bool h;
+        float e2;
+        const float d = rr.fast(rt.at(i), rd.at(i), e2, h);
+        m[i] = fmax((double)d - rm1 * (double)e2, 0.0);
+        if (h) heavy |= 1u << i;
       }
       while (heavy) {
         const int i = __builtin_ctz(heavy);
         heavy &= heavy - 1;
-        const double ex = rr.exact(run_elem<DT, NV>(rt.w, i), run_elem<DT, NV>(rd.w, i));
+        double e2;
+        const double d = rr.exact(run_elem<DT, NV>(rt.w, i), run_elem<DT, NV>(rd.w, i), e2);
+        const double ex = fmax(d - rm1 * e2, 0.0);
 #pragma unroll
         for (int j = 0; j < R; ++j)
           if (j == i) m[j] = ex;
