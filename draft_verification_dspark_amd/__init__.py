@@ -45,7 +45,9 @@ EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_schedule",
            "dspark_schedule_load_aware", "dspark_calibrate", "dspark_calib_state_bytes",
            "dspark_calib_observe", "dspark_markov_draft", "dspark_verify", "dspark_verify_greedy",
            "dspark_schedule_verify", "dspark_verify_phase", "dspark_verify_greedy_phase",
-           "dspark_schedule_verify_phase")
+           "dspark_schedule_verify_phase", "dspark_schedule_verify_noalloc")
+ERR_SCRATCH = 8
+SCRATCH_BYTES = 16 << 20
 
 
 class DsparkError(RuntimeError):
@@ -99,6 +101,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dspark_verify_greedy_phase.restype = i32
     lib.dspark_schedule_verify_phase.argtypes = [i32] + lib.dspark_schedule_verify.argtypes
     lib.dspark_schedule_verify_phase.restype = i32
+    lib.dspark_schedule_verify_noalloc.argtypes = lib.dspark_schedule_verify.argtypes[:-3] + [vp]
+    lib.dspark_schedule_verify_noalloc.restype = i32
     _lib = lib
     return lib
 
@@ -419,6 +423,44 @@ def schedule_verify(conf, threshold: float, budget: int, min_len: int, target, d
         _check(lib.dspark_schedule_verify(*args))
     else:
         _check(lib.dspark_schedule_verify_phase(int(phases), *args))
+    return dict(lengths=lengths, mask=mask, survival=survival, accepted=accepted, tokens=tokens,
+                p_tok=p_tok, q_tok=q_tok, dev_status=dev_status)
+
+
+def schedule_verify_noalloc(conf, threshold: float, budget: int, min_len: int, target, draft,
+                            drafted, temperature, uniforms, *, lengths=None, mask=None,
+                            survival=None, accepted=None, tokens=None, p_tok=None, q_tok=None,
+                            dev_status=None, stream=None):
+    """dspark_schedule_verify_noalloc on torch tensors: the same step with the
+    library's built-in device scratch instead of a workspace (outputs left to
+    None are allocated here; pass them all for a call that allocates
+    nothing).  Returns dict(lengths, mask, survival, accepted, tokens, p_tok,
+    q_tok, dev_status)."""
+    torch = _torch()
+    lib = load_library()
+    dev = target.device
+    B, K1, V = target.shape
+    K = K1 - 1
+    code = _dtype_code(target)
+    _req(conf, "conf", torch.float32, (B, K), dev)
+    _req(target, "target", target.dtype, (B, K + 1, V), dev)
+    _req(draft, "draft", target.dtype, (B, K, V), dev)
+    _req(drafted, "drafted", torch.int32, (B, K), dev)
+    _req(temperature, "temperature", torch.float32, (B,), dev)
+    _req(uniforms, "uniforms", torch.float32, (B, K + 1), dev)
+    lengths = _out(lengths, "lengths", torch.int32, (B,), dev)
+    mask = _out(mask, "mask", torch.uint8, (B, K), dev)
+    survival = _out(survival, "survival", torch.float32, (B, K), dev)
+    accepted = _out(accepted, "accepted", torch.int32, (B,), dev)
+    tokens = _out(tokens, "tokens", torch.int32, (B, K + 1), dev)
+    p_tok = _out(p_tok, "p_tok", torch.float32, (B, K), dev)
+    q_tok = _out(q_tok, "q_tok", torch.float32, (B, K), dev)
+    dev_status = _status(dev_status, dev)
+    _check(lib.dspark_schedule_verify_noalloc(
+        _ptr(conf), float(threshold), int(budget), int(min_len), _ptr(lengths), _ptr(mask),
+        _ptr(survival), _ptr(target), _ptr(draft), code, B, K, V, _ptr(drafted),
+        _ptr(temperature), _ptr(uniforms), _ptr(accepted), _ptr(tokens), _ptr(p_tok),
+        _ptr(q_tok), _ptr(dev_status), _stream(stream, dev)))
     return dict(lengths=lengths, mask=mask, survival=survival, accepted=accepted, tokens=tokens,
                 p_tok=p_tok, q_tok=q_tok, dev_status=dev_status)
 

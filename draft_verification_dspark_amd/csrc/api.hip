@@ -2,6 +2,8 @@
 // kernel launches on the caller's stream.  No allocation, no synchronisation.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "args.hpp"
 #include "schedule_args.hpp"
 #include "calib_args.hpp"
@@ -102,6 +104,9 @@ const char* dspark_status_string(int status) {
     case DSPARK_ERR_WORKSPACE: return "workspace too small or misaligned";
     case DSPARK_ERR_LAUNCH: return "kernel launch failed";
     case DSPARK_ERR_PARAM: return "parameter out of range or misaligned";
+    case DSPARK_ERR_SCRATCH:
+      return "the sizes need more workspace than the library's built-in scratch "
+             "(DSPARK_SCRATCH_BYTES); use the call with a caller workspace";
     default: return "unknown status";
   }
 }
@@ -387,6 +392,49 @@ int dspark_schedule_verify_phase(int phases, const float* conf, float threshold,
   return verify_common(target_logits, draft_logits, dtype, B, K, V, drafted, lengths, temperature,
                        uniforms, accepted, tokens, p_tok, q_tok, dev_status, workspace, vbytes,
                        stream, 0, phases, false, fuse ? &sa : nullptr);
+}
+
+// The built-in scratch of dspark_schedule_verify_noalloc: one array per GPU,
+// kept until the process ends.  Host code never uses the array's name as an
+// address: the device address comes from hipGetSymbolAddress, once per
+// device (with that device current), on the first call there.
+static __device__ __align__(256) unsigned char scratch[DSPARK_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+void* g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// device address of this device's scratch, or nullptr if it cannot be had
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch[dev] = p;
+  }
+  return g_scratch[dev];
+}
+}  // namespace
+
+int dspark_schedule_verify_noalloc(const float* conf, float threshold, int budget, int min_len,
+                                   int32_t* lengths, uint8_t* mask, float* survival,
+                                   const void* target_logits, const void* draft_logits,
+                                   int dtype, int B, int K, int V, const int32_t* drafted,
+                                   const float* temperature, const float* uniforms,
+                                   int32_t* accepted, int32_t* tokens, float* p_tok,
+                                   float* q_tok, int32_t* dev_status, void* stream) {
+  const size_t need = dspark_workspace_bytes(DSPARK_OP_SCHEDULE_VERIFY, B, K, V);
+  if (need == 0) return DSPARK_ERR_SHAPE;
+  if (need > (size_t)DSPARK_SCRATCH_BYTES) return DSPARK_ERR_SCRATCH;
+  void* ws = scratch_ptr();
+  if (!ws) return DSPARK_ERR_LAUNCH;
+  return dspark_schedule_verify_phase(kPhaseAll, conf, threshold, budget, min_len, lengths, mask,
+                                      survival, target_logits, draft_logits, dtype, B, K, V,
+                                      drafted, temperature, uniforms, accepted, tokens, p_tok,
+                                      q_tok, dev_status, ws, DSPARK_SCRATCH_BYTES, stream);
 }
 
 int dspark_schedule_verify(const float* conf, float threshold, int budget, int min_len,

@@ -84,7 +84,8 @@ typedef enum {
   DSPARK_ERR_BUDGET = 4,    /* budget >= 0 but < B*min_len, or min_len not in [0,K] */
   DSPARK_ERR_WORKSPACE = 5, /* ws_bytes too small or workspace misaligned         */
   DSPARK_ERR_LAUNCH = 6,    /* the HIP runtime rejected a launch                  */
-  DSPARK_ERR_PARAM = 7      /* a parameter out of range or misaligned (per call)  */
+  DSPARK_ERR_PARAM = 7,     /* a parameter out of range or misaligned (per call)  */
+  DSPARK_ERR_SCRATCH = 8    /* sizes beyond the built-in scratch (no-alloc call)  */
 } dspark_status;
 
 typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
@@ -429,6 +430,38 @@ DSPARK_API int dspark_schedule_verify_phase(int phases, const float* conf, float
                                             int32_t* accepted, int32_t* tokens, float* p_tok,
                                             float* q_tok, int32_t* dev_status, void* workspace,
                                             size_t ws_bytes, void* stream);
+
+/*
+ * dspark_schedule_verify_noalloc — dspark_schedule_verify for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation. It takes no workspace; its
+ * kernels use the library's built-in scratch instead, a device array of
+ * DSPARK_SCRATCH_BYTES (16 MiB) per GPU, held from the first call on that
+ * GPU until the process ends. It allocates and frees nothing.
+ *
+ * Computes exactly what dspark_schedule_verify computes (the same kernels),
+ * with the same arguments apart from the workspace.
+ *   Sizes: dspark_workspace_bytes(DSPARK_OP_SCHEDULE_VERIFY, B, K, V) must
+ *   not exceed DSPARK_SCRATCH_BYTES (for V = 151,936: B up to 387 at K = 16,
+ *   up to 695 at K = 8), else DSPARK_ERR_SCRATCH before any launch.
+ *   Every call on one GPU shares that GPU's scratch, and the scratch keeps
+ *   what the last call left (nothing in it needs to start at zero): calls
+ *   that overlap on one GPU (different streams, or different host threads
+ *   without ordering) race and must not be issued.
+ * Errors: those of dspark_schedule_verify except the workspace ones;
+ * DSPARK_ERR_SCRATCH for sizes beyond the scratch; DSPARK_ERR_LAUNCH if the
+ * scratch's device address cannot be obtained.
+ */
+#define DSPARK_SCRATCH_BYTES (16u << 20)
+
+DSPARK_API int dspark_schedule_verify_noalloc(const float* conf, float threshold, int budget,
+                                              int min_len, int32_t* lengths, uint8_t* mask,
+                                              float* survival, const void* target_logits,
+                                              const void* draft_logits, int dtype, int B, int K,
+                                              int V, const int32_t* drafted,
+                                              const float* temperature, const float* uniforms,
+                                              int32_t* accepted, int32_t* tokens, float* p_tok,
+                                              float* q_tok, int32_t* dev_status, void* stream);
 
 #ifdef __cplusplus
 }

@@ -319,3 +319,17 @@ def test_schedule_verify_workspace_is_both_layouts():
         s = w(ds.OP_SCHEDULE, B, K, 1)
         assert w(ds.OP_SCHEDULE_VERIFY, B, K, V) == (v + 255) // 256 * 256 + s
     assert w(ds.OP_SCHEDULE_VERIFY, 1, 65, 10) == 0
+
+
+def test_noalloc_size_checks_come_first():
+    # no-alloc call: sizes are checked before the scratch's address is
+    # looked up (no GPU call), and sizes past the 16 MiB scratch are refused
+    lib = ds.load_library()
+    args = lambda B, K, V: (P, 0.3, -1, 1, P, None, None, P, P, 1, B, K, V, P, P, P, P, P, None,
+                            None, P, None)
+    assert lib.dspark_schedule_verify_noalloc(*args(1024, 8, 151936)) == 8
+    assert lib.dspark_schedule_verify_noalloc(*args(0, 8, 151936)) == 2
+    assert lib.dspark_schedule_verify_noalloc(*args(4, 65, 100)) == 2
+    assert ds.dspark_workspace_bytes(ds.OP_SCHEDULE_VERIFY, 387, 16, 151936) <= ds.SCRATCH_BYTES
+    assert ds.dspark_workspace_bytes(ds.OP_SCHEDULE_VERIFY, 388, 16, 151936) > ds.SCRATCH_BYTES
+    assert "scratch" in ds.dspark_status_string(8)
