@@ -20,17 +20,19 @@ constexpr int kMaxK = 64;
 size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct VerifyLayout {
-  size_t req, part1, part2, total;
+  size_t sync, part1, part2, total;
 };
 
+// The sync block (two 128-byte lines per request) first, then the chunk
+// summaries and the residual quarter sums.
 VerifyLayout verify_layout(int B, int K, int V) {
   VerifyLayout L;
   if (B > kLaunchBatch) B = kLaunchBatch;  // sub-batches reuse the workspace
   const size_t G = (size_t)chunks_per_row_max(V);
   size_t off = 0;
-  L.req = off;   off += up(sizeof(ReqState) * (size_t)B);
+  L.sync = off;  off += up(sync_bytes(B));
   L.part1 = off; off += up(sizeof(Partial) * (size_t)B * (K + 1) * 2 * G);
-  L.part2 = off; off += up(sizeof(ResidualChunk) * (size_t)B * G);
+  L.part2 = off; off += up(sizeof(ResidualChunk) * (size_t)B * 4 * G);
   L.total = off;
   return L;
 }
@@ -208,13 +210,14 @@ static int verify_common(const void* target, const void* draft, int dtype, int B
   a.p_tok = greedy_only ? nullptr : p_tok;
   a.q_tok = greedy_only ? nullptr : q_tok;
   a.dev_status = dev_status;
-  a.req = reinterpret_cast<ReqState*>(ws + L.req);
+  a.sync = ws + L.sync;
   a.part1 = reinterpret_cast<Partial*>(ws + L.part1);
   a.part2 = reinterpret_cast<ResidualChunk*>(ws + L.part2);
   a.K = K;
   a.V = V;
   const int per_vec = dtype == DSPARK_BF16 ? 8 : 4;
   a.G = dtype == DSPARK_BF16 ? chunks_per_row<DSPARK_BF16>(V) : chunks_per_row<DSPARK_F32>(V);
+  a.QT = 4 * a.G;
   a.greedy_only = greedy_only;
   a.vec_ok = (V % per_vec == 0) && aligned(target, 16) && (greedy_only || aligned(draft, 16));
   if (dry) return DSPARK_OK;  // arguments checked, nothing launched

@@ -20,11 +20,11 @@ struct VerifyArgs {
   float* p_tok;
   float* q_tok;
   int32_t* dev_status;
-  ReqState* req;       // [B]
+  char* sync;          // sync block: start counter, per request a tag line and a counter line
   Partial* part1;      // [B*(K+1)*2*G] chunk summaries, (request, row j, side) major
-  ResidualChunk* part2;  // [B*G] residual sums per chunk of the rejected row pair
+  ResidualChunk* part2;  // [B*QT] residual sums per quarter chunk of the rejected row pair
   int B, K, V, G;
-  int groups;          // k_decide workgroups per request
+  int QT;              // quarter tasks per request: 4 per chunk
   int greedy_only;
   int vec_ok;
 };
@@ -45,6 +45,12 @@ int compute_units();  // of the current device
 // a per-request plan of this many entries in LDS); larger batches run as
 // consecutive sub-batches on the same stream.
 constexpr int kLaunchBatch = 2048;
+
+// The sync block at the start of a verify workspace (k_finish): two 128-byte
+// lines per request of a launch (tag and draw state, done counter).  The
+// streaming pass clears the tags, so the block needs no initialisation.
+constexpr int kSyncLine = 128;
+inline size_t sync_bytes(int B) { return (size_t)2 * B * kSyncLine; }
 
 // Largest batch whose schedule the fused schedule + verify call works out
 // inside the streaming pass (one request per thread of a streaming

@@ -62,34 +62,30 @@ struct alignas(8) RowSum {
   int pad;
 };
 
-// Per-chunk sums of the rejected row pair (k_decide to k_draw): with d(v)
-// the difference of the target and the rescaled draft term of token v and
-// e2(v) that draft term, z = sum max(0, d), d = sum d, q = sum of e2 where
-// d > 0, e2 = sum e2.
+// Per-quarter-chunk sums of the rejected row pair (residual tasks to the
+// draw): with d(v) the difference of the target and the rescaled draft term
+// of token v and e2(v) that draft term, z = sum max(0, d), d = sum d, q = sum
+// of e2 where d > 0 (e2 unused, padding).
 struct alignas(16) ResidualChunk {
   double z, d, q, e2;
 };
 
-// Per-request state handed from k_decide to k_draw.
-enum : int { kModeNone = 0, kModeResidual = 1, kModeBonus = 2 };
+// Per-request draw state of a rejected request, published by its decision
+// for the residual tasks and the draw (8-byte words).
+enum : int { kModeNone = 0, kModeResidual = 1 };
 enum : int { kKindSoftmax = 0, kKindGreedy = 1, kKindSkip = 2 };
 
-struct alignas(16) ReqState {
-  int mode;     // k_draw draws the correction (residual) or bonus token
-  int row;      // target row of the draw (rejected position, or L)
+struct alignas(8) ReqState {
+  int mode;     // kModeResidual
+  int row;      // the rejected position's row (target and draft)
   int a;        // accepted count (column of the drawn token)
   float c;      // log2(e) / T as fp32
   float clo;    // log2(e) / T - c
   float kt;     // shift of the target row
   float kd;     // shift of the draft row
+  int pad;
   double st;    // sum of 2^(x*c - kt) over the target row
   double sd;    // same for the draft row
-  // bonus draws located in advance: the chunk holding u * total (-1 = not
-  // located), whether rounding left no crossing, and the masses
-  int cstar;
-  int past_end;
-  double base;  // mass of the chunks before cstar
-  double total; // mass of the row (sum of its chunk masses)
 };
 
 // ---------------------------------------------------------------- wave ops

@@ -12,8 +12,7 @@
 // (DSpark Deep Dive, "GPU-Resident Scheduling": maximum-length buffers,
 // variable lengths by masking).
 //
-// Three launches on the caller's stream, shapes fixed by (B, K, V); kernel
-// boundaries are the only cross-workgroup synchronisation:
+// Two launches on the caller's stream, shapes fixed by (B, K, V):
 //   k_stream_rows  the streaming pass, one workgroup per compute unit.  Each
 //                  workgroup lays out the scheduled rows of all requests
 //                  (target rows 0..L, draft rows 0..L-1, or target rows only
@@ -26,21 +25,22 @@
 //                  fp64 accumulation), or (max, lowest index).  For the
 //                  schedule + verify call it first works out the schedule
 //                  itself (every workgroup, from the confidences, while its
-//                  first tile loads are in flight).
-//   k_decide       `groups` workgroups per request: each merges the request's
-//                  row summaries (shifts align by exact powers of two), and
-//                  wave 0 forms p(y), q(y), alpha, the accept ballot and the
-//                  first rejection; workgroup 0 writes the outputs and the
-//                  draw state (after its other work); on a rejection every
-//                  wave sums the residual mass of one 4096-token chunk of the
-//                  rejected row pair (fp32, elements with normalised mass
-//                  >= 2^-12 in fp64).
-//   k_draw         one workgroup per request with a pending draw: the bonus
-//                  token (from the pass-1 chunk sums of target row L) or the
-//                  correction token (from the residual chunk masses); a block
-//                  scan locates the chunk holding the draw, the chunk is
-//                  re-read with each thread owning a contiguous run of
-//                  tokens, and a second block scan finds the token.
+//                  first tile loads are in flight).  It also clears the
+//                  requests' tags in the sync block for the next launch.
+//   k_finish       persistent, one workgroup per compute unit.  Phase 1: a
+//                  workgroup per request merges the row summaries (shifts
+//                  align by exact powers of two), and wave 0 forms p(y),
+//                  q(y), alpha, the accept ballot and the first rejection,
+//                  writes the outputs and publishes the draw state.  Phase 2:
+//                  the residual max(0, p - q) of every rejected row pair,
+//                  split into quarter chunks over all waves of the grid (fp32
+//                  with the difference carried exactly, elements with
+//                  normalised mass >= 2^-12 in fp64); the wave that completes
+//                  a request draws its correction token.  Bonus tokens (full
+//                  acceptance) are drawn by the deciding workgroup's wave 0.
+//                  Draws locate the chunk (or quarter) holding the target
+//                  mass, re-read it with each lane owning a contiguous run of
+//                  tokens, and scan the crossing lane's run a token per lane.
 #include <hip/hip_runtime.h>
 
 #include "args.hpp"
@@ -294,7 +294,7 @@ __device__ __forceinline__ TileRef decode_tile(const VerifyArgs& a, const int* s
 
 // Summary of one tile into its slot.  Every lane stores the same 16 bytes
 // (no lane-0 branch), keeping the memory operations of the loop identical on
-// all paths; status bits travel in the record and are reported by k_decide.
+// all paths; status bits travel in the record and are reported by k_finish.
 template <int DT>
 __device__ __forceinline__ void summarise_tile(const Tile<DT>& t, const TileRef& ref, int kind,
                                                float c) {
@@ -324,6 +324,25 @@ __device__ __forceinline__ void summarise_tile(const Tile<DT>& t, const TileRef&
 // Workgroup g writes the schedule's outputs (lengths, mask, survival,
 // status) of the requests b with b % n == g, which the later launches read;
 // one workgroup writing them all would start streaming last.
+// Sync block of the workspace, per request b: line 2b holds the tag (8 bytes)
+// and the ReqState (at byte 16), line 2b + 1 the done counter.  The
+// streaming pass clears every tag; the finish kernel sets a request's tag
+// once its ReqState is written, so a tag seen set during a finish launch was
+// set by that launch.  Tag bits: 0 set, 1 a residual to draw, 8 and up the
+// rejected row (which row pair the residual tasks read).
+__device__ __forceinline__ uint64_t make_tag(int mode, int row) {
+  return 1ull | ((uint64_t)(mode == kModeResidual) << 1) | ((uint64_t)(uint32_t)row << 8);
+}
+__device__ __forceinline__ uint64_t* sync_tag(const VerifyArgs& a, int b) {
+  return reinterpret_cast<uint64_t*>(a.sync + (size_t)(2 * b) * kSyncLine);
+}
+__device__ __forceinline__ ReqState* sync_state(const VerifyArgs& a, int b) {
+  return reinterpret_cast<ReqState*>(a.sync + (size_t)(2 * b) * kSyncLine + 16);
+}
+__device__ __forceinline__ uint64_t* sync_done(const VerifyArgs& a, int b) {
+  return reinterpret_cast<uint64_t*>(a.sync + (size_t)(2 * b + 1) * kSyncLine);
+}
+
 template <int DT, bool VEC, bool FUSED>
 __global__ void __launch_bounds__(kStreamBlock) k_stream_rows(VerifyArgs a, ScheduleArgs s) {
   extern __shared__ int plan[];
@@ -334,6 +353,8 @@ __global__ void __launch_bounds__(kStreamBlock) k_stream_rows(VerifyArgs a, Sche
   const int n = gridDim.x, g = blockIdx.x;
   const int w = uniform((int)(threadIdx.x / kWave));
   auto tile_of = [&](int k) { return g + n * k; };
+  for (int b = g * kStreamBlock + (int)threadIdx.x; b < a.B; b += n * kStreamBlock)
+    *sync_tag(a, b) = 0;
   // Two tile buffers: the next tile's loads are in flight while the current
   // one is summarised.  The prefetch is issued unconditionally (past the end
   // of the range a wave re-reads its current tile, a cache hit, and drops
@@ -521,20 +542,23 @@ __device__ RowSum merge_argmax16(const Partial* p, int G, int sub) {
 // fp32 values close enough to cancel differ exactly too), with c and D0 each
 // carried as an fp32 pair (hi + lo), so g keeps its relative precision
 // however small it is; 1 - 2^-|g| comes from its Taylor series below 1 and
-// from the exponentials above.  Elements whose p or q reaches 2^-12 are
-// redone in fp64 with the same formula.  c is log2(e)/T to fp64 precision.
+// from the exponentials above.  Elements whose p or q reaches 2^-12, and
+// elements with a -inf logit on either side, are redone in fp64 with the
+// same formula.  c is log2(e)/T to fp64 precision.
 //
 // The streaming pass's St'/Sd' is accurate to about 1e-7, and its error
 // would move every d by a multiple of e2; divided by a small residual mass
 // that would show in the draw.  The pass over the rejected pair therefore
-// also sums, per chunk, D = sum d, E2 = sum e2 and Q = sum of e2 over the
-// elements with d > 0: the exact ratio of the two rows' sums is
-// rho * St'/Sd' with rho - 1 = (sum D)/(sum E2), formed from accurately
-// computed differences, and the residual at the exact ratio is
+// also sums, per chunk, D = sum d and Q = sum of e2 over the elements with
+// d > 0: the exact ratio of the two rows' sums is rho * St'/Sd' with
+// rho - 1 = (sum D)/(sum e2), formed from accurately computed differences
+// (sum e2 is St' to within the ~1e-7 of the ratio itself, which changes
+// rho - 1 only at second order), and the residual at the exact ratio is
 // max(0, d - (rho - 1) e2), whose chunk mass is Z - (rho - 1) Q to first
 // order (elements that change sign contribute at second order).
 struct ResidualRows {
-  float chi, clo, nkt, nd0hi, nd0lo, theta;
+  float chi, clo, nkt, nd0hi, nd0lo;
+  uint32_t hbits;  // bits of St' 2^-12: p or q >= 2^-12  <=>  e1 or e2 >= it
   double c64, kt64, d0;
   __device__ ResidualRows(float c_, float clo_, float kt_, double st, float kd_, double sd)
       : chi(c_), clo(clo_) {
@@ -544,48 +568,60 @@ struct ResidualRows {
     nkt = -kt_;
     nd0hi = (float)(-d0);
     nd0lo = (float)(-d0 - (double)nd0hi);
-    theta = (float)(log2(st) - 12.0);  // p or q >= 2^-12  <=>  x1 or x2 >= theta
+    hbits = __float_as_uint((float)(st * 0x1p-12));
   }
   // fp32 path: d and e2 of one element; `heavy` reports an element to redo
-  // with exact()
+  // with exact(): p or q at least 2^-12, or an undefined exponential (a
+  // logit of -inf on either side makes x*chi + x*clo or x1 - g an inf - inf;
+  // the one such case left defined, a -inf draft logit with clo > 0, gives
+  // e2 = 0 and the right d = e1).  d and e2 of a heavy element are not used.
   __device__ __forceinline__ float fast(float xt, float xd, float& e2, bool& heavy) const {
     const float dx = xt - xd;
     const float g = fmaf(dx, chi, nd0hi) + fmaf(dx, clo, nd0lo);
     const float x1 = fmaf(xt, clo, fmaf(xt, chi, nkt));
     const float x2 = x1 - g;
-    heavy = fmaxf(x1, x2) >= theta;
     const float e1 = fast_exp2(x1);
     e2 = fast_exp2(x2);
-    // 1 - 2^-|g| = 1 - e^-z, z = |g| ln 2 < 0.7: Taylor series to z^10 (the
-    // truncation is below 2e-8 relative)
+    // e1, e2 are >= 0 or NaN: as unsigned bit patterns they order as numbers,
+    // with every NaN (of either sign) above +inf, so one unsigned max and min
+    // give the larger and smaller value and the heavy test together
+    const uint32_t b1 = __float_as_uint(e1), b2 = __float_as_uint(e2);
+    const uint32_t bb = b1 > b2 ? b1 : b2, bs = b1 > b2 ? b2 : b1;
+    heavy = bb >= hbits;
+    const float big = __uint_as_float(bb), small = __uint_as_float(bs);
+    // 1 - 2^-|g| = z f(z), z = |g| ln 2 < 0.7, f(z) = (1 - e^-z)/z: a degree-5
+    // polynomial with fp32 coefficients fitted to f on [0, ln 2] for least
+    // maximum relative error (1.1e-8, below fp32 rounding)
     const float ag = fabsf(g);
     const float z = ag * 0.69314718f;
-    float t = -1.f / 3628800.f;
-    t = fmaf(t, z, 1.f / 362880.f);
-    t = fmaf(t, z, -1.f / 40320.f);
-    t = fmaf(t, z, 1.f / 5040.f);
-    t = fmaf(t, z, -1.f / 720.f);
-    t = fmaf(t, z, 1.f / 120.f);
-    t = fmaf(t, z, -1.f / 24.f);
-    t = fmaf(t, z, 1.f / 6.f);
-    t = fmaf(t, z, -0.5f);
+    float t = -1.038787537e-3f;
+    t = fmaf(t, z, 8.078070357e-3f);
+    t = fmaf(t, z, -4.157954454e-2f);
+    t = fmaf(t, z, 1.666534841e-1f);
+    t = fmaf(t, z, -4.999993443e-1f);
     t = fmaf(t, z, 1.f);
-    const float big = g >= 0.f ? e1 : e2;
-    const float ad = ag >= 1.f ? fabsf(e1 - e2) : big * (t * z);
-    const float d = g >= 0.f ? ad : -ad;
-    return g == g ? d : 0.f;  // both logits -inf: nothing on either side
+    float series = big * (z * t);
+    // both sides computed: a select, not a branch (the lanes of a wave take
+    // both sides anyway)
+    asm volatile("" : "+v"(series));
+    const float ad = ag >= 1.f ? big - small : series;
+    return copysignf(ad, g);
   }
   // fp64 path, same formula (1 - 2^-|g| from expm1, so that a small |g|
-  // keeps its relative precision against the exponentials' own error)
+  // keeps its relative precision against the exponentials' own error).
+  // x2 = xd c - kt + d0 is formed from the draft logit itself, so that a
+  // -inf logit on either side gives a zero exponential and d = e1 - e2
+  // (an infinite or undefined g takes that branch).
   __device__ __forceinline__ double exact(float xt, float xd, double& e2) const {
     const double x1 = (double)xt * c64 - kt64;
+    const double x2 = (double)xd * c64 - (kt64 - d0);
     const double g = ((double)xt - (double)xd) * c64 - d0;
     const double e1 = exp2_f64(x1);
-    e2 = exp2_f64(x1 - g);
+    e2 = exp2_f64(x2);
     const double ag = fabs(g);
-    const double ad = ag >= 1.0 ? fabs(e1 - e2) : (g >= 0.0 ? e1 : e2) * -expm1(-ag * 0.69314718055994530942);
-    const double d = g >= 0.0 ? ad : -ad;
-    return g == g ? d : 0.0;
+    if (!(ag < 1.0)) return e1 - e2;
+    const double ad = (g >= 0.0 ? e1 : e2) * -expm1(-ag * 0.69314718055994530942);
+    return g >= 0.0 ? ad : -ad;
   }
 };
 
@@ -608,6 +644,30 @@ __device__ __forceinline__ float run_elem(const uint32_t (&w)[NV][4], int i) {
     return __uint_as_float(x);
 }
 
+// Token i = lane of lane h's run (the raw words broadcast from lane h, h
+// wave-uniform), for the first NV * kPerVec lanes; -inf on the others.  Lets
+// the whole wave take one lane's run a token per lane.
+template <int DT, int NV>
+__device__ __forceinline__ float lane_run_elem(const LaneRun<DT, NV>& run, int h) {
+  constexpr int R = NV * Elem<DT>::kPerVec;
+  const int i = lane_id();
+  const int word = DT == DSPARK_BF16 ? (i >> 1) : i;
+  uint32_t x = 0;
+#pragma unroll
+  for (int v = 0; v < NV; ++v)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t sw = (uint32_t)__builtin_amdgcn_readlane((int)run.w[v][q], h);
+      if (word == v * 4 + q) x = sw;
+    }
+  float f;
+  if constexpr (DT == DSPARK_BF16)
+    f = (i & 1) ? __uint_as_float(x & 0xffff0000u) : __uint_as_float(x << 16);
+  else
+    f = __uint_as_float(x);
+  return i < R ? f : -INFINITY;
+}
+
 // element e of one 16-byte vector, e only known at run time
 template <int DT>
 __device__ __forceinline__ float vec_elem(const uint32_t (&w)[4], int e) {
@@ -625,39 +685,37 @@ __device__ __forceinline__ float vec_elem(const uint32_t (&w)[4], int e) {
 // those elements again in fp64 (a rolled loop).  The empty asm statements
 // keep each vector's work in place, so that the compiler does not spread all
 // vectors' conversions over the whole pass.
-template <int DT, bool VEC, int U>
-__device__ ResidualChunk residual_piece(const ResidualRows& rr, const char* tchunk,
-                                        const char* dchunk, int n, int v0) {
+template <int DT, int U>
+__device__ ResidualChunk residual_sums(const ResidualRows& rr, const TileN<DT, U>& tt,
+                                       const TileN<DT, U>& td) {
   constexpr int P = Elem<DT>::kPerVec;
-  TileN<DT, U> tt, td;
-  tt.template load<VEC>(tchunk, n, v0);
-  td.template load<VEC>(dchunk, n, v0);
-  float lz = 0.f, ld = 0.f, lq = 0.f, le = 0.f;
-  double hz = 0.0, hd = 0.0, hq = 0.0, he = 0.0;
+  float lz = 0.f, ld = 0.f, lq = 0.f;
+  double hz = 0.0, hd = 0.0, hq = 0.0;
 #pragma unroll
   for (int v = 0; v < U; ++v) {
     uint32_t hm = 0;  // this lane's heavy elements of vector v
-    float sz = 0.f, sd = 0.f, sq = 0.f, se = 0.f;
+    float sz = 0.f, sd = 0.f, sq = 0.f;
 #pragma unroll
     for (int e = 0; e < P; ++e) {
       bool h;
       float e2;
       const float d = rr.fast(tt.at(v, e), td.at(v, e), e2, h);
       hm |= h ? 1u << e : 0u;
-      const float dl = h ? 0.f : d, el = h ? 0.f : e2;
-      sz += fmaxf(dl, 0.f);
-      sd += dl;
-      sq += dl > 0.f ? el : 0.f;
-      se += el;
+      // heavy elements stay out of the fp32 sums (their value would dominate
+      // the partial sum's rounding, or is not defined) and are added in fp64
+      // below
+      const bool pos = !h && d > 0.f;
+      sz += pos ? d : 0.f;
+      sd += h ? 0.f : d;
+      sq += pos ? e2 : 0.f;
     }
     const bool ok = tt.valid(v);
     lz += ok ? sz : 0.f;
     ld += ok ? sd : 0.f;
     lq += ok ? sq : 0.f;
-    le += ok ? se : 0.f;
     if (!ok) hm = 0;
     if (hm) {
-      // each lane walks its own heavy elements (usually one)
+      // each lane walks its own heavy elements (usually one) in fp64
       const uint32_t wt[4] = {tt.w[v][0], tt.w[v][1], tt.w[v][2], tt.w[v][3]};
       const uint32_t wd[4] = {td.w[v][0], td.w[v][1], td.w[v][2], td.w[v][3]};
       while (hm) {
@@ -668,16 +726,15 @@ __device__ ResidualChunk residual_piece(const ResidualRows& rr, const char* tchu
         hz += fmax(d, 0.0);
         hd += d;
         hq += d > 0.0 ? e2 : 0.0;
-        he += e2;
       }
     }
-    asm volatile("" : "+v"(lz), "+v"(ld), "+v"(lq), "+v"(le));
+    asm volatile("" : "+v"(lz), "+v"(ld), "+v"(lq));
   }
   ResidualChunk c;
   c.z = wave_sum((double)lz + hz);
   c.d = wave_sum((double)ld + hd);
   c.q = wave_sum((double)lq + hq);
-  c.e2 = wave_sum((double)le + he);
+  c.e2 = 0.0;
   return c;
 }
 
@@ -710,52 +767,382 @@ __device__ __forceinline__ Located wave_locate(double x, double u) {
   return r;
 }
 
-// ------------------------------------------------------------------ decide
+// ------------------------------------------------------------------ finish
 
-// k_decide: `groups` workgroups of kDecideBlock threads per request.  Each
-// stages the request's chunk summaries in LDS and merges its rows (16-lane
-// groups, one row each), then wave 0 decides: p(y), q(y), alpha, the accept
-// ballot, the first rejection.  On a rejection the workgroup then sums the
-// residual mass of kChunksPerGroup chunks of the rejected row pair,
-// kWavesPerChunk waves per chunk.  Workgroup 0 finally writes the outputs and
-// the draw state.
-#ifndef DSPARK_DECIDE_BLOCK
-#define DSPARK_DECIDE_BLOCK 640
-#endif
-#ifndef DSPARK_WAVES_PER_CHUNK
-#define DSPARK_WAVES_PER_CHUNK 1
-#endif
-constexpr int kDecideBlock = DSPARK_DECIDE_BLOCK;
-constexpr int kDecideWaves = kDecideBlock / kWave;
-// waves per residual chunk (each takes an equal share of its vectors).  Ten
-// waves with one wave per chunk: a request at 151,936 tokens (38 chunks)
-// needs 4 workgroups, so a batch of 64 requests is one workgroup per compute
-// unit, all resident at once (two waves per chunk measured slower at full
-// length and no faster as scheduled)
-constexpr int kWavesPerChunk = DSPARK_WAVES_PER_CHUNK;
-constexpr int kChunksPerGroup = kDecideWaves / kWavesPerChunk;
+// k_finish: the decision, the residual and the draw of every request, in one
+// persistent launch of one workgroup per compute unit (kFinishBlock threads,
+// 8 waves), after the streaming pass.
+//   Phase 1  workgroup g decides requests g, g + n, ... (n workgroups): it
+//            stages the request's chunk summaries in LDS, merges its rows
+//            (16-lane groups, one row each), and wave 0 forms p(y), q(y),
+//            alpha, the accept ballot and the first rejection and writes the
+//            outputs.  Greedy requests are then complete; after a full
+//            acceptance wave 0 draws the bonus token itself; after a
+//            rejection it publishes the draw state (ReqState) and sets the
+//            request's tag.
+//   Phase 2  the residual of every rejected request is split into quarter
+//            chunks (4 per 4096-token chunk of the row pair); quarter task
+//            t = b * QT + q goes to wave t mod W of the grid (W waves in all),
+//            which waits for the request's tag, sums its quarter (d, D, Q;
+//            see ResidualRows) and counts itself done on the request's
+//            counter.  The wave that completes the request draws the
+//            correction token.
+// Cross-workgroup hand-over goes through the sync block of the workspace:
+// per request a tag line (tag, ReqState) and a counter line, each on its own
+// 128-byte line (atomics on a shared line serialise).  Stores that another
+// workgroup reads are agent-scope atomic stores, completed (waitcnt) before
+// the store or atomic that publishes them; readers use agent-scope atomic
+// loads issued after they saw the publication.  Waits poll with
+// s_sleep and give up after kSpinLimit ticks of the 100 MHz real-time
+// counter (DSPARK_DEV_INCOMPLETE), so every wave ends.
+// The waits need every workgroup of the launch resident at once (one per
+// compute unit, which the register and LDS use allow): a workgroup that
+// cannot start until a waiting one ends leaves its requests undecided, and
+// the waits on them end by time-out.
+constexpr int kFinishBlock = 512;
+constexpr int kFinishWaves = kFinishBlock / kWave;
 constexpr int kMaxRows = 2 * 64 + 1;
-// chunk summaries staged in LDS per round of the merges (30 KB)
-constexpr int kStage = 3 * kDecideBlock;
+// chunk summaries staged in LDS per round of the merges (24 KB)
+constexpr int kStage = 3 * kFinishBlock;
+constexpr uint64_t kSpinLimit = 100000000ull;  // 1 s at 100 MHz
+constexpr int kTaskBatch = 3;  // quarter tasks a wave has in flight at once
 
+// A full acceptance's bonus draw, deferred by wave 0 (at most kMaxPending
+// per workgroup; more are drawn at once)
+struct PendingBonus {
+  int b, L;
+  float c, kp;
+  double u;
+  Located loc;
+};
+constexpr int kMaxPending = 16;
+
+
+__device__ __forceinline__ uint64_t ld_agent(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// every earlier memory operation of this wave completed
+__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+
+// a record of 8-byte words moved with agent-scope atomic stores / loads
+template <typename T> __device__ __forceinline__ void st_rec(T* dst, const T& v) {
+  static_assert(sizeof(T) % 8 == 0, "8-byte words");
+  const uint64_t* s = reinterpret_cast<const uint64_t*>(&v);
+  uint64_t* d = reinterpret_cast<uint64_t*>(dst);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 8); ++i) st_agent(d + i, s[i]);
+}
+template <typename T> __device__ __forceinline__ T ld_rec(const T* src) {
+  T v;
+  uint64_t* d = reinterpret_cast<uint64_t*>(&v);
+  const uint64_t* s = reinterpret_cast<const uint64_t*>(src);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 8); ++i) d[i] = ld_agent(s + i);
+  return v;
+}
+
+// Wait (lane 0 polls, the wave waits) until *p == want; false on time-out.
+__device__ bool wait_tag(const uint64_t* p, uint64_t want) {
+  int ok = 1;
+  if (lane_id() == 0) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (ld_agent(p) != want) {
+      __builtin_amdgcn_s_sleep(2);
+      if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
+        ok = 0;
+        break;
+      }
+    }
+  }
+  return readlane(ok, 0) != 0;
+}
+
+// Inverse CDF over n weights f(0..n-1) by one wave, in index order, in
+// rounds of 64 (same rule as wave_locate): the index and the mass before it.
+template <typename F>
+__device__ Located wave_locate_rounds(F f, int n, double u) {
+  const int l = lane_id();
+  double part = 0.0;
+  for (int i = l; i < n; i += kWave) part += f(i);
+  const double total = wave_sum(part);
+  const double target = u * total;
+  double run = 0.0;
+  int last = -1;
+  for (int r0 = 0; r0 < n; r0 += kWave) {
+    const int i = r0 + l;
+    const double x = i < n ? f(i) : 0.0;
+    const double incl = run + wave_incl_scan(x);
+    const uint64_t hit = __ballot(incl > target && x > 0.0);
+    const uint64_t pos = __ballot(x > 0.0);
+    if (pos) last = r0 + 63 - __builtin_clzll(pos);
+    if (hit) {
+      const int h = __builtin_ctzll(hit);
+      Located r;
+      r.idx = r0 + h;
+      r.past_end = 0;
+      r.base = readlane(incl - x, h);
+      r.total = total;
+      return r;
+    }
+    run = readlane(incl, kWave - 1);
+  }
+  Located r;
+  r.idx = last;
+  r.past_end = 1;
+  r.base = total;
+  r.total = total;
+  return r;
+}
+
+// Inside runs of tokens laid out R per lane in token order (LaneRun), the
+// first token whose running mass exceeds `target`, else the last with mass,
+// else 0.  One wave: each lane sums its run, a wave scan finds the lane h
+// holding the crossing, then lane h's run is taken a token per lane and
+// scanned again.  mass(x) is the mass of a token of value x (0 for -inf).
+template <int DT, int NV, typename M>
+__device__ int wave_scan_runs(const LaneRun<DT, NV>& run, M mass, double target) {
+  constexpr int R = NV * Elem<DT>::kPerVec;
+  const int l = lane_id();
+  double ls = 0.0;
+  int lp = -1;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const double x = mass(run.at(i));
+    ls += x;
+    if (x > 0.0) lp = l * R + i;
+    // keep each group of 8 masses in place (no hoisting of every
+    // exponential ahead of the sum, which would not fit in registers)
+    if ((i & 7) == 7) asm volatile("" : "+v"(ls), "+v"(lp));
+  }
+  const double incl = wave_incl_scan(ls);
+  const int last = wave_max_i(lp);
+  const uint64_t hit = __ballot(incl > target && ls > 0.0);
+  if (!hit) return last >= 0 ? last : 0;
+  const int h = __builtin_ctzll(hit);
+  const double x = mass(lane_run_elem<DT, NV>(run, h));  // 0 past the run
+  const double sc = wave_incl_scan(x);
+  const double base = readlane(incl - ls, h);
+  const uint64_t hit2 = __ballot(base + sc > target && x > 0.0);
+  // rounding can leave no crossing inside lane h's run: its last token with mass
+  return hit2 ? h * R + __builtin_ctzll(hit2) : readlane(lp, h);
+}
+
+// Draw from the softmax of target row `row` (the bonus token, or the
+// fallback of an all-zero residual), by one wave: chunk masses from the
+// row's pass-1 summaries scaled to the merged shift kp, then the chosen
+// chunk re-read as four quarters (each lane a run of consecutive tokens of
+// each) with the pass's own fp32 arithmetic: the quarter holding the target,
+// then the token inside it.  `loc` may hold the chunk already located from
+// staged summaries.
 template <int DT, bool VEC>
-__global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
+__device__ int draw_from_row(const VerifyArgs& a, int b, int row, float c, float kp, double u,
+                             Located loc) {
   constexpr int S = Elem<DT>::kBytes;
   constexpr int E = item_elems<DT>();
-  __shared__ RowSum s_rows[kMaxRows + 2];  // merged rows, then the rejected pair
-  __shared__ Partial s_part[kStage];       // chunk summaries of the rows being merged
-  __shared__ int s_a, s_bad;
-  __shared__ ResidualChunk s_half[kDecideWaves];
-  const int b = blockIdx.x / a.groups;
-  const int g = blockIdx.x - b * a.groups;
+  constexpr int EQ = E / 4;
+  constexpr int R = EQ / kWave;
+  constexpr int NV = R / Elem<DT>::kPerVec;
+  const Partial* pr = row_parts(a, b, row, 0);
+  auto chunk_mass = [&](int ci) -> double {
+    const Partial p = pr[ci];
+    return p.s > 0.0 ? ldexp(p.s, shift_amount(p.k - kp)) : 0.0;
+  };
+  if (loc.idx < 0) loc = wave_locate_rounds(chunk_mass, a.G, u);
+  if (loc.idx < 0) return 0;
+  const int e0 = loc.idx * E;
+  const int n = min(E, a.V - e0);
+  const char* base = target_row(a, b, row, S) + (size_t)e0 * S;
+  LaneRun<DT, NV> qr[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    qr[k].template load<VEC>(base + (size_t)k * EQ * S, max(0, min(EQ, n - k * EQ)), lane_id());
+  const float kc = pr[loc.idx].k;
+  const int sh_c = shift_amount(kc - kp);
+  double qs[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    double ls = 0.0;
+#pragma unroll
+    for (int i = 0; i < R; ++i) ls += ldexp((double)fast_exp2(fmaf(qr[k].at(i), c, -kc)), sh_c);
+    qs[k] = wave_sum(ls);
+  }
+  // the quarter holding the target (else the last with mass)
+  const double target = loc.past_end ? INFINITY : u * loc.total - loc.base;
+  double before = 0.0;
+  int kq = -1, klast = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (qs[k] > 0.0) klast = k;
+    if (kq < 0 && before + qs[k] > target && qs[k] > 0.0) kq = k;
+    if (kq < 0) before += qs[k];
+  }
+  const bool past = kq < 0;
+  if (past) kq = klast;
+  LaneRun<DT, NV> run = qr[0];
+#pragma unroll
+  for (int k = 1; k < 4; ++k)
+    if (kq == k) run = qr[k];
+  return e0 + kq * EQ +
+         wave_scan_runs<DT, NV>(
+             run,
+             [&](float x) -> double { return ldexp((double)fast_exp2(fmaf(x, c, -kc)), sh_c); },
+             past ? INFINITY : target - before);
+}
+
+// Quarter records of a request held in registers, kRecLanes per lane (quarter
+// q = lane + 64 k): read in one batch of loads, so that the sums and the
+// locate below cost one memory round trip.  Requests with more quarters
+// (V above 64 k * kRecLanes / 4 * 4096 tokens) read them in rounds instead.
+constexpr int kRecLanes = 4;
+
+// The correction token of a rejected request, by one wave: quarter masses
+// corrected to the exact ratio of the row sums, the quarter holding u * Z,
+// then its 4096/4 tokens recomputed (each lane a run of consecutive tokens).
+template <int DT, bool VEC>
+__device__ int draw_residual(const VerifyArgs& a, int b, double u, int& tok_pos) {
+  constexpr int S = Elem<DT>::kBytes;
+  constexpr int E = item_elems<DT>();
+  constexpr int EQ = E / 4;          // tokens per quarter
+  constexpr int R = EQ / kWave;      // per lane
+  constexpr int NV = R / Elem<DT>::kPerVec;
+  const ResidualChunk* zq = a.part2 + (size_t)b * a.QT;
+  const int l = lane_id();
+  Located loc;
+  double rm1;
+  // the draw state, loaded with the quarter records below
+  const ReqState st = ld_rec(sync_state(a, b));
+  tok_pos = st.a;
+  if (a.QT <= kWave * kRecLanes) {
+    double z[kRecLanes], d[kRecLanes], q[kRecLanes];
+#pragma unroll
+    for (int k = 0; k < kRecLanes; ++k) {
+      const int i = l + kWave * k;
+      const uint64_t* p = reinterpret_cast<const uint64_t*>(zq + (i < a.QT ? i : 0));
+      z[k] = __longlong_as_double((long long)ld_agent(p + 0));
+      d[k] = __longlong_as_double((long long)ld_agent(p + 1));
+      q[k] = __longlong_as_double((long long)ld_agent(p + 2));
+    }
+    // rho - 1 from the signed differences over sum e2 = St' (see ResidualRows)
+    double pd = 0.0;
+#pragma unroll
+    for (int k = 0; k < kRecLanes; ++k) pd += l + kWave * k < a.QT ? d[k] : 0.0;
+    const double sd = wave_sum(pd);
+    rm1 = st.st > 0.0 ? sd / st.st : 0.0;
+    double m[kRecLanes], part = 0.0;
+#pragma unroll
+    for (int k = 0; k < kRecLanes; ++k) {
+      m[k] = l + kWave * k < a.QT ? fmax(z[k] - rm1 * q[k], 0.0) : 0.0;
+      part += m[k];
+    }
+    // inverse CDF in quarter order, as wave_locate_rounds does
+    const double total = wave_sum(part);
+    const double target = u * total;
+    double run = 0.0;
+    int last = -1;
+    loc = Located{-1, 1, total, total};
+#pragma unroll
+    for (int k = 0; k < kRecLanes; ++k) {
+      const double incl = run + wave_incl_scan(m[k]);
+      const uint64_t hit = __ballot(incl > target && m[k] > 0.0);
+      const uint64_t pos = __ballot(m[k] > 0.0);
+      if (pos) last = kWave * k + 63 - __builtin_clzll(pos);
+      if (hit && loc.past_end) {
+        const int h = __builtin_ctzll(hit);
+        loc = Located{kWave * k + h, 0, readlane(incl - m[k], h), total};
+      }
+      run = readlane(incl, kWave - 1);
+    }
+    if (loc.past_end) loc.idx = last;
+  } else {
+    auto rd = [&](int i) -> ResidualChunk { return ld_rec(zq + i); };
+    double pd = 0.0;
+    for (int i = l; i < a.QT; i += kWave) pd += rd(i).d;
+    const double sd = wave_sum(pd);
+    rm1 = st.st > 0.0 ? sd / st.st : 0.0;
+    loc = wave_locate_rounds(
+        [&](int i) -> double {
+          const ResidualChunk c = rd(i);
+          return fmax(c.z - rm1 * c.q, 0.0);
+        },
+        a.QT, u);
+  }
+  if (!(loc.total > 0.0) || loc.idx < 0)
+    return draw_from_row<DT, VEC>(a, b, st.row, st.c, st.kt, u, Located{-1, 0, 0.0, 0.0});
+  const ResidualRows rr(st.c, st.clo, st.kt, st.st, st.kd, st.sd);
+  const int e0 = loc.idx * EQ;
+  const int n = min(EQ, a.V - e0);
+  LaneRun<DT, NV> rt, rdr;
+  rt.template load<VEC>(target_row(a, b, st.row, S) + (size_t)e0 * S, n, lane_id());
+  rdr.template load<VEC>(draft_row(a, b, st.row, S) + (size_t)e0 * S, n, lane_id());
+  // the residual at the corrected ratio, max(0, d - (rho - 1) e2): the fp32
+  // form, and for an element whose p or q reaches 2^-12 the fp64 one, taken
+  // in a rolled loop over those few elements (one copy of the fp64 code)
+  auto mass = [&](float xt, float xd, bool& h) -> double {
+    float e2f;
+    const float d = rr.fast(xt, xd, e2f, h);
+    return fmax((double)d - rm1 * (double)e2f, 0.0);
+  };
+  auto exact_mass = [&](float xt, float xd) -> double {
+    double e2;
+    const double dx = rr.exact(xt, xd, e2);
+    return fmax(dx - rm1 * e2, 0.0);
+  };
+  double ls = 0.0;
+  int lp = -1;
+  uint32_t heavy = 0;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    bool h;
+    const double x = mass(rt.at(i), rdr.at(i), h);
+    heavy |= h ? 1u << i : 0u;
+    ls += h ? 0.0 : x;
+    if (!h && x > 0.0) lp = l * R + i;
+  }
+  for (uint32_t hm = heavy; hm; hm &= hm - 1) {
+    const int i = __builtin_ctz(hm);
+    const double x = exact_mass(run_elem<DT, NV>(rt.w, i), run_elem<DT, NV>(rdr.w, i));
+    ls += x;
+    if (x > 0.0) lp = max(lp, l * R + i);
+  }
+  const double target = loc.past_end ? INFINITY : u * loc.total - loc.base;
+  const double incl = wave_incl_scan(ls);
+  const int last = wave_max_i(lp);
+  const uint64_t hit = __ballot(incl > target && ls > 0.0);
+  int f = last;
+  if (hit) {
+    // lane h holds the crossing: its run a token per lane, scanned again with
+    // the same per-token arithmetic (fp64 for the heavy ones)
+    const int h = __builtin_ctzll(hit);
+    const float xt = lane_run_elem<DT, NV>(rt, h), xd = lane_run_elem<DT, NV>(rdr, h);
+    double x = 0.0;
+    if (l < R) {
+      bool hh;
+      x = mass(xt, xd, hh);
+      if (hh) x = exact_mass(xt, xd);
+    }
+    const double sc = wave_incl_scan(x);
+    const double base = readlane(incl - ls, h);
+    const uint64_t hit2 = __ballot(base + sc > target && x > 0.0);
+    // rounding can leave no crossing inside lane h's run: its last token with mass
+    f = hit2 ? h * R + __builtin_ctzll(hit2) : readlane(lp, h);
+  }
+  return e0 + (f >= 0 ? f : 0);
+}
+
+// Phase 1 for request b by the whole workgroup (every thread must call it).
+template <int DT, bool VEC>
+__device__ void decide_request(const VerifyArgs& a, int b, RowSum* s_rows, Partial* s_part,
+                               PendingBonus* s_pend, int& npend) {
+  constexpr int S = Elem<DT>::kBytes;
   const int w = uniform((int)(threadIdx.x / kWave));
   const int l = lane_id();
   const int K = a.K;
   // Requested together, before anything waits: the request's length and
   // temperature, the final uniform and, for wave 0 lane l, the drafted id
-  // and accept uniform of position l+1.  Loads whose value is used later are
-  // kept out of lane-dependent branches (lanes past K re-read column K-1),
-  // so that the compiler does not wait for them on the spot.
+  // and accept uniform of position l+1 (lanes past K re-read column K-1).
   const int lcol = min(l, K - 1);
   // (a greedy-only call has no uniforms: the drafted ids stand in, unused)
   const float* ub = a.uniforms ? a.uniforms + (size_t)b * (K + 1)
@@ -766,10 +1153,9 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
   const ReqInfo r = req_info(a, b);
   const int L = r.L;
   int32_t* tok = a.tokens + (size_t)b * (K + 1);
-  const bool lead = g == 0;  // writes the request's outputs
 
   if (r.kind == kKindSkip) {
-    if (lead && w == 0) {
+    if (w == 0) {
       for (int i = l; i <= K; i += kWave) tok[i] = -1;
       if (l < K) {
         if (a.p_tok) a.p_tok[(size_t)b * K + l] = 0.f;
@@ -777,7 +1163,6 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
       }
       if (l == 0) {
         a.accepted[b] = 0;
-        a.req[b].mode = kModeNone;
         flag(a.dev_status, r.bad);
       }
     }
@@ -787,8 +1172,7 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
 
   // The drafted tokens' logits, gathered with the first staged summaries so
   // that one round trip covers both.  Lanes past L (and bad ids) read a
-  // scheduled row at id 0 and ignore it: only target rows 0..L and draft
-  // rows 0..L-1 are touched.
+  // scheduled row at id 0 and ignore it.
   const bool in_range = y >= 0 && y < a.V;
   const int yc = in_range ? y : 0;
   const bool yok = l >= L || in_range;
@@ -809,8 +1193,6 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
   };
   int q_last = 0;  // first row of the last staged round
   if (G <= kStage) {
-    // all threads stage up to kStage summaries at once, then 16-lane groups
-    // merge one row each
     const int per_round = kStage / G;
     const int grp = threadIdx.x >> 4, sub = threadIdx.x & 15;
     for (int q0 = 0; q0 < nrows; q0 += per_round) {
@@ -818,13 +1200,11 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
       const int cnt = nr * G;
       q_last = q0;
       if (q0 > 0) __syncthreads();  // the previous round's merges are done
-      // every load first (slots past the count re-read the first summary),
-      // then every LDS store, so the loads share one round trip
-      constexpr int kPer = kStage / kDecideBlock;
+      constexpr int kPer = kStage / kFinishBlock;
       Partial tmp[kPer];
 #pragma unroll
       for (int k = 0; k < kPer; ++k) {
-        const int i = k * kDecideBlock + (int)threadIdx.x;
+        const int i = k * kFinishBlock + (int)threadIdx.x;
         const int ii = i < cnt ? i : 0;
         const int rr = ii / G;
         int side;
@@ -834,15 +1214,16 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
       xt_raw = load_raw<DT>(trow, yc);  // (re-gathered in later rounds)
       xd_raw = load_raw<DT>(drow, yc);
 #pragma unroll
-      for (int k = 0; k < kPer; ++k) asm volatile("" : "+v"(tmp[k].k), "+v"(tmp[k].idx), "+v"(tmp[k].s));
+      for (int k = 0; k < kPer; ++k)
+        asm volatile("" : "+v"(tmp[k].k), "+v"(tmp[k].idx), "+v"(tmp[k].s));
       asm volatile("" : "+v"(xt_raw), "+v"(xd_raw));
 #pragma unroll
       for (int k = 0; k < kPer; ++k) {
-        const int i = k * kDecideBlock + (int)threadIdx.x;
+        const int i = k * kFinishBlock + (int)threadIdx.x;
         if (i < cnt) s_part[i] = tmp[k];
       }
       __syncthreads();
-      for (int rr = grp; rr < nr; rr += kDecideBlock / 16) {
+      for (int rr = grp; rr < nr; rr += kFinishBlock / 16) {
         const RowSum m = soft ? merge_softmax16(s_part + rr * G, G, sub)
                               : merge_argmax16(s_part + rr * G, G, sub);
         if (sub == 0) s_rows[q0 + rr] = m;
@@ -852,7 +1233,7 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
     // very long rows: waves merge whole rows straight from global memory
     xt_raw = load_raw<DT>(trow, yc);
     xd_raw = load_raw<DT>(drow, yc);
-    for (int q = w; q < nrows; q += kDecideWaves) {
+    for (int q = w; q < nrows; q += kFinishWaves) {
       int side;
       const int j = row_of(q, side);
       const Partial* base = row_parts(a, b, j, side);
@@ -862,418 +1243,254 @@ __global__ void __launch_bounds__(kDecideBlock) k_decide(VerifyArgs a) {
     }
   }
   __syncthreads();
+  if (w != 0) return;  // wave 0 decides; the others move on
   const float xt = raw_to_float<DT>(xt_raw), xd = raw_to_float<DT>(xd_raw);
-
-  // outputs of this request (wave 0), written at the end of the kernel
-  int an = 0, bad = 0, gtok = 0;
+  const RowSum rL = s_rows[qL];  // target row L: the bonus row
+  RowSum rt{}, rd{};
+  if (l < L) {
+    rt = s_rows[l];
+    if (soft) rd = s_rows[L + l];
+  }
+  int bad = r.bad;
+  if (!yok) bad |= DSPARK_DEV_BAD_TOKEN;
+  if (l < L) bad |= rt.bad | rd.bad;
+  if (l == 0) bad |= rL.bad;
+  bool acc = false;
   float pf = 0.f, qf = 0.f;
-  ReqState st{};
-  if (w == 0) {
-    const RowSum rL = s_rows[qL];  // target row L: the bonus row
-    RowSum rt{}, rd{};
+  if (soft) {
     if (l < L) {
-      rt = s_rows[l];
-      if (soft) rd = s_rows[L + l];
-    }
-    bad = r.bad;
-    if (!yok) bad |= DSPARK_DEV_BAD_TOKEN;
-    if (l < L) bad |= rt.bad | rd.bad;
-    if (l == 0) bad |= rL.bad;
-    bool acc = false;
-    if (soft) {
-      if (l < L) {
-        if (!(rt.s > 0.0) || !(rd.s > 0.0)) bad |= DSPARK_DEV_NONFINITE;  // no finite logit
-        if (!(u >= 0.f && u < 1.f)) bad |= DSPARK_DEV_BAD_UNIFORM;
-        if (yok) {
-          const double p = row_prob(xt, r.c, rt.k, rt.s);
-          const double qv = row_prob(xd, r.c, rd.k, rd.s);
-          const double alpha = p == 0.0 ? 0.0 : (qv == 0.0 ? 1.0 : fmin(1.0, p / qv));
-          acc = (double)u < alpha;
-          pf = (float)p;
-          qf = (float)qv;
-        }
+      if (!(rt.s > 0.0) || !(rd.s > 0.0)) bad |= DSPARK_DEV_NONFINITE;  // no finite logit
+      if (!(u >= 0.f && u < 1.f)) bad |= DSPARK_DEV_BAD_UNIFORM;
+      if (yok) {
+        const double p = row_prob(xt, r.c, rt.k, rt.s);
+        const double qv = row_prob(xd, r.c, rd.k, rd.s);
+        const double alpha = p == 0.0 ? 0.0 : (qv == 0.0 ? 1.0 : fmin(1.0, p / qv));
+        acc = (double)u < alpha;
+        pf = (float)p;
+        qf = (float)qv;
       }
-      if (l == 0) {
-        if (!(rL.s > 0.0)) bad |= DSPARK_DEV_NONFINITE;
-        if (!(u_draw >= 0.f && u_draw < 1.f)) bad |= DSPARK_DEV_BAD_UNIFORM;
-      }
-    } else {
-      if (l < L && rt.k == -INFINITY) bad |= DSPARK_DEV_NONFINITE;  // no finite logit
-      if (l == 0 && rL.k == -INFINITY) bad |= DSPARK_DEV_NONFINITE;
-      acc = l < L && yok && y == rt.idx;
-    }
-    const uint64_t m = __ballot(acc);
-    const uint64_t want = L >= 64 ? ~0ull : ((1ull << L) - 1ull);
-    const uint64_t rej = ~m & want;
-    an = rej ? __builtin_ctzll(rej) : L;
-    bad = wave_or(bad);
-    if (lead) {
-      if (!soft) gtok = an < L ? readlane(rt.idx, an) : rL.idx;
-      // draw state: the target row of the draw and, on a rejection, the
-      // draft row's shift and sum as well
-      const RowSum dt = an < L ? RowSum{readlane(rt.s, an), readlane(rt.k, an), 0, 0, 0} : rL;
-      const RowSum dd = an < L ? RowSum{readlane(rd.s, an), readlane(rd.k, an), 0, 0, 0} : RowSum{};
-      // the bonus draw's chunk, located now from the staged summaries of
-      // target row L (the last row staged)
-      Located bonus{-1, 0, 0.0, 0.0};
-      const bool located = soft && an == L && G <= kWave && G <= kStage;
-      if (located) {
-        const Partial pc = l < G ? s_part[(qL - q_last) * G + l] : Partial{-INFINITY, 0, 0.0};
-        const double mass = l < G && pc.s > 0.0 ? ldexp(pc.s, shift_amount(pc.k - rL.k)) : 0.0;
-        bonus = wave_locate(mass, (double)u_draw);
-      }
-      st.mode = (!soft || (bad & (DSPARK_DEV_BAD_TOKEN | DSPARK_DEV_NONFINITE)))
-                    ? kModeNone
-                    : (an == L ? kModeBonus : kModeResidual);
-      st.row = an;
-      st.a = an;
-      st.c = r.c;
-      st.clo = r.clo;
-      st.kt = dt.k;
-      st.st = dt.s;
-      st.kd = dd.k;
-      st.sd = dd.s;
-      st.cstar = bonus.idx;
-      st.past_end = bonus.past_end;
-      st.base = bonus.base;
-      st.total = bonus.total;
-    }
-    if (an < L && an == l) {
-      s_rows[kMaxRows] = rt;  // the rejected target row
-      s_rows[kMaxRows + 1] = rd;  // and its draft row
     }
     if (l == 0) {
-      s_a = an;
-      s_bad = bad;
+      if (!(rL.s > 0.0)) bad |= DSPARK_DEV_NONFINITE;
+      if (!(u_draw >= 0.f && u_draw < 1.f)) bad |= DSPARK_DEV_BAD_UNIFORM;
     }
+  } else {
+    if (l < L && rt.k == -INFINITY) bad |= DSPARK_DEV_NONFINITE;  // no finite logit
+    if (l == 0 && rL.k == -INFINITY) bad |= DSPARK_DEV_NONFINITE;
+    acc = l < L && yok && y == rt.idx;
   }
-  __syncthreads();
-  // on a rejection (sampled, no fault) every workgroup of the request sums
-  // the residual of its chunks; greedy requests are complete, faulty ones
-  // have unspecified outputs, and after a full acceptance k_draw draws the
-  // bonus token from the pass-1 sums
-  const int an_all = s_a;
-  const int bad_all = s_bad;
-  if (soft && !(bad_all & (DSPARK_DEV_BAD_TOKEN | DSPARK_DEV_NONFINITE)) && an_all < L) {
-    const int an = an_all;
-    const RowSum rt = s_rows[kMaxRows], rd = s_rows[kMaxRows + 1];
-    const ResidualRows rr(r.c, r.clo, rt.k, rt.s, rd.k, rd.s);
-    constexpr int kPart = kUnroll / kWavesPerChunk;  // vectors per wave
-    const int cl = w % kChunksPerGroup, part = w / kChunksPerGroup;
-    const int pi = g * kChunksPerGroup + cl;
-    ResidualChunk z{0.0, 0.0, 0.0, 0.0};
-    if (pi < a.G) {
-      const int e0 = pi * E;
-      const int n = min(E, a.V - e0);
-      z = residual_piece<DT, VEC, kPart>(rr, target_row(a, b, an, S) + (size_t)e0 * S,
-                                         draft_row(a, b, an, S) + (size_t)e0 * S, n,
-                                         part * kPart);
+  const uint64_t m = __ballot(acc);
+  const uint64_t want = L >= 64 ? ~0ull : ((1ull << L) - 1ull);
+  const uint64_t rej = ~m & want;
+  const int an = rej ? __builtin_ctzll(rej) : L;
+  bad = wave_or(bad);
+  const bool fault = (bad & (DSPARK_DEV_BAD_TOKEN | DSPARK_DEV_NONFINITE)) != 0;
+  int gtok = 0;
+  if (!soft) gtok = an < L ? readlane(rt.idx, an) : rL.idx;
+  // outputs: the accepted prefix, p(y) and q(y), and (greedy) the last token
+  if (l < K) {
+    if (a.p_tok) a.p_tok[(size_t)b * K + l] = pf;
+    if (a.q_tok) a.q_tok[(size_t)b * K + l] = qf;
+  }
+  for (int i = l; i <= K; i += kWave) {
+    if (i < an) tok[i] = y;  // lane i holds the drafted id of position i+1
+    else if (i > an || !soft) tok[i] = i == an ? gtok : -1;
+  }
+  if (l == 0) {
+    a.accepted[b] = an;
+    if (bad) flag(a.dev_status, bad);
+  }
+  if (!soft) return;  // greedy done
+  // the draw state for the residual tasks, which wait for every sampled
+  // request with L > 0: kModeNone releases them when there is no residual
+  // (a full acceptance, or a faulty request, whose tokens are unspecified)
+  ReqState st{};
+  st.mode = kModeNone;
+  if (!fault && an < L) {
+    st.mode = kModeResidual;
+    st.row = an;
+    st.a = an;
+    st.c = r.c;
+    st.clo = r.clo;
+    st.kt = readlane(rt.k, an);
+    st.st = readlane(rt.s, an);
+    st.kd = readlane(rd.k, an);
+    st.sd = readlane(rd.s, an);
+  }
+  if (l == 0) {
+    st_rec(sync_state(a, b), st);
+    st_agent(sync_done(a, b), 0ull);
+    wait_all();
+    st_agent(sync_tag(a, b), make_tag(st.mode, st.row));
+  }
+  if (fault) return;
+  if (an == L) {
+    // full acceptance: the bonus token from target row L, its chunk located
+    // from the staged summaries when they are all there
+    Located bonus{-1, 0, 0.0, 0.0};
+    if (G <= kWave && G <= kStage) {
+      const Partial pc = l < G ? s_part[(qL - q_last) * G + l] : Partial{-INFINITY, 0, 0.0};
+      const double mass = l < G && pc.s > 0.0 ? ldexp(pc.s, shift_amount(pc.k - rL.k)) : 0.0;
+      bonus = wave_locate(mass, (double)u_draw);
     }
-    if (kWavesPerChunk == 1) {
-      if (pi < a.G && l == 0) a.part2[(size_t)b * a.G + pi] = z;
-    } else {
-      if (l == 0) s_half[w] = z;
-      __syncthreads();
-      if (part == 0 && pi < a.G && l == 0) {
-        ResidualChunk t{0.0, 0.0, 0.0, 0.0};
-        for (int h = 0; h < kWavesPerChunk; ++h) {
-          const ResidualChunk& o = s_half[w + h * kChunksPerGroup];
-          t.z += o.z;
-          t.d += o.d;
-          t.q += o.q;
-          t.e2 += o.e2;
+    if (npend < kMaxPending) {
+      // drawn after this wave's residual tasks (the draw's memory round trips
+      // would otherwise hold the whole workgroup back from them)
+      if (l == 0) s_pend[npend] = PendingBonus{b, L, r.c, rL.k, (double)u_draw, bonus};
+      ++npend;
+      return;
+    }
+    const int t = draw_from_row<DT, VEC>(a, b, L, r.c, rL.k, (double)u_draw, bonus);
+    if (l == 0) tok[L] = t;
+  }
+}
+
+// The requests with a residual to draw, by one wave: every sampled request
+// with L > 0 has its tag set in phase 1 (lane l polls request b0 + l, 64 at
+// a time, bounded by kSpinLimit); those whose tag says residual go to s_live
+// in request order as (request | row << 16).  A tag not set in time flags
+// DSPARK_DEV_INCOMPLETE in `bad` and leaves the request out.
+__device__ int live_requests(const VerifyArgs& a, int* s_live, int& bad) {
+  int nlive = 0;
+  for (int b0 = 0; b0 < a.B; b0 += kWave) {
+    const int b = b0 + lane_id();
+    bool want = false;
+    if (b < a.B) {
+      const ReqInfo r = req_info(a, b);
+      want = r.kind == kKindSoftmax && r.L > 0;
+    }
+    uint64_t tag = 0;
+    int ok = 1;
+    if (want) {
+      const uint64_t* p = sync_tag(a, b);
+      const uint64_t ts = __builtin_amdgcn_s_memrealtime();
+      while (!((tag = ld_agent(p)) & 1ull)) {
+        __builtin_amdgcn_s_sleep(2);
+        if (__builtin_amdgcn_s_memrealtime() - ts > kSpinLimit) {
+          ok = 0;
+          break;
         }
-        a.part2[(size_t)b * a.G + pi] = t;
       }
     }
+    if (!ok) bad |= DSPARK_DEV_INCOMPLETE;
+    const bool live = want && ok && ((tag >> 1) & 1ull);
+    const uint64_t m = __ballot(live);
+    const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+    if (live) s_live[nlive + below] = b | ((int)(tag >> 8) << 16);
+    nlive += __builtin_popcountll(m);
   }
-  // the lead workgroup writes the request's outputs last, so that none of its
-  // stores holds up the residual work above
-  if (lead && w == 0) {
-    if (l < K) {
-      if (a.p_tok) a.p_tok[(size_t)b * K + l] = pf;
-      if (a.q_tok) a.q_tok[(size_t)b * K + l] = qf;
-    }
-    for (int i = l; i <= K; i += kWave) {
-      if (i < an) tok[i] = y;  // lane i holds the drafted id of position i+1
-      else if (i > an || !soft) tok[i] = i == an ? gtok : -1;
-    }
-    if (l == 0) {
-      a.accepted[b] = an;
-      if (bad) flag(a.dev_status, bad);
-      a.req[b] = st;
-    }
-  }
+  return nlive;
 }
 
-// ------------------------------------------------------------------ draw
-
-struct DrawShared {
-  double w[kWavesPerBlock];
-  int i[kWavesPerBlock];
-  double base, total;
-  int idx, past_end, found;
-};
-
-// Inverse CDF over n > 64 weights f(0..n-1) for the whole block, in index
-// order (same rule as wave_locate), in rounds of kBlock weights.  Every
-// thread must call it.
-template <typename F>
-__device__ Located block_locate(F f, int n, double u, DrawShared& sh) {
-  const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
-  double part = 0.0;
-  for (int i = tid; i < n; i += kBlock) part += f(i);
-  const double pw = wave_sum(part);
-  if (l == 0) sh.w[w] = pw;
-  __syncthreads();
-  double total = 0.0;
-#pragma unroll
-  for (int k = 0; k < kWavesPerBlock; ++k) total += sh.w[k];
-  __syncthreads();
-  const double target = u * total;
-  double run = 0.0;
-  int last = -1;
-  for (int r0 = 0; r0 < n; r0 += kBlock) {
-    const int i = r0 + tid;
-    const double x = i < n ? f(i) : 0.0;
-    const double incl_w = wave_incl_scan(x);
-    const int lpw = wave_max_i(x > 0.0 ? i : -1);
-    if (l == kWave - 1) {
-      sh.w[w] = incl_w;
-      sh.i[w] = lpw;
-    }
-    __syncthreads();
-    double pre = run, cum = run;
-    int ws = -1;
-#pragma unroll
-    for (int k = 0; k < kWavesPerBlock; ++k) {
-      const double t = sh.w[k];
-      if (k < w) pre += t;
-      cum += t;
-      if (ws < 0 && cum > target && t > 0.0) ws = k;
-      last = max(last, sh.i[k]);
-    }
-    if (w == ws) {
-      const double incl = pre + incl_w;
-      const uint64_t hit = __ballot(incl > target && x > 0.0);
-      const int hl = hit ? __builtin_ctzll(hit) : 0;
-      const double before = readlane(incl - x, hl);
-      if (l == 0) {
-        sh.idx = hit ? r0 + w * kWave + hl : lpw;
-        sh.base = hit ? before : cum;
-      }
-    }
-    __syncthreads();
-    if (ws >= 0) {
-      Located r;
-      r.idx = sh.idx;
-      r.past_end = 0;
-      r.base = sh.base;
-      r.total = total;
-      return r;
-    }
-    run = cum;
-  }
-  Located r;
-  r.idx = last;
-  r.past_end = 1;
-  r.base = total;
-  r.total = total;
-  return r;
-}
-
-// Inside one chunk whose elements are split into contiguous runs of R per
-// thread (masses m), the first element whose running mass exceeds `target`,
-// else the last element with mass, else 0.  Two barriers: wave totals, then
-// the crossing thread's answer.
-template <int R>
-__device__ int block_scan_run(const double (&m)[R], double target, DrawShared& sh) {
-  const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
-  double ls = 0.0;
-  int lp = -1;
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    ls += m[i];
-    if (m[i] > 0.0) lp = tid * R + i;
-  }
-  const double incl_w = wave_incl_scan(ls);
-  const int lpw = wave_max_i(lp);
-  if (l == kWave - 1) {
-    sh.w[w] = incl_w;
-    sh.i[w] = lpw;
-  }
-  __syncthreads();
-  double pre = 0.0, cum = 0.0;
-  int ws = -1, last = -1;
-#pragma unroll
-  for (int i = 0; i < kWavesPerBlock; ++i) {
-    const double t = sh.w[i];
-    if (i < w) pre += t;
-    cum += t;
-    if (ws < 0 && cum > target && t > 0.0) ws = i;
-    last = max(last, sh.i[i]);
-  }
-  if (w == ws) {
-    const double incl = pre + incl_w;
-    const uint64_t hit = __ballot(incl > target && ls > 0.0);
-    if (!hit) {
-      if (l == 0) sh.found = lpw;  // rounding left no crossing lane
-    } else if (l == __builtin_ctzll(hit)) {
-      double run = incl - ls;
-      int f = -1;
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        run += m[i];
-        if (f < 0 && run > target && m[i] > 0.0) f = tid * R + i;
-      }
-      sh.found = f >= 0 ? f : lp;
-    }
-  }
-  __syncthreads();
-  const int f = ws >= 0 ? sh.found : last;
-  return f >= 0 ? f : 0;
-}
-
-// Draw from the softmax of target row `row` (bonus token, or the fallback of
-// an all-zero residual): chunk masses come from the row's pass-1 summaries
-// scaled to the merged shift kp (the chunk may already be located); the
-// chosen chunk is recomputed with the same fp32 arithmetic as pass 1.
 template <int DT, bool VEC>
-__device__ int draw_from_p(const VerifyArgs& a, int b, int row, float c, float kp, double u,
-                           Located loc, DrawShared& sh) {
+__global__ void __launch_bounds__(kFinishBlock) k_finish(VerifyArgs a) {
   constexpr int S = Elem<DT>::kBytes;
   constexpr int E = item_elems<DT>();
-  constexpr int R = E / kBlock;
-  constexpr int NV = R / Elem<DT>::kPerVec;
-  const Partial* pr = row_parts(a, b, row, 0);
-  auto chunk_mass = [&](int ci) -> double {
-    const Partial p = pr[ci];
-    return p.s > 0.0 ? ldexp(p.s, shift_amount(p.k - kp)) : 0.0;
-  };
-  if (loc.idx < 0) {
-    if (a.G <= kWave)
-      loc = wave_locate(lane_id() < a.G ? chunk_mass(lane_id()) : 0.0, u);
-    else
-      loc = block_locate(chunk_mass, a.G, u, sh);
-  }
-  if (loc.idx < 0) return 0;
-  const int e0 = loc.idx * E;
-  const int n = min(E, a.V - e0);
-  LaneRun<DT, NV> run;
-  run.template load<VEC>(target_row(a, b, row, S) + (size_t)e0 * S, n, threadIdx.x);
-  const float kc = pr[loc.idx].k;
-  const int sh_c = shift_amount(kc - kp);
-  double m[R];
-#pragma unroll
-  for (int i = 0; i < R; ++i) m[i] = ldexp((double)fast_exp2(fmaf(run.at(i), c, -kc)), sh_c);
-  const int f = block_scan_run<R>(m, loc.past_end ? INFINITY : u * loc.total - loc.base, sh);
-  return e0 + f;
-}
-
-// k_draw: one workgroup per request with a pending draw.
-template <int DT, bool VEC>
-__global__ void __launch_bounds__(kBlock) k_draw(VerifyArgs a) {
-  constexpr int S = Elem<DT>::kBytes;
-  constexpr int E = item_elems<DT>();
-  constexpr int R = E / kBlock;
-  constexpr int NV = R / Elem<DT>::kPerVec;
-  __shared__ DrawShared sh;
-  const int b = blockIdx.x;
-  const int K = a.K;
+  constexpr int EQ = E / 4;
+  constexpr int UQ = kUnroll / 4;  // vectors per lane in a quarter task
+  __shared__ RowSum s_rows[kMaxRows];
+  __shared__ Partial s_part[kStage];
+  __shared__ int s_nlive;
+  __shared__ PendingBonus s_pend[kMaxPending];
+  const int n = gridDim.x, g = blockIdx.x;
+  const int w = uniform((int)(threadIdx.x / kWave));
   const int l = lane_id();
-  // requested together: the draw state, the final uniform and this
-  // request's residual chunk sums (used only after a rejection)
-  const ReqState st = a.req[b];
-  const double u = (double)a.uniforms[(size_t)b * (K + 1) + K];
-  const ResidualChunk* zc = a.part2 + (size_t)b * a.G;
-  ResidualChunk zl = l < a.G ? zc[l] : ResidualChunk{0.0, 0.0, 0.0, 0.0};
-  asm volatile("" : "+v"(zl.z), "+v"(zl.d), "+v"(zl.q), "+v"(zl.e2));
-  if (st.mode != kModeResidual && st.mode != kModeBonus) return;
-  int t = 0;
-  bool from_p = st.mode == kModeBonus;
-  if (!from_p) {
-    // rho - 1: the correction of the streaming pass's ratio of the two rows'
-    // sums (see ResidualRows), from the signed differences of every chunk
-    double sd_ = 0.0, se_ = 0.0;
-    if (a.G <= kWave) {
-      sd_ = wave_sum(zl.d);
-      se_ = wave_sum(zl.e2);
-    } else {
-      double pd = 0.0, pe = 0.0;
-      for (int ci = threadIdx.x; ci < a.G; ci += kBlock) {
-        pd += zc[ci].d;
-        pe += zc[ci].e2;
-      }
-      pd = wave_sum(pd);
-      pe = wave_sum(pe);
-      if (l == 0) {
-        sh.w[threadIdx.x / kWave] = pd;
-        sh.i[threadIdx.x / kWave] = 0;
-      }
-      __syncthreads();
+  // Phase 1: this workgroup's decisions
+  int npend = 0;  // wave 0's deferred bonus draws
+  for (int b = g; b < a.B; b += n) {
+    decide_request<DT, VEC>(a, b, s_rows, s_part, s_pend, npend);
+    __syncthreads();  // LDS reused by the next request
+  }
+  if (a.greedy_only) return;  // (no bonus draws: greedy requests take the argmax)
+  // Phase 2.  Wave 0 lists the requests that have a residual (from their
+  // tags) in LDS; their quarter tasks, t = live * QT + quarter, go to the
+  // grid's waves kTaskBatch consecutive tasks at a time (batch k = tasks
+  // kTaskBatch k ..., to wave k mod W), so that one batch spans at most two
+  // requests and a slow wave holds back few draws.  A batch has its row
+  // tiles and draw states all in flight before the sums, stores its
+  // records, waits once, and counts itself done.
+  int* s_live = reinterpret_cast<int*>(s_part);  // free after phase 1
+  if (w == 0) {
+    int badl = 0;
+    const int nl = live_requests(a, s_live, badl);
+    if (badl) flag(a.dev_status, badl);
+    if (l == 0) s_nlive = nl;
+  }
+  __syncthreads();
+  const int W = n * kFinishWaves;
+  const int gw = w * n + g;  // neighbouring tasks on different compute units
+  const long long ntask = (long long)s_nlive * a.QT;
+  for (long long t0 = (long long)gw * kTaskBatch; t0 < ntask; t0 += (long long)kTaskBatch * W) {
+    int tb[kTaskBatch], tq[kTaskBatch], trow[kTaskBatch];
+    bool live[kTaskBatch];
 #pragma unroll
-      for (int k = 0; k < kWavesPerBlock; ++k) sd_ += sh.w[k];
-      __syncthreads();
-      if (l == 0) sh.w[threadIdx.x / kWave] = pe;
-      __syncthreads();
-#pragma unroll
-      for (int k = 0; k < kWavesPerBlock; ++k) se_ += sh.w[k];
-      __syncthreads();
+    for (int j = 0; j < kTaskBatch; ++j) {
+      const long long t = t0 + j;
+      live[j] = t < ntask;
+      const int li = live[j] ? (int)(t / a.QT) : 0;
+      tq[j] = live[j] ? (int)(t - (long long)li * a.QT) : 0;
+      const int e = s_live[li];
+      tb[j] = e & 0xffff;
+      trow[j] = e >> 16;
     }
-    const double rm1 = se_ > 0.0 ? sd_ / se_ : 0.0;
-    auto corrected = [&](const ResidualChunk& c) -> double {
-      return fmax(c.z - rm1 * c.q, 0.0);
-    };
-    const Located loc = a.G <= kWave ? wave_locate(l < a.G ? corrected(zl) : 0.0, u)
-                                     : block_locate([&](int ci) -> double {
-                                         return corrected(zc[ci]);
-                                       }, a.G, u, sh);
-    if (!(loc.total > 0.0) || loc.idx < 0) {
-      from_p = true;  // no residual mass: draw from p at the rejected position
-    } else {
-      const ResidualRows rr(st.c, st.clo, st.kt, st.st, st.kd, st.sd);
-      const int e0 = loc.idx * E;
-      const int n = min(E, a.V - e0);
-      LaneRun<DT, NV> rt, rd;
-      rt.template load<VEC>(target_row(a, b, st.row, S) + (size_t)e0 * S, n, threadIdx.x);
-      rd.template load<VEC>(draft_row(a, b, st.row, S) + (size_t)e0 * S, n, threadIdx.x);
-      // the residual at the corrected ratio, max(0, d - (rho - 1) e2): fp32
-      // terms, then the heavy elements redone in fp64 by a rolled loop
-      double m[R];
-      uint32_t heavy = 0;
+    TileN<DT, UQ> tt[kTaskBatch], td[kTaskBatch];
+    ReqState sj[kTaskBatch];
 #pragma unroll
-      for (int i = 0; i < R; ++i) {
-        bool h;
-        float e2;
-        const float d = rr.fast(rt.at(i), rd.at(i), e2, h);
-        m[i] = fmax((double)d - rm1 * (double)e2, 0.0);
-        if (h) heavy |= 1u << i;
-      }
-      while (heavy) {
-        const int i = __builtin_ctz(heavy);
-        heavy &= heavy - 1;
-        double e2;
-        const double d = rr.exact(run_elem<DT, NV>(rt.w, i), run_elem<DT, NV>(rd.w, i), e2);
-        const double ex = fmax(d - rm1 * e2, 0.0);
+    for (int j = 0; j < kTaskBatch; ++j) {
+      if (!live[j]) continue;
+      const int e0 = (tq[j] >> 2) * E;
+      const int nn = min(E, a.V - e0);
+      const int v0 = (tq[j] & 3) * UQ;
+      tt[j].template load<VEC>(target_row(a, tb[j], trow[j], S) + (size_t)e0 * S, nn, v0);
+      td[j].template load<VEC>(draft_row(a, tb[j], trow[j], S) + (size_t)e0 * S, nn, v0);
+      sj[j] = ld_rec(sync_state(a, tb[j]));
+    }
+    ResidualChunk zj[kTaskBatch];
 #pragma unroll
-        for (int j = 0; j < R; ++j)
-          if (j == i) m[j] = ex;
-      }
-      const int f = block_scan_run<R>(m, loc.past_end ? INFINITY : u * loc.total - loc.base, sh);
-      t = e0 + f;
+    for (int j = 0; j < kTaskBatch; ++j) {
+      if (!live[j]) continue;
+      const ResidualRows rr(sj[j].c, sj[j].clo, sj[j].kt, sj[j].st, sj[j].kd, sj[j].sd);
+      zj[j] = residual_sums<DT, UQ>(rr, tt[j], td[j]);
+    }
+    int last[kTaskBatch];
+#pragma unroll
+    for (int j = 0; j < kTaskBatch; ++j) last[j] = 0;
+    if (l == 0) {
+#pragma unroll
+      for (int j = 0; j < kTaskBatch; ++j)
+        if (live[j]) st_rec(a.part2 + (size_t)tb[j] * a.QT + tq[j], zj[j]);
+      wait_all();
+#pragma unroll
+      for (int j = 0; j < kTaskBatch; ++j)
+        if (live[j]) {
+          const uint64_t old = __hip_atomic_fetch_add(sync_done(a, tb[j]), 1ull,
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          last[j] = old + 1 == (uint64_t)a.QT;
+        }
+    }
+    // the requests this wave completed: their correction tokens
+    int done_mask = 0;
+#pragma unroll
+    for (int j = 0; j < kTaskBatch; ++j)
+      if (live[j] && readlane(last[j], 0)) done_mask |= 1 << j;
+    for (int j = 0; j < kTaskBatch; ++j) {
+      if (!((done_mask >> j) & 1)) continue;
+      const int b = readlane(tb[j], 0);
+      const double u = (double)a.uniforms[(size_t)b * (a.K + 1) + a.K];
+      int pos;
+      const int tk = draw_residual<DT, VEC>(a, b, u, pos);
+      if (l == 0) a.tokens[(size_t)b * (a.K + 1) + pos] = tk;
     }
   }
-  if (from_p) {
-    Located loc{-1, 0, 0.0, 0.0};
-    if (st.mode == kModeBonus && st.cstar >= 0) {
-      loc.idx = st.cstar;
-      loc.past_end = st.past_end;
-      loc.base = st.base;
-      loc.total = st.total;
+  // wave 0's deferred bonus draws, after its residual tasks
+  if (w == 0)
+    for (int i = 0; i < npend; ++i) {
+      const PendingBonus pb = s_pend[i];
+      const int t = draw_from_row<DT, VEC>(a, pb.b, pb.L, pb.c, pb.kp, pb.u, pb.loc);
+      if (l == 0) a.tokens[(size_t)pb.b * (a.K + 1) + pb.L] = t;
     }
-    t = draw_from_p<DT, VEC>(a, b, st.row, st.c, st.kt, u, loc, sh);
-  }
-  if (threadIdx.x == 0) a.tokens[(size_t)b * (K + 1) + st.a] = t;
+  (void)EQ;
 }
 
 // ------------------------------------------------------------------ launch
@@ -1290,13 +1507,8 @@ static int launch_verify_t(VerifyArgs& a, hipStream_t st, int phases, const Sche
       hipLaunchKernelGGL((k_stream_rows<DT, VEC, false>), dim3((unsigned)grid),
                          dim3(kStreamBlock), lds, st, a, ScheduleArgs{});
   }
-  if (phases & kPhaseFinish) {
-    a.groups = (a.G + kChunksPerGroup - 1) / kChunksPerGroup;
-    hipLaunchKernelGGL((k_decide<DT, VEC>), dim3((unsigned)((long)a.B * a.groups)),
-                       dim3(kDecideBlock), 0, st, a);
-    if (!a.greedy_only)
-      hipLaunchKernelGGL((k_draw<DT, VEC>), dim3((unsigned)a.B), dim3(kBlock), 0, st, a);
-  }
+  if (phases & kPhaseFinish)
+    hipLaunchKernelGGL((k_finish<DT, VEC>), dim3((unsigned)grid), dim3(kFinishBlock), 0, st, a);
   return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_ERR_LAUNCH;
 }
 

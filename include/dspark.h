@@ -99,6 +99,7 @@ typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
 #define DSPARK_DEV_BAD_LENGTH 32  /* lengths[b] outside [0, K] (clamped)                 */
 #define DSPARK_DEV_BAD_LOAD 64    /* queue depth or memory in use NaN, infinite or < 0    */
 #define DSPARK_DEV_BAD_CURVE 128  /* throughput curve breaks the rules of dspark_schedule_load_aware */
+#define DSPARK_DEV_INCOMPLETE 256 /* a verify launch gave up waiting for another workgroup (1 s): outputs unspecified */
 
 #define DSPARK_OP_SCHEDULE 0
 #define DSPARK_OP_VERIFY 1
@@ -442,8 +443,8 @@ DSPARK_API int dspark_schedule_verify_phase(int phases, const float* conf, float
  * Computes exactly what dspark_schedule_verify computes (the same kernels),
  * with the same arguments apart from the workspace.
  *   Sizes: dspark_workspace_bytes(DSPARK_OP_SCHEDULE_VERIFY, B, K, V) must
- *   not exceed DSPARK_SCRATCH_BYTES (for V = 151,936: B up to 387 at K = 16,
- *   up to 695 at K = 8), else DSPARK_ERR_SCRATCH before any launch.
+ *   not exceed DSPARK_SCRATCH_BYTES (for V = 151,936: B up to 330 at K = 16,
+ *   up to 532 at K = 8), else DSPARK_ERR_SCRATCH before any launch.
  *   Every call on one GPU shares that GPU's scratch, and the scratch keeps
  *   what the last call left (nothing in it needs to start at zero): calls
  *   that overlap on one GPU (different streams, or different host threads

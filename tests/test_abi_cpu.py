@@ -330,6 +330,6 @@ def test_noalloc_size_checks_come_first():
     assert lib.dspark_schedule_verify_noalloc(*args(1024, 8, 151936)) == 8
     assert lib.dspark_schedule_verify_noalloc(*args(0, 8, 151936)) == 2
     assert lib.dspark_schedule_verify_noalloc(*args(4, 65, 100)) == 2
-    assert ds.dspark_workspace_bytes(ds.OP_SCHEDULE_VERIFY, 387, 16, 151936) <= ds.SCRATCH_BYTES
-    assert ds.dspark_workspace_bytes(ds.OP_SCHEDULE_VERIFY, 388, 16, 151936) > ds.SCRATCH_BYTES
+    assert ds.dspark_workspace_bytes(ds.OP_SCHEDULE_VERIFY, 330, 16, 151936) <= ds.SCRATCH_BYTES
+    assert ds.dspark_workspace_bytes(ds.OP_SCHEDULE_VERIFY, 331, 16, 151936) > ds.SCRATCH_BYTES
     assert "scratch" in ds.dspark_status_string(8)

@@ -237,6 +237,51 @@ def test_large_and_masked_logits():
     _verify_and_compare(tgt2, dft2, drafted2, L, temp, u)
 
 
+def _temps_with_both_lo_signs(n):
+    """n temperatures in [0.3, 1.6], half of them with log2(e)/T above its
+    nearest fp32 value and half below: the kernels carry log2(e)/T as an fp32
+    pair (hi + lo), and a -inf logit times a lo of either sign must stay
+    -inf."""
+    pos, neg = [], []
+    for T in np.linspace(0.3, 1.6, 4001).astype(np.float32):
+        c = np.log2(np.e) / float(T)
+        lo = c - float(np.float32(c))
+        (pos if lo > 0 else neg if lo < 0 else []).append(float(T))
+    h = n // 2
+    return [pos[(2 * i + 1) * len(pos) // (2 * h)] for i in range(h)] + \
+           [neg[(2 * i + 1) * len(neg) // (2 * (n - h))] for i in range(n - h)]
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 9000), ("bf16", 9001), ("f32", 9000),
+                                     ("f32", 9001), ("f32", 1001)])
+def test_one_sided_masks(dtype, V):
+    # target logits -inf where the draft's are finite (the draft proposes
+    # tokens the target rules out) and the reverse, on rejected rows at
+    # temperatures of both lo signs, full rows and ragged tails
+    B, K = 8, 4
+    g = torch.Generator(device=DEV)
+    g.manual_seed(V + (dtype == "f32"))
+    tgt = 3.0 * torch.randn((B, K + 1, V), generator=g, device=DEV)
+    dft = tgt[:, :K] + 1.5 * torch.randn((B, K, V), generator=g, device=DEV)
+    ids = torch.arange(V, device=DEV)
+    tgt = torch.where(ids % 5 == 0, -float("inf"), tgt)   # target rules these out
+    dft = torch.where(ids % 7 == 1, -float("inf"), dft)   # the draft never proposes these
+    st = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tgt, dft = tgt.to(st).contiguous(), dft.to(st).contiguous()
+    temp = torch.tensor(_temps_with_both_lo_signs(B), device=DEV)
+    probs = torch.softmax(dft.float() / temp.view(B, 1, 1), -1)
+    drafted = torch.multinomial(probs.view(B * K, V), 1, generator=g).view(B, K).int().contiguous()
+    L = torch.full((B,), K, dtype=torch.int32, device=DEV)
+    u = torch.rand((B, K + 1), generator=g, device=DEV).contiguous()
+    out, ref = _verify_and_compare(tgt, dft, drafted, L, temp, u)
+    # most requests end in a correction drawn from the residual, and it never
+    # lands on a token the target rules out
+    rejected = out["accepted"] < K
+    assert rejected.sum() >= B // 2
+    for b in np.nonzero(rejected)[0]:
+        assert out["tokens"][b, out["accepted"][b]] % 5 != 0
+
+
 def test_mixed_greedy_and_sampled_requests():
     B, K, V = 40, 8, 32000
     tgt, dft, drafted, L, temp, u = _rand_case(B, K, V, "bf16", seed=23)
