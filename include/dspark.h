@@ -400,9 +400,10 @@ DSPARK_API int dspark_schedule_verify(const float* conf, float threshold, int bu
  *           workspace;
  *           both bits: the whole call.
  *   other arguments: as for the call without the suffix.
- * The FINISH half must follow the STREAM half on the same stream, with the
- * same arguments and workspace, and nothing that writes the workspace in
- * between. A split call (phases other than both bits) needs
+ * The FINISH half must follow the STREAM half on the same stream, once, with
+ * the same arguments and workspace, and nothing that writes the workspace in
+ * between (the STREAM half also resets the hand-over state the FINISH half
+ * uses). A split call (phases other than both bits) needs
  * B <= 2048 (the workspace holds one launch batch); larger batches return
  * DSPARK_ERR_SHAPE. phases outside 1..3 returns DSPARK_ERR_PARAM.
  */
