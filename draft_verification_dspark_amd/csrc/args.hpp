@@ -56,7 +56,7 @@ inline size_t sync_bytes(int B) { return (size_t)2 * B * kSyncLine; }
 // inside the streaming pass (one request per thread of a streaming
 // workgroup, at most 16 positions per request, every position's key in
 // LDS); larger batches launch the schedule on its own first.
-constexpr int kFusedMaxB = 768;
+constexpr int kFusedMaxB = 512;
 constexpr int kFusedMaxK = 16;  // a thread's confidences are loaded in one round trip
 constexpr int kFusedMaxPositions = 12288;
 

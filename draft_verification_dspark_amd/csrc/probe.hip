@@ -3,7 +3,7 @@
 // benchmark's own library (libdspark_bench.so), not into libdspark.so:
 // nothing on the verification path calls it.
 //
-// One workgroup of 768 threads per compute unit, as the streaming pass.  Wave
+// One workgroup of 512 threads per compute unit, as the streaming pass.  Wave
 // w of the grid reads 8 KB tiles w, w + W, w + 2W, ... (W waves), each as
 // eight coalesced 16-byte loads per lane, all eight in flight at once, and
 // folds the words into a checksum; the bytes past the last whole tile are
@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr int kProbeBlock = 768;
+constexpr int kProbeBlock = 512;
 constexpr int kProbeWave = 64;
 constexpr uint32_t kProbeMagic = 0x9e3779b9u;
 

@@ -365,7 +365,7 @@ DSPARK_API int dspark_verify_greedy(const void* target_logits, int dtype, int B,
  *                 q_tok, ...)
  * on the same stream; the arguments mean what they mean there, and lengths
  * is required (it is the schedule's output and the verification's input).
- * With B <= 768, K <= 16 and B*K <= 12288 the schedule is worked out inside
+ * With B <= 512, K <= 16 and B*K <= 12288 the schedule is worked out inside
  * the streaming pass (every workgroup computes it from the confidences while
  * its first loads are in flight, and each writes the lengths, mask rows and
  * survival rows of its share of the requests), which saves a launch; larger
@@ -393,7 +393,7 @@ DSPARK_API int dspark_schedule_verify(const float* conf, float threshold, int bu
  *
  *   phases  DSPARK_PHASE_STREAM: enqueue everything up to and including the
  *           streaming pass (the launch that reads every scheduled logits row
- *           once; for dspark_schedule_verify_phase with more than 768
+ *           once; for dspark_schedule_verify_phase with more than 512
  *           requests, the schedule's own launch first);
  *           DSPARK_PHASE_FINISH: enqueue the rest (the decision, the residual
  *           and the draw), which reads what the streaming pass left in the

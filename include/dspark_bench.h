@@ -18,7 +18,7 @@ extern "C" {
  * dspark_bench_read_probe — plain contiguous read of a device buffer.
  *
  * Reads `bytes` bytes at `x` (device memory, 16-byte aligned) once, in the
- * launch shape of the streaming pass (one 768-thread workgroup per compute
+ * launch shape of the streaming pass (one 512-thread workgroup per compute
  * unit, 8 KB tiles of coalesced 16-byte loads per wave), and computes nothing
  * from them that reaches memory: `sink` (one uint32_t of device memory) is
  * written only if a checksum of the data equals a fixed constant.  Work goes

@@ -23,7 +23,7 @@ def _sched(w):
 def _check_workload(w, requests=None, check_sched=True):
     """Both ways of running a step, against one oracle run on the same inputs:
     dspark_schedule then dspark_verify, and dspark_schedule_verify (the
-    schedule worked out inside the streaming launch for B <= 768, its own
+    schedule worked out inside the streaming launch for B <= 512, its own
     launch first above)."""
     print(f"[{w.name} seed+{w.seed_offset}] B={w.B} K={w.K} V={w.V}", flush=True)
     lengths, mask, surv, st = _sched(w)
@@ -620,8 +620,8 @@ def _fused_vs_separate(w, budget=None, conf=None):
     (5, dict(B=512), None),               # temperatures 0 / 0.6 / 1 (greedy requests fused)
     (5, dict(B=512), 700),                # the same with a binding budget
     (5, dict(B=64, V=9001), None),        # unaligned rows: the scalar streaming path
-    (3, dict(B=768, V=4096), 1000),       # the largest fused batch: 768 requests, 12288 keys
-    (3, dict(B=769, V=4096), 1000),       # one more: the schedule launches on its own
+    (3, dict(B=512, V=4096), 600),        # the largest fused batch: 512 requests, 8192 keys
+    (3, dict(B=513, V=4096), 600),        # one more: the schedule launches on its own
     (5, {}, None),                        # 1024 requests: launched separately
 ])
 def test_schedule_verify_matches_separate_calls(wid, kw, budget):
@@ -781,7 +781,7 @@ def _same(a, b, keys):
 @pytest.mark.parametrize("wid,kw", [(3, {}), (5, dict(B=900, V=20000)), (2, dict(B=5, V=4097))])
 def test_split_phases_equal_the_whole_call(wid, kw):
     # the STREAM half then the FINISH half, with events around the first,
-    # give bit for bit what the whole call gives (fused schedule for B <= 768,
+    # give bit for bit what the whole call gives (fused schedule for B <= 512,
     # the schedule's own launch first above it)
     w = workloads.make(wid, device=DEV, **kw)
     print(f"split phases {w.name} B={w.B} V={w.V}", flush=True)
