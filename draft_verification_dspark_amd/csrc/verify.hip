@@ -327,10 +327,17 @@ __device__ __forceinline__ void summarise_tile(const Tile<DT>& t, const TileRef&
 // one workgroup writing them all would start streaming last.
 // Sync block of the workspace, per request b: line 2b holds the tag (8 bytes)
 // and the ReqState (at byte 16), line 2b + 1 the done counter.  The
-// streaming pass clears every tag; the finish kernel sets a request's tag
-// once its ReqState is written, so a tag seen set during a finish launch was
-// set by that launch.  Tag bits: 0 set, 1 a residual to draw, 8 and up the
-// rejected row (which row pair the residual tasks read).
+// streaming pass clears every tag and done counter and fills every ReqState
+// and quarter record (z, d, q) with kUnset; the finish kernel then writes a
+// request's ReqState and tag, and each quarter's record, without waiting for
+// those stores to land: a tag seen set during a finish launch was set by
+// that launch, and a reader that finds a kUnset word in a state or record
+// that must be there reads it again until the store arrives.  Tag bits: 0
+// set, 1 a residual to draw, 8 and up the rejected row (which row pair the
+// residual tasks read).
+// kUnset: a signalling-NaN pattern that no arithmetic produces and that, as
+// a ReqState word, holds a negative mode or count or a NaN shift or sum.
+constexpr uint64_t kUnset = 0x7ff4a5a5a5a5a5a5ull;
 __device__ __forceinline__ uint64_t make_tag(int mode, int row) {
   return 1ull | ((uint64_t)(mode == kModeResidual) << 1) | ((uint64_t)(uint32_t)row << 8);
 }
@@ -354,8 +361,23 @@ __global__ void __launch_bounds__(kStreamBlock) k_stream_rows(VerifyArgs a, Sche
   const int n = gridDim.x, g = blockIdx.x;
   const int w = uniform((int)(threadIdx.x / kWave));
   auto tile_of = [&](int k) { return g + n * k; };
-  for (int b = g * kStreamBlock + (int)threadIdx.x; b < a.B; b += n * kStreamBlock)
+  for (int b = g * kStreamBlock + (int)threadIdx.x; b < a.B; b += n * kStreamBlock) {
     *sync_tag(a, b) = 0;
+    if (!a.greedy_only) {
+      *sync_done(a, b) = 0;
+      uint64_t* st = reinterpret_cast<uint64_t*>(sync_state(a, b));
+#pragma unroll
+      for (int i = 0; i < (int)(sizeof(ReqState) / 8); ++i) st[i] = kUnset;
+    }
+  }
+  if (!a.greedy_only)
+    for (long long i = (long long)g * kStreamBlock + threadIdx.x; i < (long long)a.B * a.QT;
+         i += (long long)n * kStreamBlock) {
+      uint64_t* r = reinterpret_cast<uint64_t*>(a.part2 + i);
+      r[0] = kUnset;
+      r[1] = kUnset;
+      r[2] = kUnset;
+    }
   // Two tile buffers: the next tile's loads are in flight while the current
   // one is summarised.  The prefetch is issued unconditionally (past the end
   // of the range a wave re-reads its current tile, a cache hit, and drops
@@ -806,7 +828,7 @@ constexpr int kMaxRows = 2 * 64 + 1;
 // chunk summaries staged in LDS per round of the merges (24 KB)
 constexpr int kStage = 3 * kFinishBlock;
 constexpr uint64_t kSpinLimit = 100000000ull;  // 1 s at 100 MHz
-constexpr int kTaskBatch = 3;  // quarter tasks a wave has in flight at once
+constexpr int kTaskBatch = 3;  // most quarter tasks a wave has in flight at once
 
 // A full acceptance's bonus draw, deferred by wave 0 (at most kMaxPending
 // per workgroup; more are drawn at once)
@@ -843,6 +865,33 @@ template <typename T> __device__ __forceinline__ T ld_rec(const T* src) {
 #pragma unroll
   for (int i = 0; i < (int)(sizeof(T) / 8); ++i) d[i] = ld_agent(s + i);
   return v;
+}
+
+constexpr int kStateWords = sizeof(ReqState) / 8;
+constexpr int kRecWords = 3;  // z, d, q of a ResidualChunk
+// whether every one of the first `words` 8-byte words of v has arrived (none
+// is kUnset)
+template <typename T> __device__ __forceinline__ bool rec_set(const T& v, int words) {
+  const uint64_t* w = reinterpret_cast<const uint64_t*>(&v);
+  bool ok = true;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 8); ++i)
+    if (i < words) ok = ok && w[i] != kUnset;
+  return ok;
+}
+// Read a record that another wave has written (or is writing) until every
+// one of its first `words` words has arrived; false (and the last read) on
+// time-out.
+template <typename T> __device__ bool ld_rec_set(const T* src, T& v, int words) {
+  v = ld_rec(src);
+  if (rec_set(v, words)) return true;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  do {
+    __builtin_amdgcn_s_sleep(2);
+    v = ld_rec(src);
+    if (rec_set(v, words)) return true;
+  } while (__builtin_amdgcn_s_memrealtime() - t0 <= kSpinLimit);
+  return false;
 }
 
 // Wait (lane 0 polls, the wave waits) until *p == want; false on time-out.
@@ -1018,13 +1067,29 @@ __device__ int draw_residual(const VerifyArgs& a, int b, double u, int& tok_pos)
   tok_pos = st.a;
   if (a.QT <= kWave * kRecLanes) {
     double z[kRecLanes], d[kRecLanes], q[kRecLanes];
+    auto load = [&]() -> bool {
+      bool ok = true;
 #pragma unroll
-    for (int k = 0; k < kRecLanes; ++k) {
-      const int i = l + kWave * k;
-      const uint64_t* p = reinterpret_cast<const uint64_t*>(zq + (i < a.QT ? i : 0));
-      z[k] = __longlong_as_double((long long)ld_agent(p + 0));
-      d[k] = __longlong_as_double((long long)ld_agent(p + 1));
-      q[k] = __longlong_as_double((long long)ld_agent(p + 2));
+      for (int k = 0; k < kRecLanes; ++k) {
+        const int i = l + kWave * k;
+        const uint64_t* p = reinterpret_cast<const uint64_t*>(zq + (i < a.QT ? i : 0));
+        const uint64_t wz = ld_agent(p + 0), wd = ld_agent(p + 1), wq = ld_agent(p + 2);
+        ok = ok && wz != kUnset && wd != kUnset && wq != kUnset;
+        z[k] = __longlong_as_double((long long)wz);
+        d[k] = __longlong_as_double((long long)wd);
+        q[k] = __longlong_as_double((long long)wq);
+      }
+      return ok;
+    };
+    // records counted before their stores landed are read again
+    if (__ballot(!load())) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      bool ok;
+      do {
+        __builtin_amdgcn_s_sleep(2);
+        ok = !__ballot(!load());
+      } while (!ok && __builtin_amdgcn_s_memrealtime() - t0 <= kSpinLimit);
+      if (!ok && l == 0) flag(a.dev_status, DSPARK_DEV_INCOMPLETE);
     }
     // rho - 1 from the signed differences over sum e2 = St' (see ResidualRows)
     double pd = 0.0;
@@ -1058,6 +1123,13 @@ __device__ int draw_residual(const VerifyArgs& a, int b, double u, int& tok_pos)
     }
     if (loc.past_end) loc.idx = last;
   } else {
+    // every record arrived (read until it has) before the two passes below
+    bool ok = true;
+    for (int i = l; i < a.QT; i += kWave) {
+      ResidualChunk c;
+      ok = ld_rec_set(zq + i, c, kRecWords) && ok;
+    }
+    if (!ok) flag(a.dev_status, DSPARK_DEV_INCOMPLETE);
     auto rd = [&](int i) -> ResidualChunk { return ld_rec(zq + i); };
     double pd = 0.0;
     for (int i = l; i < a.QT; i += kWave) pd += rd(i).d;
@@ -1319,9 +1391,9 @@ __device__ void decide_request(const VerifyArgs& a, int b, RowSum* s_rows, Parti
     st.sd = readlane(rd.s, an);
   }
   if (l == 0) {
+    // the tag may land before the state: the tasks read the state until
+    // it has arrived (no kUnset word)
     st_rec(sync_state(a, b), st);
-    st_agent(sync_done(a, b), 0ull);
-    wait_all();
     st_agent(sync_tag(a, b), make_tag(st.mode, st.row));
   }
   if (fault) return;
@@ -1405,12 +1477,13 @@ __global__ void __launch_bounds__(kFinishBlock) k_finish(VerifyArgs a) {
   }
   if (a.greedy_only) return;  // (no bonus draws: greedy requests take the argmax)
   // Phase 2.  Wave 0 lists the requests that have a residual (from their
-  // tags) in LDS; their quarter tasks, t = live * QT + quarter, go to the
-  // grid's waves kTaskBatch consecutive tasks at a time (batch k = tasks
-  // kTaskBatch k ..., to wave k mod W), so that one batch spans at most two
-  // requests and a slow wave holds back few draws.  A batch has its row
-  // tiles and draw states all in flight before the sums, stores its
-  // records, waits once, and counts itself done.
+  // tags) in LDS; their quarter tasks, t = live * QT + quarter, are split
+  // over the grid's W waves in W runs of consecutive tasks whose lengths
+  // differ by at most one (wave k: tasks k T / W to (k + 1) T / W), so that
+  // the sums' arithmetic is spread over every wave and no wave holds back
+  // its draws with a second round.  A wave takes its run kTaskBatch tasks
+  // at a time: the batch's row tiles and draw states all in flight before
+  // the sums; it stores its records, waits once, and counts itself done.
   int* s_live = reinterpret_cast<int*>(s_part);  // free after phase 1
   if (w == 0) {
     int badl = 0;
@@ -1422,13 +1495,14 @@ __global__ void __launch_bounds__(kFinishBlock) k_finish(VerifyArgs a) {
   const int W = n * kFinishWaves;
   const int gw = w * n + g;  // neighbouring tasks on different compute units
   const long long ntask = (long long)s_nlive * a.QT;
-  for (long long t0 = (long long)gw * kTaskBatch; t0 < ntask; t0 += (long long)kTaskBatch * W) {
+  const long long t_end = ntask * (gw + 1) / W;
+  for (long long t0 = ntask * gw / W; t0 < t_end; t0 += kTaskBatch) {
     int tb[kTaskBatch], tq[kTaskBatch], trow[kTaskBatch];
     bool live[kTaskBatch];
 #pragma unroll
     for (int j = 0; j < kTaskBatch; ++j) {
       const long long t = t0 + j;
-      live[j] = t < ntask;
+      live[j] = t < t_end;
       const int li = live[j] ? (int)(t / a.QT) : 0;
       tq[j] = live[j] ? (int)(t - (long long)li * a.QT) : 0;
       const int e = s_live[li];
@@ -1447,6 +1521,13 @@ __global__ void __launch_bounds__(kFinishBlock) k_finish(VerifyArgs a) {
       td[j].template load<VEC>(draft_row(a, tb[j], trow[j], S) + (size_t)e0 * S, nn, v0);
       sj[j] = ld_rec(sync_state(a, tb[j]));
     }
+    // a state read before its stores landed is read again
+    bool st_ok = true;
+#pragma unroll
+    for (int j = 0; j < kTaskBatch; ++j)
+      if (live[j] && !rec_set(sj[j], kStateWords))
+        st_ok = ld_rec_set(sync_state(a, tb[j]), sj[j], kStateWords) && st_ok;
+    if (!st_ok) flag(a.dev_status, DSPARK_DEV_INCOMPLETE);
     ResidualChunk zj[kTaskBatch];
 #pragma unroll
     for (int j = 0; j < kTaskBatch; ++j) {
@@ -1461,7 +1542,8 @@ __global__ void __launch_bounds__(kFinishBlock) k_finish(VerifyArgs a) {
 #pragma unroll
       for (int j = 0; j < kTaskBatch; ++j)
         if (live[j]) st_rec(a.part2 + (size_t)tb[j] * a.QT + tq[j], zj[j]);
-      wait_all();
+      // counted without waiting for the records to land: the drawing wave
+      // reads a record until it has arrived
 #pragma unroll
       for (int j = 0; j < kTaskBatch; ++j)
         if (live[j]) {
