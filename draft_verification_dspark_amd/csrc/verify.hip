@@ -612,18 +612,19 @@ struct ResidualRows {
     const uint32_t bb = b1 > b2 ? b1 : b2, bs = b1 > b2 ? b2 : b1;
     heavy = bb >= hbits;
     const float big = __uint_as_float(bb), small = __uint_as_float(bs);
-    // 1 - 2^-|g| = z f(z), z = |g| ln 2 < 0.7, f(z) = (1 - e^-z)/z: a degree-5
-    // polynomial with fp32 coefficients fitted to f on [0, ln 2] for least
-    // maximum relative error (1.1e-8, below fp32 rounding)
+    // 1 - 2^-|g| = z f(z), z = |g| ln 2 < 0.7, f(z) = (1 - e^-z)/z, with f a
+    // degree-5 polynomial fitted to it on [0, ln 2] for least maximum
+    // relative error (1.1e-8); its k-th coefficient times (ln 2)^(k+1),
+    // rounded to fp32, gives P with 1 - 2^-a = a P(a) (1.4e-8 relative, below
+    // fp32 rounding), one multiplication fewer per element
     const float ag = fabsf(g);
-    const float z = ag * 0.69314718f;
-    float t = -1.038787537e-3f;
-    t = fmaf(t, z, 8.078070357e-3f);
-    t = fmaf(t, z, -4.157954454e-2f);
-    t = fmaf(t, z, 1.666534841e-1f);
-    t = fmaf(t, z, -4.999993443e-1f);
-    t = fmaf(t, z, 1.f);
-    float series = big * (z * t);
+    float t = -0.000115207164f;
+    t = fmaf(t, ag, 0.00129251310f);
+    t = fmaf(t, ag, -0.00959801860f);
+    t = fmaf(t, ag, 0.0554997176f);
+    t = fmaf(t, ag, -0.240226194f);
+    t = fmaf(t, ag, 0.693147182f);
+    float series = big * (ag * t);
     // both sides computed: a select, not a branch (the lanes of a wave take
     // both sides anyway)
     asm volatile("" : "+v"(series));
@@ -1521,17 +1522,15 @@ __global__ void __launch_bounds__(kFinishBlock) k_finish(VerifyArgs a) {
       td[j].template load<VEC>(draft_row(a, tb[j], trow[j], S) + (size_t)e0 * S, nn, v0);
       sj[j] = ld_rec(sync_state(a, tb[j]));
     }
-    // a state read before its stores landed is read again
-    bool st_ok = true;
-#pragma unroll
-    for (int j = 0; j < kTaskBatch; ++j)
-      if (live[j] && !rec_set(sj[j], kStateWords))
-        st_ok = ld_rec_set(sync_state(a, tb[j]), sj[j], kStateWords) && st_ok;
-    if (!st_ok) flag(a.dev_status, DSPARK_DEV_INCOMPLETE);
     ResidualChunk zj[kTaskBatch];
 #pragma unroll
     for (int j = 0; j < kTaskBatch; ++j) {
       if (!live[j]) continue;
+      // a state read before its stores landed is read again (checked task by
+      // task, so that task j waits only for its own loads)
+      if (!rec_set(sj[j], kStateWords) &&
+          !ld_rec_set(sync_state(a, tb[j]), sj[j], kStateWords))
+        flag(a.dev_status, DSPARK_DEV_INCOMPLETE);
       const ResidualRows rr(sj[j].c, sj[j].clo, sj[j].kt, sj[j].st, sj[j].kd, sj[j].sd);
       zj[j] = residual_sums<DT, UQ>(rr, tt[j], td[j]);
     }
