@@ -16,10 +16,11 @@ Order of the run:
    against its bounds before use;
 3. the timed region: the K steps launched back to back on one stream,
    behind a spin kernel that lets the host queue them all first;
-4. kernel timing: the same steps again, each as its two halves
-   (dspark_schedule_verify_phase: the streaming launch, then the rest) with
-   events around the streaming launch, and in a second pass whole calls with
-   events around the call;
+4. kernel timing: the streaming launches of the same steps alone
+   (dspark_schedule_verify_phase, STREAM half), back to back between one
+   event pair; the same steps again, each as its two halves with events
+   around the streaming launch (the spread, dispatch included); and whole
+   calls with events around the call;
 5. context: the same steps as two calls (dspark_schedule, dspark_verify), the
    plain read of the same bytes (libdspark_bench.so), the other hot-path
    rows (``--no-rows`` skips them);
@@ -31,8 +32,8 @@ Prints ONE JSON line on stdout.  ``value`` = verified positions per second of
 schedule + verify.  ``roofline`` reports the dominant kernel, the streaming
 launch (k_stream_rows), against the 8 TB/s HBM peak: its algorithmic bytes
 per launch, s*V*sum_b rows_b with rows_b = 2 L_b + 1 (T > 0) or L_b + 1
-(T = 0), over its mean event-timed duration; ``call_*`` the same for the
-whole call (streaming bytes plus the rejected row pairs it re-reads).
+(T = 0), over its mean duration launched back to back; ``call_*`` the same
+for the whole call (streaming bytes plus the rejected row pairs it re-reads).
 ``traffic`` is the HBM bytes per launch that rocprofv3 counters measured for
 the same kernel (FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel of known
 size), used only while the kernel sources hash to the recorded value.
@@ -190,6 +191,25 @@ def time_phases(call, reps, stream, torch, np):
     return float(np.mean(st)), ca[len(ca) // 2], st
 
 
+def time_stream_back_to_back(call, reps, stream, torch):
+    """Mean streaming-launch time (ms): `reps` STREAM halves call(i, 1)
+    launched back to back, one event pair around them all, so that no launch
+    waits on an event (each pair of events around a single launch also spans
+    its dispatch).  Rotating over the input sets keeps the reads from the
+    last-level cache as in the timed steps."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(SPIN_CYCLES)
+    e0.record(stream)
+    for i in range(reps):
+        call(i, 1)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def probe_offset(k: int, nbytes: int, span: int, stride: int) -> int:
     """Offset of the k-th plain read of `nbytes` (a multiple of 16) in a buffer
     of `span` bytes: at least `stride` past the previous read, 256-aligned,
@@ -236,24 +256,23 @@ class ReadProbe:
             raise RuntimeError(f"dspark_bench_read_probe returned {st}")
 
     def timed(self, nbytes, reps, stream, np):
-        """Mean event-timed duration (ms) of `reps` calls, the host queued ahead."""
+        """Mean duration (ms) of `reps` calls launched back to back, one event
+        pair around them all (as the streaming launches are timed), the host
+        queued ahead."""
         torch = self.torch
         for _ in range(4):
             self.call(nbytes, stream)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(reps)]
-        for e in evs:
-            for x in e:
-                x.record(stream)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
             torch.cuda._sleep(SPIN_CYCLES)
-        for e0, e1 in evs:
-            e0.record(stream)
+        e0.record(stream)
+        for _ in range(reps):
             self.call(nbytes, stream)
-            e1.record(stream)
+        e1.record(stream)
         torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        return e0.elapsed_time(e1) / reps
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -731,8 +750,11 @@ def main():
     log(f"timed {args.steps} steps: {total_ms:.3f} ms, {total_ms / args.steps * 1e3:.1f} us/step, "
         f"{value:.0f} positions/s")
 
-    # Kernel timing: the same steps as their two halves, events around the
-    # streaming launch; then whole calls, events around the call.
+    # Kernel timing: the streaming launches of the same steps back to back
+    # (the launch time the roofline uses); the same steps as their two halves,
+    # events around the streaming launch (its spread, and the time with the
+    # dispatch); then whole calls, events around the call.
+    b2b_ms = time_stream_back_to_back(lambda i, ph: step(i, ph), args.steps, stream, torch)
     str_mean, _, str_ms = time_phases(lambda i, ph: step(i, ph), args.steps, stream, torch, np)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     for e in ev:
@@ -747,9 +769,11 @@ def main():
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     call_ms = [a.elapsed_time(b) for a, b in ev]
-    stream_gbs = s_bytes / (sum(str_ms) / 1e3) / 1e9
+    stream_gbs = s_bytes / (b2b_ms * args.steps / 1e3) / 1e9
+    stream_ev_gbs = s_bytes / (sum(str_ms) / 1e3) / 1e9
     call_gbs = c_bytes / (sum(call_ms) / 1e3) / 1e9
-    log(f"streaming launch mean {np.mean(str_ms) * 1e3:.2f} us ({stream_gbs:.0f} GB/s); call "
+    log(f"streaming launch mean {b2b_ms * 1e3:.2f} us back to back ({stream_gbs:.0f} GB/s), "
+        f"{np.mean(str_ms) * 1e3:.2f} us between events ({stream_ev_gbs:.0f} GB/s); call "
         f"median {np.median(call_ms) * 1e3:.2f} us ({call_gbs:.0f} GB/s)")
 
     # the same steps as two calls (schedule, then verify), timed the same way
@@ -825,11 +849,16 @@ def main():
             "traffic": None if traffic is None else round(traffic),
             "traffic_note": traffic_note,
             "algorithmic_bytes_per_launch": round(s_bytes / args.steps),
-            "launch_us_mean": round(float(np.mean(str_ms)) * 1e3, 2),
-            "launch_us_p10_p50_p90": [pct(str_ms, 10), pct(str_ms, 50), pct(str_ms, 90)],
-            "kernel_timing": "events on the call's stream around the STREAM half of "
-                             "dspark_schedule_verify_phase (the streaming launch alone), one pass "
-                             "over the timed steps",
+            "launch_us_mean": round(b2b_ms * 1e3, 2),
+            "kernel_timing": "the STREAM halves of dspark_schedule_verify_phase (the streaming "
+                             "launch alone) of the timed steps launched back to back on the "
+                             "call's stream, one event pair around them all, mean per launch",
+            "launch_us_between_events": {
+                "mean": round(float(np.mean(str_ms)) * 1e3, 2),
+                "p10_p50_p90": [pct(str_ms, 10), pct(str_ms, 50), pct(str_ms, 90)],
+                "gbs": round(stream_ev_gbs, 1),
+                "note": "an event pair around each STREAM half, the FINISH half after it: "
+                        "each interval also spans the launch's dispatch"},
             "call_bytes_per_call": round(c_bytes / args.steps),
             "call_achieved": round(call_gbs, 1),
             "call_frac": round(call_gbs / HBM_PEAK_GBS, 4),
@@ -839,12 +868,12 @@ def main():
                          "row pairs re-read, over the call's event-timed duration",
             "early_exit_bytes_per_call": round(e_bytes / args.steps),
             "read_ceiling_2gb": {"gbs": round(big_gbs, 1), "frac": round(big_gbs / HBM_PEAK_GBS, 4),
-                                 "note": "dspark_bench_read_probe over 2 GB, events around the call"},
+                                 "note": "dspark_bench_read_probe over 2 GB, 8 calls back to back"},
             "contiguous_read_reference": {
                 "bytes": ref_bytes, "us_mean": round(ref_ms * 1e3, 2), "gbs": round(ref_gbs, 1),
                 "frac": round(ref_gbs / HBM_PEAK_GBS, 4),
                 "note": "dspark_bench_read_probe: the same bytes read contiguously, same launch "
-                        "shape, events around the call"},
+                        "shape, 30 calls back to back at rotating offsets, mean per call"},
         },
         "accepted_mean": round(mean_acc, 3),
         "waste_ratio": round(waste, 4),
