@@ -23,7 +23,8 @@ Order of the run:
    calls with events around the call;
 5. context: the same steps as two calls (dspark_schedule, dspark_verify), the
    plain read of the same bytes (libdspark_bench.so), the other hot-path
-   rows (``--no-rows`` skips them);
+   rows (``--no-rows`` skips them; their streaming launches are timed back
+   to back as above, their whole calls between events);
 6. the CPU baseline: the oracle on the host's cores (one worker process per
    core, at most 16, requests split statically), which also checks the GPU's
    outputs of input set 0 request by request (``parity``).
@@ -432,7 +433,8 @@ def row_measurements(ds, workloads, sets, outs, ws_v, dev, stream, torch, np, lo
     for i in range(n):
         greedy(i)
     gb = [s * V * int((outs[i]["lengths"].cpu().numpy().astype(np.int64) + 1).sum()) for i in range(n)]
-    t_s, t_c, _ = time_phases(greedy, 24, stream, torch, np)
+    _, t_c, _ = time_phases(greedy, 24, stream, torch, np)
+    t_s = time_stream_back_to_back(greedy, 24, stream, torch)
     gbs = float(np.mean(gb)) / (t_s / 1e3) / 1e9
     rows["G1_verify_greedy"] = {"workload": "b64-k16-v151936 logits, scheduled lengths",
                                 "stream_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -456,7 +458,8 @@ def row_measurements(ds, workloads, sets, outs, ws_v, dev, stream, torch, np, lo
     for i in range(n):
         vfull(i)
     fb = s * V * B * (2 * K + 1)
-    t_s, t_c, _ = time_phases(vfull, 18, stream, torch, np)
+    _, t_c, _ = time_phases(vfull, 18, stream, torch, np)
+    t_s = time_stream_back_to_back(vfull, 18, stream, torch)
     gbs = fb / (t_s / 1e3) / 1e9
     rows["V_full_length"] = {"workload": "b64-k16-v151936, every length = K (641.8 MB per pass)",
                              "stream_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -472,7 +475,7 @@ def row_measurements(ds, workloads, sets, outs, ws_v, dev, stream, torch, np, lo
         for i in range(n):
             vl(i)
         by = s * V * B * (2 * Lx + 1)
-        t_s, _, _ = time_phases(vl, 18, stream, torch, np)
+        t_s = time_stream_back_to_back(vl, 18, stream, torch)
         t_p = probe.timed(by, 18, stream, np)
         sweep.append((by, t_s * 1e3, t_p * 1e3))
     xb = np.array([x[0] for x in sweep], dtype=np.float64)
@@ -615,7 +618,8 @@ def row_measurements(ds, workloads, sets, outs, ws_v, dev, stream, torch, np, lo
     L = L5.cpu().numpy().astype(np.int64)
     T = w5.temperature.cpu().numpy()
     b5 = s * V5 * int((((2 * L + 1) * (T > 0)) + ((L + 1) * (T == 0))).sum())
-    t_s, t_c, _ = time_phases(v5, 12, stream, torch, np)
+    _, t_c, _ = time_phases(v5, 12, stream, torch, np)
+    t_s = time_stream_back_to_back(v5, 12, stream, torch)
     gbs = b5 / (t_s / 1e3) / 1e9
     rows["V_G1_mixed_b1024"] = {"workload": "b1024-k8-v151936, temperatures 0 / 0.6 / 1, scheduled",
                                 "positions": int(L.sum()), "stream_bytes": b5,
