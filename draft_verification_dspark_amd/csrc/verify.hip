@@ -1484,7 +1484,8 @@ __global__ void __launch_bounds__(kFinishBlock) k_finish(VerifyArgs a) {
   // the sums' arithmetic is spread over every wave and no wave holds back
   // its draws with a second round.  A wave takes its run kTaskBatch tasks
   // at a time: the batch's row tiles and draw states all in flight before
-  // the sums; it stores its records, waits once, and counts itself done.
+  // the sums; it stores its records and counts itself done without waiting
+  // for them to land.
   int* s_live = reinterpret_cast<int*>(s_part);  // free after phase 1
   if (w == 0) {
     int badl = 0;
