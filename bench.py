@@ -411,13 +411,18 @@ def parity_of_sample(first, gpu: dict, temperature, K):
 
 # ---------------------------------------------------------------- other rows
 
-def row_measurements(ds, workloads, sets, outs, ws_v, dev, stream, torch, np, log, probe):
+def row_measurements(ds, workloads, sets, outs, ws_v, dev, stream, torch, np, log, probe,
+                     until=None):
     """The hot-path rows the headline step does not exercise, each timed
     apart (not part of `value`): the greedy rule, full-length blocks, a length
     sweep against the plain read, the schedule with a binding budget, the
     load-aware schedule, online calibration, Markov drafting and a
-    mixed-temperature batch of 1024 requests."""
+    mixed-temperature batch of 1024 requests.  With `until`, the rows run in
+    that order and stop after the one of that name (for profiling a row)."""
     rows = {}
+
+    def stop():
+        return until is not None and until in rows
     n = len(sets)
     B, K, V = sets[0].B, sets[0].K, sets[0].V
     s = 2
@@ -439,6 +444,8 @@ def row_measurements(ds, workloads, sets, outs, ws_v, dev, stream, torch, np, lo
     rows["G1_verify_greedy"] = {"workload": "b64-k16-v151936 logits, scheduled lengths",
                                 "stream_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
                                 "stream_us_mean": round(t_s * 1e3, 2), "call_us_median": round(t_c * 1e3, 2)}
+    if stop():
+        return rows
 
     # V1-V5 at full length: every block verified to K
     full = torch.full((B,), K, dtype=torch.int32, device=dev)
@@ -465,6 +472,8 @@ def row_measurements(ds, workloads, sets, outs, ws_v, dev, stream, torch, np, lo
                              "stream_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
                              "stream_us_mean": round(t_s * 1e3, 2), "call_us_median": round(t_c * 1e3, 2),
                              "positions_per_s": round(B * K / (t_c / 1e3), 1)}
+    if stop():
+        return rows
 
     # The streaming pass against its byte count: every length = L for several
     # L, a least-squares line through (bytes, time), and the plain contiguous
@@ -489,6 +498,8 @@ def row_measurements(ds, workloads, sets, outs, ws_v, dev, stream, torch, np, lo
         "read_slope_gbs": round(1e-3 / fit_p[0], 1), "read_intercept_us": round(fit_p[1], 2),
         "note": "read = dspark_bench_read_probe, a plain contiguous read of the same bytes in the "
                 "same launch shape"}
+    if stop():
+        return rows
 
     # S3 and the mixed batch: workload b1024-k8-v151936 (temperatures 0 / 0.6 / 1)
     w5 = workloads.make(5, device=dev)
@@ -649,6 +660,9 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the separate timings of the other hot-path rows")
+    ap.add_argument("--rows-until", default=None, metavar="ROW",
+                    help="run the rows in order and stop after this one (G1_verify_greedy, "
+                         "V_full_length or V_length_sweep; for profiling a row)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this path runs on a "
@@ -883,7 +897,7 @@ def main():
         "waste_ratio": round(waste, 4),
     }
     result["rows"] = None if args.no_rows else row_measurements(
-        ds, workloads, sets, outs, ws_v, dev, stream, torch, np, log, probe)
+        ds, workloads, sets, outs, ws_v, dev, stream, torch, np, log, probe, until=args.rows_until)
 
     if args.calibrate_copy > 0:
         n = args.calibrate_copy * (1 << 20) // 4
