@@ -351,7 +351,10 @@ __device__ __forceinline__ uint64_t* sync_done(const VerifyArgs& a, int b) {
   return reinterpret_cast<uint64_t*>(a.sync + (size_t)(2 * b + 1) * kSyncLine);
 }
 
-template <int DT, bool VEC, bool FUSED>
+// FUSED: 0 lengths given, 1 schedule inside, 2 schedule inside with each
+// request's confidences read as 16-byte pieces (K a multiple of 4, rows
+// 16-byte aligned).
+template <int DT, bool VEC, int FUSED>
 __global__ void __launch_bounds__(kStreamBlock) k_stream_rows(VerifyArgs a, ScheduleArgs s) {
   extern __shared__ int plan[];
   __shared__ int s_next;
@@ -400,9 +403,21 @@ __global__ void __launch_bounds__(kStreamBlock) k_stream_rows(VerifyArgs a, Sche
     if (!a.greedy_only) t_raw = a.temperature[threadIdx.x];
     if constexpr (FUSED) {
       // one path of plain loads (two would meet in a copy that waits)
-      const float* cr = s.conf + (size_t)threadIdx.x * s.K;
+      if constexpr (FUSED == 2) {
+        const float4* cr = reinterpret_cast<const float4*>(s.conf + (size_t)threadIdx.x * s.K);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) cpre[i] = cr[min(i, s.K - 1)];
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = cr[min(q, s.K / 4 - 1)];
+          cpre[4 * q] = v.x;
+          cpre[4 * q + 1] = v.y;
+          cpre[4 * q + 2] = v.z;
+          cpre[4 * q + 3] = v.w;
+        }
+      } else {
+        const float* cr = s.conf + (size_t)threadIdx.x * s.K;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) cpre[i] = cr[min(i, s.K - 1)];
+      }
     } else {
       if (a.lengths) l_raw = a.lengths[threadIdx.x];
     }
@@ -1583,11 +1598,14 @@ static int launch_verify_t(VerifyArgs& a, hipStream_t st, int phases, const Sche
   const size_t lds = sizeof(int) * (3 * (size_t)a.B + 1);
   const int grid = compute_units();
   if (phases & kPhaseStream) {
-    if (fused)
-      hipLaunchKernelGGL((k_stream_rows<DT, VEC, true>), dim3((unsigned)grid), dim3(kStreamBlock),
+    if (fused && fused->vec4)
+      hipLaunchKernelGGL((k_stream_rows<DT, VEC, 2>), dim3((unsigned)grid), dim3(kStreamBlock),
+                         lds, st, a, *fused);
+    else if (fused)
+      hipLaunchKernelGGL((k_stream_rows<DT, VEC, 1>), dim3((unsigned)grid), dim3(kStreamBlock),
                          lds, st, a, *fused);
     else
-      hipLaunchKernelGGL((k_stream_rows<DT, VEC, false>), dim3((unsigned)grid),
+      hipLaunchKernelGGL((k_stream_rows<DT, VEC, 0>), dim3((unsigned)grid),
                          dim3(kStreamBlock), lds, st, a, ScheduleArgs{});
   }
   if (phases & kPhaseFinish)
