@@ -645,6 +645,25 @@ def test_schedule_verify_min_len_and_odd_k(K, min_len, budget):
     compare_schedule((host(fu["lengths"]), host(fu["mask"]), host(fu["survival"])), ref_s)
 
 
+def test_schedule_verify_confidence_alignment():
+    # the fused launch reads a request's confidences as 16-byte pieces when K
+    # is a multiple of 4 and the rows are 16-byte aligned, else one by one:
+    # the same confidences one float off alignment give the same outputs
+    w = workloads.make(3, seed_offset=17, device=DEV)
+    args = (w.threshold, w.budget, w.min_len, w.target, w.draft, w.drafted, w.temperature,
+            w.uniforms)
+    print("fused: aligned against misaligned confidences", flush=True)
+    a = ds.schedule_verify(w.conf, *args)
+    buf = torch.empty(w.conf.numel() + 1, dtype=torch.float32, device=DEV)
+    shifted = buf[1:].view(w.conf.shape)
+    shifted.copy_(w.conf)
+    assert shifted.data_ptr() % 16 != 0
+    b = ds.schedule_verify(shifted, *args)
+    torch.cuda.synchronize()
+    for k in ("lengths", "mask", "survival", "accepted", "tokens", "p_tok", "q_tok", "dev_status"):
+        assert torch.equal(a[k], b[k]), k
+
+
 def test_schedule_verify_against_oracle():
     w = workloads.make(3, seed_offset=300, device=DEV)
     fu = ds.schedule_verify(w.conf, w.threshold, w.budget, w.min_len, w.target, w.draft,
