@@ -863,8 +863,6 @@ __device__ __forceinline__ uint64_t ld_agent(const uint64_t* p) {
 __device__ __forceinline__ void st_agent(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// every earlier memory operation of this wave completed
-__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
 // a record of 8-byte words moved with agent-scope atomic stores / loads
 template <typename T> __device__ __forceinline__ void st_rec(T* dst, const T& v) {
@@ -908,22 +906,6 @@ template <typename T> __device__ bool ld_rec_set(const T* src, T& v, int words) 
     if (rec_set(v, words)) return true;
   } while (__builtin_amdgcn_s_memrealtime() - t0 <= kSpinLimit);
   return false;
-}
-
-// Wait (lane 0 polls, the wave waits) until *p == want; false on time-out.
-__device__ bool wait_tag(const uint64_t* p, uint64_t want) {
-  int ok = 1;
-  if (lane_id() == 0) {
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    while (ld_agent(p) != want) {
-      __builtin_amdgcn_s_sleep(2);
-      if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
-        ok = 0;
-        break;
-      }
-    }
-  }
-  return readlane(ok, 0) != 0;
 }
 
 // Inverse CDF over n weights f(0..n-1) by one wave, in index order, in
