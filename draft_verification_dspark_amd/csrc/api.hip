@@ -217,7 +217,11 @@ static int verify_common(const void* target, const void* draft, int dtype, int B
   a.V = V;
   const int per_vec = dtype == DSPARK_BF16 ? 8 : 4;
   a.G = dtype == DSPARK_BF16 ? chunks_per_row<DSPARK_BF16>(V) : chunks_per_row<DSPARK_F32>(V);
-  a.QT = 4 * a.G;
+  // one quarter task per quarter chunk that holds part of the row: the last
+  // chunk's quarters past the row's end would be empty tasks
+  const int quarter =
+      (dtype == DSPARK_BF16 ? item_elems<DSPARK_BF16>() : item_elems<DSPARK_F32>()) / 4;
+  a.QT = (V + quarter - 1) / quarter;
   a.greedy_only = greedy_only;
   a.vec_ok = (V % per_vec == 0) && aligned(target, 16) && (greedy_only || aligned(draft, 16));
   if (dry) return DSPARK_OK;  // arguments checked, nothing launched

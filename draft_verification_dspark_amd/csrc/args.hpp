@@ -24,7 +24,7 @@ struct VerifyArgs {
   Partial* part1;      // [B*(K+1)*2*G] chunk summaries, (request, row j, side) major
   ResidualChunk* part2;  // [B*QT] residual sums per quarter chunk of the rejected row pair
   int B, K, V, G;
-  int QT;              // quarter tasks per request: 4 per chunk
+  int QT;              // quarter tasks per request: one per quarter chunk up to the row's end
   int greedy_only;
   int vec_ok;
 };

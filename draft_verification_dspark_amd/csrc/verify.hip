@@ -820,12 +820,11 @@ __device__ __forceinline__ Located wave_locate(double x, double u) {
 //            rejection it publishes the draw state (ReqState) and sets the
 //            request's tag.
 //   Phase 2  the residual of every rejected request is split into quarter
-//            chunks (4 per 4096-token chunk of the row pair); quarter task
-//            t = b * QT + q goes to wave t mod W of the grid (W waves in all),
-//            which waits for the request's tag, sums its quarter (d, D, Q;
-//            see ResidualRows) and counts itself done on the request's
-//            counter.  The wave that completes the request draws the
-//            correction token.
+//            chunks (a quarter of a chunk each, QT per request, none past
+//            the row's end); the grid's W waves take runs of consecutive
+//            tasks.  A task sums its quarter (d, D, Q; see ResidualRows) and
+//            counts itself done on the request's counter.  The wave that
+//            completes the request draws the correction token.
 // Cross-workgroup hand-over goes through the sync block of the workspace:
 // per request a tag line (tag, ReqState) and a counter line, each on its own
 // 128-byte line (atomics on a shared line serialise).  Stores that another
