@@ -220,6 +220,38 @@ __device__ void budget_cut(int n, const Src& src, long long m, long long ncand, 
   }
 }
 
+// Length and mask of request b.
+__device__ __forceinline__ void store_len_mask(const ScheduleArgs& a, int b, int len) {
+  const int K = a.K;
+  a.lengths[b] = len;
+  if (a.mask) {
+    uint8_t* mr = a.mask + (size_t)b * K;
+    if ((K & 3) == 0 && ((uintptr_t)a.mask & 3) == 0) {
+      // four mask bytes per store
+      uint32_t* mw = reinterpret_cast<uint32_t*>(mr);
+      for (int k = 0; k < K; k += 4) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) word |= (uint32_t)(k + q < len ? 1u : 0u) << (8 * q);
+        mw[k >> 2] = word;
+      }
+    } else {
+      for (int k = 0; k < K; ++k) mr[k] = (uint8_t)(k < len ? 1 : 0);
+    }
+  }
+}
+
+// Tile-count prefix of a caller's plan over the requests in thread order,
+// worked out at the schedule's own barrier when the budget does not bind
+// (off stays negative otherwise: the lengths change after the barrier).
+struct PlanPrefix {
+  int off = -1;   // the counts of the requests before this thread's
+  int total = 0;  // the counts of all requests
+};
+struct NoPlanCount {
+  __device__ int operator()(int) const { return 0; }
+};
+
 // The schedule of the whole batch by one workgroup of kSchedThreads threads
 // (every thread calls it; thread t owns requests t, t + T, ...).  The
 // outputs of request b (survival products, length, mask, status bits) go to
@@ -231,12 +263,23 @@ __device__ void budget_cut(int n, const Src& src, long long m, long long ncand, 
 // request threadIdx.x (0 for threads without a request).
 // kStage: confidences per thread loaded at once (one round trip per kStage
 // positions).  kPre: the caller has loaded them already, into `pre`, for its
-// own request (one request per thread, K <= kStage).
-template <int kSchedThreads, int kStage = kConfStage, bool kPre = false>
+// own request (one request per thread, K <= kStage); `pre` then returns the
+// survival products, and the request's outputs (survival products, length,
+// mask) are left to the caller, who writes them with schedule_store_own once
+// it has nothing more to wait for: on this target stores and loads share one
+// in-order counter, and a store inside a branch makes the compiler wait for
+// younger loads as well.  With `plan` (kPre only), plan_count(L) is the
+// caller's count for its request at length L, and `plan` receives the
+// prefix of those counts at the threshold lengths when the budget does not
+// bind, so that the caller's plan needs no barrier of its own for it.
+template <int kSchedThreads, int kStage = kConfStage, bool kPre = false,
+          typename PlanCount = NoPlanCount>
 __device__ int schedule_body(const ScheduleArgs& a, float tau, int budget, int wg, int nwg,
-                             const float* pre = nullptr) {
+                             float* pre = nullptr, PlanCount plan_count = PlanCount{},
+                             PlanPrefix* plan = nullptr) {
   constexpr int kSchedWaves = kSchedThreads / kWave;
   __shared__ long long red[kSchedWaves];
+  __shared__ int red_plan[kSchedWaves];
   __shared__ uint32_t red_or[kSchedWaves], red_and[kSchedWaves];
   __shared__ __align__(16) int cnt[2][kSchedWaves][16][4];  // [pass & 1][wave][digit][row]
   __shared__ uint32_t s_key[kSchedLds];
@@ -252,15 +295,15 @@ __device__ int schedule_body(const ScheduleArgs& a, float tau, int budget, int w
   int lt_reg[kSchedRegs];
   long long local = 0;
   int bad = 0;
+  int pc = 0;  // kPre: the caller's plan count at the threshold length
   if constexpr (kPre) {
     // One request per thread, its K <= kStage confidences in registers: the
     // same steps straight-line, with no branch per position.  A position
     // past K leaves the product and the run as they are and stores again
-    // the last position's survival value and key into that position's slot.
+    // the last position's key into that position's slot.
     const int b = tid;
     if (b < B) {
       const bool write = nwg == 1 || b % nwg == wg;
-      float* __restrict__ sr = a.surv + (size_t)b * K;
       float C = 1.f;
       int run = 0;
       bool go = true;
@@ -278,10 +321,11 @@ __device__ int schedule_body(const ScheduleArgs& a, float tau, int budget, int w
         key = in ? ((go && k + 1 > ml) ? surv_key(C) + 1u : 0u) : key;
         const int slot = k < K ? k : K - 1;
         if (keys_in_lds) s_key[(size_t)b * K + slot] = key;
-        if (write) sr[slot] = C;
+        pre[k] = C;
       }
       const int lt = max(ml, run);
       lt_reg[0] = lt;
+      pc = plan_count(lt);
       if (nwg == 1 && !keys_in_lds) a.lthr[b] = lt;  // read back by the budget cut
       local = lt;
       if (write && bad) flag(a.dev_status, bad);
@@ -358,6 +402,18 @@ __device__ int schedule_body(const ScheduleArgs& a, float tau, int budget, int w
   // block sum of Lthr (the barrier also publishes the LDS keys and the
   // stored survival and threshold lengths to the other threads; a wave's sum
   // is at most B*K <= 2^30: int)
+  int pc_excl = 0;
+  if constexpr (kPre) {
+    // the plan counts scanned across the wave, published at the same barrier
+    int incl = pc;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane_id() >= o) incl += t;
+    }
+    if (lane_id() == kWave - 1) red_plan[tid / kWave] = incl;
+    pc_excl = incl - pc;
+  }
   const int wsum = wave_reduce((int)local, [](int x, int y) { return x + y; });
   if (lane_id() == 0) red[tid / kWave] = wsum;
   __syncthreads();
@@ -366,6 +422,18 @@ __device__ int schedule_body(const ScheduleArgs& a, float tau, int budget, int w
 
   const long long floor_all = (long long)B * ml;
   const bool binds = budget >= 0 && total > budget;
+  if constexpr (kPre) {
+    if (plan && !binds) {
+      int off = pc_excl, all = 0;
+      for (int w = 0; w < kSchedWaves; ++w) {
+        const int x = red_plan[w];
+        if (w < tid / kWave) off += x;
+        all += x;
+      }
+      plan->off = off;
+      plan->total = all;
+    }
+  }
   const long long m = binds ? (long long)budget - floor_all : 0;  // free slots, >= 0
   uint32_t kstar = 0xffffffffu, istar = 0u;  // no candidate is taken by default
   if (binds && m > 0) {
@@ -392,25 +460,33 @@ __device__ int schedule_body(const ScheduleArgs& a, float tau, int budget, int w
       len = ml + take;
     }
     if (b == tid) my_len = len;
-    if (!(nwg == 1 || b % nwg == wg)) continue;
-    a.lengths[b] = len;
-    if (a.mask) {
-      uint8_t* mr = a.mask + (size_t)b * K;
-      if ((K & 3) == 0 && ((uintptr_t)a.mask & 3) == 0) {
-        // four mask bytes per store
-        uint32_t* mw = reinterpret_cast<uint32_t*>(mr);
-        for (int k = 0; k < K; k += 4) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) word |= (uint32_t)(k + q < len ? 1u : 0u) << (8 * q);
-          mw[k >> 2] = word;
-        }
-      } else {
-        for (int k = 0; k < K; ++k) mr[k] = (uint8_t)(k < len ? 1 : 0);
-      }
-    }
+    if (kPre || !(nwg == 1 || b % nwg == wg)) continue;
+    store_len_mask(a, b, len);
   }
   return my_len;
+}
+
+// The outputs of request threadIdx.x that schedule_body<..., kPre = true>
+// left to its caller: `surv` (its survival products) and `len` go to memory
+// when this workgroup owns the request.
+template <int kN>
+__device__ __forceinline__ void schedule_store_own(const ScheduleArgs& a, int wg, int nwg,
+                                                   int len, const float (&surv)[kN]) {
+  const int b = threadIdx.x;
+  if (b >= a.B || !(nwg == 1 || b % nwg == wg)) return;
+  float* __restrict__ sr = a.surv + (size_t)b * a.K;
+  if (a.vec4) {
+#pragma unroll
+    for (int q = 0; q < kN / 4; ++q)
+      if (4 * q < a.K)
+        *reinterpret_cast<float4*>(sr + 4 * q) =
+            make_float4(surv[4 * q], surv[4 * q + 1], surv[4 * q + 2], surv[4 * q + 3]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < kN; ++k)
+      if (k < a.K) sr[k] = surv[k];
+  }
+  store_len_mask(a, b, len);
 }
 
 }  // namespace dspark

@@ -248,6 +248,21 @@ __device__ __forceinline__ void build_plan(const VerifyArgs& a, int* start, int*
   __syncthreads();
 }
 
+// The plan when the fused schedule has already taken the prefix of the
+// requests' tile counts at its own barrier (one request per thread): the
+// same layout as build_plan, with one barrier fewer.
+__device__ __forceinline__ void build_plan_known(const VerifyArgs& a, int* start, int* info,
+                                                 float* cval, ReqInfo pre, const PlanPrefix& pp) {
+  const int b = threadIdx.x;
+  if (b < a.B) {
+    info[b] = pre.L | (pre.kind << 8);
+    cval[b] = pre.c;
+    start[b] = a.B * a.G + pp.off;
+  }
+  if (b == kStreamBlock - 1) start[a.B] = a.B * a.G + pp.total;
+  __syncthreads();
+}
+
 // Tile t of the list.  Tiles of target row 0 need no plan.
 template <int DT>
 __device__ __forceinline__ TileRef decode_tile(const VerifyArgs& a, const int* start,
@@ -323,12 +338,15 @@ __device__ __forceinline__ void summarise_tile(const Tile<DT>& t, const TileRef&
 // from the confidences `s` itself, while its row-0 loads are in flight, and
 // takes the lengths from it; the schedule is deterministic, so all agree.
 // Workgroup g writes the schedule's outputs (lengths, mask, survival,
-// status) of the requests b with b % n == g, which the later launches read;
-// one workgroup writing them all would start streaming last.
+// status) of the requests b with b % n == g, which the later launches read,
+// after its streaming loop; one workgroup writing them all would start
+// streaming last.
 // Sync block of the workspace, per request b: line 2b holds the tag (8 bytes)
 // and the ReqState (at byte 16), line 2b + 1 the done counter.  The
-// streaming pass clears every tag and done counter and fills every ReqState
-// and quarter record (z, d, q) with kUnset; the finish kernel then writes a
+// streaming pass (of a call with sampled requests; a greedy-only call's
+// finish kernel uses none of this) clears every tag and done counter and
+// fills every ReqState and quarter record (z, d, q) with kUnset, after its
+// streaming loop; the finish kernel then writes a
 // request's ReqState and tag, and each quarter's record, without waiting for
 // those stores to land: a tag seen set during a finish launch was set by
 // that launch, and a reader that finds a kUnset word in a state or record
@@ -364,23 +382,6 @@ __global__ void __launch_bounds__(kStreamBlock) k_stream_rows(VerifyArgs a, Sche
   const int n = gridDim.x, g = blockIdx.x;
   const int w = uniform((int)(threadIdx.x / kWave));
   auto tile_of = [&](int k) { return g + n * k; };
-  for (int b = g * kStreamBlock + (int)threadIdx.x; b < a.B; b += n * kStreamBlock) {
-    *sync_tag(a, b) = 0;
-    if (!a.greedy_only) {
-      *sync_done(a, b) = 0;
-      uint64_t* st = reinterpret_cast<uint64_t*>(sync_state(a, b));
-#pragma unroll
-      for (int i = 0; i < (int)(sizeof(ReqState) / 8); ++i) st[i] = kUnset;
-    }
-  }
-  if (!a.greedy_only)
-    for (long long i = (long long)g * kStreamBlock + threadIdx.x; i < (long long)a.B * a.QT;
-         i += (long long)n * kStreamBlock) {
-      uint64_t* r = reinterpret_cast<uint64_t*>(a.part2 + i);
-      r[0] = kUnset;
-      r[1] = kUnset;
-      r[2] = kUnset;
-    }
   // Two tile buffers: the next tile's loads are in flight while the current
   // one is summarised.  The prefetch is issued unconditionally (past the end
   // of the range a wave re-reads its current tile, a cache hit, and drops
@@ -433,39 +434,73 @@ __global__ void __launch_bounds__(kStreamBlock) k_stream_rows(VerifyArgs a, Sche
     A.template load<VEC>(ra.base, ra.n);
   }
   ReqInfo mine{0, kKindSkip, 0, 0.f};
+  int len = 0;  // FUSED: this thread's request's length, stored after the loop
+  PlanPrefix pp;
   if constexpr (FUSED) {
-    const int len = schedule_body<kStreamBlock, 16, true>(s, s.tau, s.budget, g, n, cpre);
+    // the request's tiles after row 0 at length L, as build_plan counts them
+    auto tiles_at = [&](int L) -> int {
+      if (!mine_req) return 0;
+      const ReqInfo r = req_info_lt(a, L, t_raw);
+      return (r.kind == kKindSoftmax ? 2 * r.L : (r.kind == kKindGreedy ? r.L : 0)) * a.G;
+    };
+    // (cpre returns the survival products)
+    len = schedule_body<kStreamBlock, 16, true>(s, s.tau, s.budget, g, n, cpre, tiles_at, &pp);
     if (mine_req) mine = req_info_lt(a, len, t_raw);
   } else {
     if (mine_req) mine = req_info_lt(a, l_raw, t_raw);
   }
-  build_plan(a, start, info, cval, one_each, mine);
+  // the tile counter, published by the plan's closing barrier
+  if (threadIdx.x == 0) s_next = kStreamWaves;
+  // (pp.off is the same sign in every thread: whether the budget binds)
+  if (FUSED && pp.off >= 0)
+    build_plan_known(a, start, info, cval, mine, pp);
+  else
+    build_plan(a, start, info, cval, one_each, mine);
   const int total = uniform(start[a.B]);
   const int end = uniform((total - g + n - 1) / n);  // tiles of this workgroup
-  if (threadIdx.x == 0) s_next = kStreamWaves;
-  __syncthreads();
   // next tile index for this wave (one LDS atomic by lane 0)
   auto grab = [&]() -> int {
     int x = 0;
     if (lane_id() == 0) x = atomicAdd(&s_next, 1);
     return uniform(readlane(x, 0));
   };
-  if (t0 >= end) return;
-  if (!early) {
-    ra = decode_tile<DT>(a, start, info, tile_of(t0));
-    A.template load<VEC>(ra.base, ra.n);
+  if (t0 < end) {
+    if (!early) {
+      ra = decode_tile<DT>(a, start, info, tile_of(t0));
+      A.template load<VEC>(ra.base, ra.n);
+    }
+    while (true) {
+      const int t1 = grab();
+      rb = decode_tile<DT>(a, start, info, tile_of(t1 < end ? t1 : t0));
+      Bt.template load<VEC>(rb.base, rb.n);
+      summarise_tile<DT>(A, ra, uniform(info[ra.b]) >> 8, uniform(cval[ra.b]));
+      if (t1 >= end) break;
+      t0 = grab();
+      ra = decode_tile<DT>(a, start, info, tile_of(t0 < end ? t0 : t1));
+      A.template load<VEC>(ra.base, ra.n);
+      summarise_tile<DT>(Bt, rb, uniform(info[rb.b]) >> 8, uniform(cval[rb.b]));
+      if (t0 >= end) break;
+    }
   }
-  while (true) {
-    const int t1 = grab();
-    rb = decode_tile<DT>(a, start, info, tile_of(t1 < end ? t1 : t0));
-    Bt.template load<VEC>(rb.base, rb.n);
-    summarise_tile<DT>(A, ra, uniform(info[ra.b]) >> 8, uniform(cval[ra.b]));
-    if (t1 >= end) break;
-    t0 = grab();
-    ra = decode_tile<DT>(a, start, info, tile_of(t0 < end ? t0 : t1));
-    A.template load<VEC>(ra.base, ra.n);
-    summarise_tile<DT>(Bt, rb, uniform(info[rb.b]) >> 8, uniform(cval[rb.b]));
-    if (t0 >= end) break;
+  // Stores once nothing more is loaded (stores and loads share one in-order
+  // counter): the schedule's outputs of this workgroup's requests, and the
+  // finish kernel's sync block and records reset for its launch (a greedy-only
+  // call's finish kernel uses neither).
+  if constexpr (FUSED) schedule_store_own(s, g, n, len, cpre);
+  if (a.greedy_only) return;
+  for (int b = g * kStreamBlock + (int)threadIdx.x; b < a.B; b += n * kStreamBlock) {
+    *sync_tag(a, b) = 0;
+    *sync_done(a, b) = 0;
+    uint64_t* st = reinterpret_cast<uint64_t*>(sync_state(a, b));
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(ReqState) / 8); ++i) st[i] = kUnset;
+  }
+  for (long long i = (long long)g * kStreamBlock + threadIdx.x; i < (long long)a.B * a.QT;
+       i += (long long)n * kStreamBlock) {
+    uint64_t* r = reinterpret_cast<uint64_t*>(a.part2 + i);
+    r[0] = kUnset;
+    r[1] = kUnset;
+    r[2] = kUnset;
   }
 }
 
