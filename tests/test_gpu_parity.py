@@ -860,6 +860,27 @@ def test_workspaces_are_per_stream():
     _same(o2, r2, ("accepted", "tokens", "p_tok", "q_tok"))
 
 
+def test_one_workspace_shared_by_greedy_and_sampled_calls():
+    # a greedy-only call leaves the finish kernel's sync block alone; a
+    # sampled call on the same workspace right after it resets the block
+    # itself and gives what it gives on a workspace of its own, and so does
+    # the greedy call after a sampled one
+    w = workloads.make(3, device=DEV, B=16, V=30000)
+    ws = ds.Workspace(ds.dspark_workspace_bytes(ds.OP_VERIFY, w.B, w.K, w.V), torch.device(DEV))
+    ref = ds.verify(w.target, w.draft, w.drafted, None, w.temperature, w.uniforms)
+    g_ref = ds.verify_greedy(w.target, w.drafted, None)
+    runs = []
+    for _ in range(2):
+        g = ds.verify_greedy(w.target, w.drafted, None, ws=ws)
+        v = ds.verify(w.target, w.draft, w.drafted, None, w.temperature, w.uniforms, ws=ws)
+        runs.append((g, v))
+    torch.cuda.synchronize()
+    assert int((ref["accepted"] < w.K).sum()) > 0  # residual draws took part
+    for g, v in runs:
+        _same(g, g_ref, ("accepted", "tokens", "dev_status"))
+        _same(v, ref, ("accepted", "tokens", "p_tok", "q_tok", "dev_status"))
+
+
 # ---------------------------------------------------------------- calibration
 
 def _ulps(a, b):
