@@ -237,6 +237,26 @@ def test_large_and_masked_logits():
     _verify_and_compare(tgt2, dft2, drafted2, L, temp, u)
 
 
+@pytest.mark.parametrize("dtype,V", [("bf16", 5000), ("bf16", 4097), ("f32", 4609), ("f32", 2049)])
+def test_residual_mass_in_the_last_partial_quarter(dtype, V):
+    # the rejected rows' residual mass sits on the last token of the row, in
+    # a quarter chunk that the row's end cuts short (one token long for
+    # V = 4097 bf16 and V = 2049 / 4609 fp32): the residual tasks stop at the
+    # row's end and the draw must still land there
+    B, K = 8, 3
+    tgt, dft, drafted, L, temp, u = _rand_case(B, K, V, dtype, seed=V + 11, T=0.5, scale=0.5,
+                                               draft_noise=0.3, lengths="full")
+    st = tgt.dtype
+    t32, d32 = tgt.float(), dft.float()
+    t32[:, :, V - 1] += 9.0   # the target wants the last token
+    d32[:, :, 7] += 9.0       # the draft proposes token 7 instead
+    tgt, dft = t32.to(st).contiguous(), d32.to(st).contiguous()
+    drafted = torch.full((B, K), 7, dtype=torch.int32, device=DEV)
+    g, ref = _verify_and_compare(tgt, dft, drafted, L, temp, u)
+    drawn = [int(g["tokens"][b, g["accepted"][b]]) for b in range(B) if g["accepted"][b] < K]
+    assert drawn and all(t == V - 1 for t in drawn), drawn
+
+
 def _temps_with_both_lo_signs(n):
     """n temperatures in [0.3, 1.6], half of them with log2(e)/T above its
     nearest fp32 value and half below: the kernels carry log2(e)/T as an fp32
